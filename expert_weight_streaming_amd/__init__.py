@@ -1,0 +1,154 @@
+"""Python binding of libmoe (argument marshalling only).
+
+Every function here forwards to the C entry point of the same name in
+libmoe.so (include/moe.h); all arithmetic runs in the library's HIP kernels.
+Tensors are torch tensors on the GPU (PyTorch supplies device memory and
+streams).  There is no fallback: the first call raises ImportError when
+libmoe.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import SO as _SO, build  # noqa: F401
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EHIP = -3
+MOE_ESTATE = -4
+MOE_DEVERR_EXPERT_RANGE = 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("router_w", ctypes.c_void_p),
+                ("gamma", ctypes.c_void_p), ("experts", ctypes.c_void_p), ("shared", ctypes.c_void_p),
+                ("slab", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64)]
+
+
+class Streamer(ctypes.Structure):
+    _fields_ = [("host_arena", ctypes.c_void_p), ("host_shared", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64),
+                ("n_experts", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("arena_blobs", ctypes.c_int64),
+                ("shared_blobs", ctypes.c_int64), ("slab", ctypes.c_void_p * 2), ("slab_blobs", ctypes.c_int32)]
+
+
+EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_last_error", "moe_route",
+           "moe_expert_forward", "moe_layer_step", "moe_layer_plan", "moe_stream_prefetch"]
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            raise ImportError(f"libmoe.so is not built ({_SO}); run __graft_entry__.build()")
+        L = ctypes.CDLL(_SO)
+        i32, u64, sz, vp, cp = ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
+        L.moe_blob_bytes.restype = sz
+        L.moe_blob_bytes.argtypes = [i32, i32, i32, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
+        L.moe_strerror.restype = cp
+        L.moe_strerror.argtypes = [ctypes.c_int]
+        L.moe_last_error.restype = cp
+        L.moe_last_error.argtypes = []
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_forward.restype = ctypes.c_int
+        L.moe_expert_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_step.restype = ctypes.c_int
+        L.moe_layer_step.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_layer_plan.restype = ctypes.c_int
+        L.moe_layer_plan.argtypes = [ctypes.POINTER(LayerDesc), i32, vp]
+        L.moe_stream_prefetch.restype = ctypes.c_int
+        L.moe_stream_prefetch.argtypes = [ctypes.POINTER(Streamer), i32, vp, i32, i32, i32, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def make_desc(*, hidden, n_experts, top_k, inter, n_shared, bits, group=64, rms_eps=1e-6, router_w, gamma,
+              experts=None, shared=None, slab=None, blob_bytes=None) -> LayerDesc:
+    bb = blob_bytes if blob_bytes is not None else moe_blob_bytes(hidden, inter, bits, group)
+    return LayerDesc(hidden, n_experts, top_k, inter, n_shared, bits, group, rms_eps, _ptr(router_w), _ptr(gamma),
+                     _ptr(experts), _ptr(shared), _ptr(slab), bb)
+
+
+def moe_blob_bytes(hidden: int, inter: int, bits: int, group: int = 64) -> int:
+    return int(lib().moe_blob_bytes(hidden, inter, bits, group))
+
+
+def moe_workspace_bytes(desc: LayerDesc, n_tokens: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(desc), n_tokens))
+
+
+def moe_strerror(status: int) -> str:
+    return lib().moe_strerror(status).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_route(desc, x, n_tokens, topk_idx, topk_w, logits, workspace, stream=None, ws_bytes=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().moe_route(ctypes.byref(desc), _ptr(x), n_tokens, _ptr(topk_idx), _ptr(topk_w), _ptr(logits),
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_expert_forward(desc, x, n_tokens, topk_idx, topk_w, y, workspace, stream=None, ws_bytes=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().moe_expert_forward(ctypes.byref(desc), _ptr(x), n_tokens, _ptr(topk_idx), _ptr(topk_w), _ptr(y),
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_layer_step(desc, resid, x, n_tokens, topk_idx, topk_w, workspace, stream=None, ws_bytes=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().moe_layer_step(ctypes.byref(desc), _ptr(resid), _ptr(x), n_tokens, _ptr(topk_idx), _ptr(topk_w),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_layer_plan(desc, n_tokens: int = 1) -> dict:
+    out = (ctypes.c_int32 * 7)()
+    _check(lib().moe_layer_plan(ctypes.byref(desc), n_tokens, ctypes.cast(out, ctypes.c_void_p)))
+    keys = ("fused", "grid", "block", "per_cu", "n_cu", "vgprs", "scratch")
+    return dict(zip(keys, (int(v) for v in out)))
+
+
+def moe_stream_prefetch(streamer: Streamer, layer: int, expert_ids, slot: int, with_shared: bool, copy_stream,
+                        done_event=None) -> None:
+    ids = (ctypes.c_int32 * len(expert_ids))(*[int(e) for e in expert_ids])
+    ev = None if done_event is None else (done_event if isinstance(done_event, int) else done_event.cuda_event)
+    _check(lib().moe_stream_prefetch(ctypes.byref(streamer), layer, ctypes.cast(ids, ctypes.c_void_p),
+                                     len(expert_ids), slot, 1 if with_shared else 0, _stream(copy_stream), ev))

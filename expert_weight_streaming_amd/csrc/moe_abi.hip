@@ -1,0 +1,339 @@
+// moe_abi.hip -- libmoe's C entry points: validation, workspace layout,
+// launches, and the host->HBM expert streamer.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+uint64_t blob_bytes_of(int32_t D, int32_t I, int32_t bits, int32_t group)
+{
+    if (D <= 0 || I <= 0 || (bits != 2 && bits != 4) || group != moe::kGroup) return 0;
+    if (D % group || I % group) return 0;
+    const uint64_t n = 3ull * (uint64_t)D * (uint64_t)I;
+    return n * (uint64_t)bits / 8 + n / (uint64_t)group * 4;
+}
+
+int check_desc(const moe_layer_desc *d, int32_t T)
+{
+    if (!d) return fail(MOE_EINVAL, "desc is NULL");
+    if (d->group != moe::kGroup) return fail(MOE_EINVAL, "group must be 64 (got %d)", d->group);
+    if (d->bits != 2 && d->bits != 4) return fail(MOE_EINVAL, "bits must be 2 or 4 (got %d)", d->bits);
+    if (d->hidden <= 0 || d->hidden % 64 || d->hidden > 8192)
+        return fail(MOE_EINVAL, "hidden must be a positive multiple of 64, <= 8192 (got %d)", d->hidden);
+    if (d->inter <= 0 || d->inter % 64 || d->inter > 4096)
+        return fail(MOE_EINVAL, "inter must be a positive multiple of 64, <= 4096 (got %d)", d->inter);
+    if (d->n_experts <= 0 || d->n_experts > 4096)
+        return fail(MOE_EINVAL, "n_experts must be in [1, 4096] (got %d)", d->n_experts);
+    if (d->top_k < 1 || d->top_k > moe::kMaxTopK || d->top_k > d->n_experts)
+        return fail(MOE_EINVAL, "top_k must be in [1, min(n_experts, 8)] (got %d)", d->top_k);
+    if (d->n_shared != 0 && d->n_shared != 1) return fail(MOE_EINVAL, "n_shared must be 0 or 1");
+    if (!(d->rms_eps >= 0.f)) return fail(MOE_EINVAL, "rms_eps must be >= 0");
+    if (T < 1 || T > 64) return fail(MOE_EINVAL, "n_tokens must be in [1, 64] (got %d)", T);
+    if (d->blob_bytes != blob_bytes_of(d->hidden, d->inter, d->bits, d->group))
+        return fail(MOE_EINVAL, "blob_bytes %llu does not match the shape (%llu)", (unsigned long long)d->blob_bytes,
+                    (unsigned long long)blob_bytes_of(d->hidden, d->inter, d->bits, d->group));
+    if (!d->router_w || !aligned16(d->router_w)) return fail(MOE_EINVAL, "router_w NULL or not 16-byte aligned");
+    if (!d->gamma || !aligned16(d->gamma)) return fail(MOE_EINVAL, "gamma NULL or not 16-byte aligned");
+    const bool streamed = d->experts == nullptr;
+    if (streamed) {
+        if (!d->slab || !aligned16(d->slab)) return fail(MOE_EINVAL, "streamed mode needs a 16-byte aligned slab");
+        if (T != 1) return fail(MOE_EUNSUPPORTED, "streamed mode takes one token per call");
+    } else {
+        if (!aligned16(d->experts)) return fail(MOE_EINVAL, "experts not 16-byte aligned");
+        if (d->n_shared && (!d->shared || !aligned16(d->shared)))
+            return fail(MOE_EINVAL, "n_shared=1 needs a 16-byte aligned shared blob");
+    }
+    return MOE_OK;
+}
+
+int check_ptr(const void *p, const char *name)
+{
+    if (!p || !aligned16(p)) return fail(MOE_EINVAL, "%s NULL or not 16-byte aligned", name);
+    return MOE_OK;
+}
+
+int check_ptr4(const void *p, const char *name)
+{
+    if (!p || ((uintptr_t)p & 3u)) return fail(MOE_EINVAL, "%s NULL or not 4-byte aligned", name);
+    return MOE_OK;
+}
+
+moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
+{
+    moe::WsLayout L;
+    size_t off = 256;
+    L.logits = off;
+    off = round_up(off + (size_t)T * d->n_experts * 4, 256);
+    L.h = off;
+    off = round_up(off + (size_t)T * (d->top_k + d->n_shared) * d->inter * 4, 256);
+    L.ss = off;
+    const size_t nss = (size_t)moe::kMaxLayerBlocks > (size_t)moe::down_blocks(d->hidden, d->inter, d->bits)
+                           ? (size_t)moe::kMaxLayerBlocks
+                           : (size_t)moe::down_blocks(d->hidden, d->inter, d->bits);
+    off = round_up(off + nss * 4, 256);
+    L.total = off;
+    return L;
+}
+
+moe::BlobSrc blob_src(const moe_layer_desc *d)
+{
+    moe::BlobSrc s;
+    s.experts = d->experts;
+    s.shared = d->experts ? d->shared : nullptr;
+    s.slab = d->experts ? nullptr : d->slab;
+    s.blob_bytes = d->blob_bytes;
+    s.n_experts = d->n_experts;
+    s.top_k = d->top_k;
+    s.n_slots = d->top_k + d->n_shared;
+    return s;
+}
+
+int check_ws(const moe_layer_desc *d, int32_t T, void *ws, size_t ws_bytes)
+{
+    if (!ws || ((uintptr_t)ws & 255u)) return fail(MOE_EINVAL, "workspace NULL or not 256-byte aligned");
+    const size_t need = layout(d, T).total;
+    if (ws_bytes < need) return fail(MOE_EINVAL, "workspace too small: %zu < %zu", ws_bytes, need);
+    return MOE_OK;
+}
+
+int enqueue_route(const moe_layer_desc *d, const float *x, int32_t *idx, float *w, float *logits, uint8_t *ws,
+                  const moe::WsLayout &L, hipStream_t s)
+{
+    moe::RouteArgs a;
+    a.router = d->router_w;
+    a.x = x;
+    a.logits = logits ? logits : reinterpret_cast<float *>(ws + L.logits);
+    a.topk_idx = idx;
+    a.topk_w = w;
+    a.counter = reinterpret_cast<uint32_t *>(ws + L.ctr_route);
+    a.D = d->hidden;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    hipError_t e = moe::launch_route(a, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
+}
+
+// Gate/up then down + combine.  y != NULL: y = combine (no residual).
+// y == NULL: resid += combine, xout = RMSNorm(resid) * gamma.
+int enqueue_forward(const moe_layer_desc *d, const float *x, const int32_t *idx, const float *w, float *y,
+                    float *resid, float *xout, uint8_t *ws, const moe::WsLayout &L, hipStream_t s)
+{
+    moe::GateUpArgs g;
+    g.src = blob_src(d);
+    g.topk_idx = idx;
+    g.x = x;
+    g.h = reinterpret_cast<float *>(ws + L.h);
+    g.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    g.D = d->hidden;
+    g.I = d->inter;
+    g.blocks_per_slot = moe::gate_up_blocks_per_slot(d->inter);
+    hipError_t e = moe::launch_gate_up(g, d->bits, s);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+
+    moe::DownArgs a;
+    a.src = g.src;
+    a.topk_idx = idx;
+    a.topk_w = w;
+    a.h = g.h;
+    a.y = y;
+    a.resid = resid;
+    a.x = xout;
+    a.gamma = d->gamma;
+    a.ss = reinterpret_cast<float *>(ws + L.ss);
+    a.counter = reinterpret_cast<uint32_t *>(ws + L.ctr_down);
+    a.flags = g.flags;
+    a.D = d->hidden;
+    a.I = d->inter;
+    a.eps = d->rms_eps;
+    a.mode = y ? 0 : 1;
+    e = moe::launch_down(a, d->bits, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
+}
+
+int enqueue_layer(const moe_layer_desc *d, float *resid, float *x, int32_t *idx, float *w, uint8_t *ws,
+                  const moe::WsLayout &L, hipStream_t s)
+{
+    moe::LayerArgs a;
+    a.src = blob_src(d);
+    a.router = d->router_w;
+    a.gamma = d->gamma;
+    a.resid = resid;
+    a.x = x;
+    a.topk_idx = idx;
+    a.topk_w = w;
+    a.logits = reinterpret_cast<float *>(ws + L.logits);
+    a.h = reinterpret_cast<float *>(ws + L.h);
+    a.ss = reinterpret_cast<float *>(ws + L.ss);
+    a.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
+    a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    a.D = d->hidden;
+    a.E = d->n_experts;
+    a.K = d->top_k;
+    a.I = d->inter;
+    a.eps = d->rms_eps;
+    int grid = 0;
+    hipError_t e = moe::launch_layer(a, d->bits, s, &grid);
+    if (e == hipErrorNotSupported) {
+        // no scratch-free fused kernel for this shape: three launches
+        int rc = enqueue_route(d, x, idx, w, nullptr, ws, L, s);
+        if (rc) return rc;
+        return enqueue_forward(d, x, idx, w, nullptr, resid, x, ws, L, s);
+    }
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "layer launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_blob_bytes(int32_t hidden, int32_t inter, int32_t bits, int32_t group)
+{
+    return (size_t)blob_bytes_of(hidden, inter, bits, group);
+}
+
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens)
+{
+    if (check_desc(desc, n_tokens) != MOE_OK) return 0;
+    return layout(desc, n_tokens).total;
+}
+
+const char *moe_strerror(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported request";
+    case MOE_EHIP: return "HIP runtime error";
+    case MOE_ESTATE: return "streamer state error";
+    default: return "unknown status";
+    }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int moe_route(const moe_layer_desc *desc, const float *x, int32_t n_tokens, int32_t *topk_idx, float *topk_w,
+              float *logits, void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_desc(desc, n_tokens);
+    if (rc) return rc;
+    if ((rc = check_ptr(x, "x")) || (rc = check_ptr4(topk_idx, "topk_idx")) || (rc = check_ptr4(topk_w, "topk_w")))
+        return rc;
+    if (logits && ((uintptr_t)logits & 3u)) return fail(MOE_EINVAL, "logits not 4-byte aligned");
+    if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
+    if (n_tokens != 1) return fail(MOE_EUNSUPPORTED, "batched routing not built");
+    const moe::WsLayout L = layout(desc, n_tokens);
+    return enqueue_route(desc, x, topk_idx, topk_w, logits, (uint8_t *)workspace, L, (hipStream_t)stream);
+}
+
+int moe_expert_forward(const moe_layer_desc *desc, const float *x, int32_t n_tokens, const int32_t *topk_idx,
+                       const float *topk_w, float *y, void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_desc(desc, n_tokens);
+    if (rc) return rc;
+    if ((rc = check_ptr(x, "x")) || (rc = check_ptr4(topk_idx, "topk_idx")) || (rc = check_ptr4(topk_w, "topk_w")) ||
+        (rc = check_ptr(y, "y")))
+        return rc;
+    if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
+    if (n_tokens != 1) return fail(MOE_EUNSUPPORTED, "batched expert forward not built");
+    const moe::WsLayout L = layout(desc, n_tokens);
+    return enqueue_forward(desc, x, topk_idx, topk_w, y, nullptr, nullptr, (uint8_t *)workspace, L,
+                           (hipStream_t)stream);
+}
+
+int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n_tokens, int32_t *topk_idx,
+                   float *topk_w, void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_desc(desc, n_tokens);
+    if (rc) return rc;
+    if ((rc = check_ptr(resid, "resid")) || (rc = check_ptr(x, "x")) || (rc = check_ptr4(topk_idx, "topk_idx")) ||
+        (rc = check_ptr4(topk_w, "topk_w")))
+        return rc;
+    const size_t span = (size_t)n_tokens * desc->hidden * 4;
+    if ((const uint8_t *)resid < (const uint8_t *)x + span && (const uint8_t *)x < (const uint8_t *)resid + span)
+        return fail(MOE_EINVAL, "resid and x overlap");
+    if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
+    if (n_tokens != 1) return fail(MOE_EUNSUPPORTED, "batched layer step not built");
+    const moe::WsLayout L = layout(desc, n_tokens);
+    return enqueue_layer(desc, resid, x, topk_idx, topk_w, (uint8_t *)workspace, L, (hipStream_t)stream);
+}
+
+int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out)
+{
+    int rc = check_desc(desc, n_tokens);
+    if (rc) return rc;
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    moe::LayerPlan p;
+    hipError_t e = moe::plan_layer(desc->hidden, desc->inter, desc->bits, desc->top_k + desc->n_shared, &p);
+    if (e != hipSuccess) return hip_fail(e, "layer plan");
+    out[0] = p.grid > 0 && n_tokens == 1 ? 1 : 0;
+    out[1] = p.grid;
+    out[2] = p.block;
+    out[3] = p.per_cu;
+    out[4] = p.n_cu;
+    out[5] = p.vgprs;
+    out[6] = p.scratch;
+    return MOE_OK;
+}
+
+int moe_stream_prefetch(const moe_streamer *st, int32_t layer, const int32_t *expert_ids, int32_t n_ids,
+                        int32_t slot, int32_t with_shared, void *copy_stream, void *done_event)
+{
+    if (!st) return fail(MOE_ESTATE, "streamer is NULL");
+    if (!st->host_arena || st->arena_blobs <= 0) return fail(MOE_ESTATE, "no host arena registered");
+    if (with_shared && (!st->host_shared || st->shared_blobs <= 0)) return fail(MOE_ESTATE, "no shared arena registered");
+    if (slot != 0 && slot != 1) return fail(MOE_ESTATE, "slot must be 0 or 1 (got %d)", slot);
+    if (!st->slab[slot]) return fail(MOE_ESTATE, "slab slot %d is NULL", slot);
+    if (layer < 0 || layer >= st->n_layers) return fail(MOE_ESTATE, "layer %d out of range", layer);
+    if (st->blob_bytes == 0 || st->n_experts <= 0) return fail(MOE_ESTATE, "streamer shape unset");
+    if (n_ids < 0 || n_ids + (with_shared ? 1 : 0) > st->slab_blobs)
+        return fail(MOE_ESTATE, "%d ids (+shared) do not fit %d slab blobs", n_ids, st->slab_blobs);
+    if (n_ids > 0 && !expert_ids) return fail(MOE_ESTATE, "expert_ids is NULL");
+    for (int32_t j = 0; j < n_ids; ++j)
+        if (expert_ids[j] < 0 || expert_ids[j] >= st->n_experts)
+            return fail(MOE_ESTATE, "expert id %d out of range", expert_ids[j]);
+    hipStream_t cs = (hipStream_t)copy_stream;
+    const uint64_t bb = st->blob_bytes;
+    for (int32_t j = 0; j < n_ids; ++j) {
+        const int64_t pb = ((int64_t)layer * st->n_experts + expert_ids[j]) % st->arena_blobs;
+        hipError_t e = hipMemcpyAsync(st->slab[slot] + (uint64_t)j * bb, st->host_arena + (uint64_t)pb * bb, bb,
+                                      hipMemcpyHostToDevice, cs);
+        if (e != hipSuccess) return hip_fail(e, "expert copy");
+    }
+    if (with_shared) {
+        const int64_t pb = (int64_t)layer % st->shared_blobs;
+        hipError_t e = hipMemcpyAsync(st->slab[slot] + (uint64_t)(st->slab_blobs - 1) * bb,
+                                      st->host_shared + (uint64_t)pb * bb, bb, hipMemcpyHostToDevice, cs);
+        if (e != hipSuccess) return hip_fail(e, "shared copy");
+    }
+    if (done_event) {
+        hipError_t e = hipEventRecord((hipEvent_t)done_event, cs);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

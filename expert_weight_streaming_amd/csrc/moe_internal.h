@@ -1,0 +1,117 @@
+// moe_internal.h -- shared between libmoe's host entry points and kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 64;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxSlots = kMaxTopK + 1;  // routed + shared
+constexpr int kMaxLayerBlocks = 4096;    // grid cap of the fused layer kernel
+
+// Workspace layout (byte offsets), all 64-byte aligned.
+struct WsLayout {
+    size_t flags = 0;        // uint32 device error bits (OR-ed)
+    size_t ctr_route = 64;   // uint32 arrival counter of the route kernel
+    size_t bar = 128;        // uint32[2] grid-barrier counters of the fused layer kernel
+    size_t ctr_down = 192;   // uint32 arrival counter of the down kernel (layer mode)
+    size_t logits = 0;       // float [T][E]
+    size_t h = 0;            // float [T][slots][I]
+    size_t ss = 0;           // float [kMaxLayerBlocks]
+    size_t total = 0;
+};
+
+// Where the blobs of one layer live.
+struct BlobSrc {
+    const uint8_t *experts;  // resident arena (NULL when streamed)
+    const uint8_t *shared;   // resident shared blob (or NULL)
+    const uint8_t *slab;     // streamed slab (or NULL)
+    uint64_t blob_bytes;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t n_slots;         // top_k + n_shared
+};
+
+struct RouteArgs {
+    const float *router;     // [E][D]
+    const float *x;          // [D]
+    float *logits;           // [E]
+    int32_t *topk_idx;       // [K]
+    float *topk_w;           // [K]
+    uint32_t *counter;
+    int32_t D, E, K;
+};
+
+struct GateUpArgs {
+    BlobSrc src;
+    const int32_t *topk_idx; // [K]
+    const float *x;          // [D]
+    float *h;                // [slots][I]
+    uint32_t *flags;
+    int32_t D, I;
+    int32_t blocks_per_slot;
+};
+
+struct DownArgs {
+    BlobSrc src;
+    const int32_t *topk_idx; // [K]
+    const float *topk_w;     // [K]
+    const float *h;          // [slots][I]
+    float *y;                // [D] combine output (mode 0)
+    float *resid;            // [D] in/out (mode 1)
+    float *x;                // [D] out (mode 1)
+    const float *gamma;      // [D] (mode 1)
+    float *ss;               // [blocks] (mode 1)
+    uint32_t *counter;       // (mode 1)
+    uint32_t *flags;
+    int32_t D, I;
+    float eps;
+    int32_t mode;            // 0: y = combine; 1: resid += combine, x = RMSNorm(resid)
+};
+
+struct LayerArgs {
+    BlobSrc src;
+    const float *router;     // [E][D]
+    const float *gamma;      // [D]
+    float *resid;            // [D] in/out
+    float *x;                // [D] in/out
+    int32_t *topk_idx;       // [K] out
+    float *topk_w;           // [K] out
+    float *logits;           // [E] workspace
+    float *h;                // [slots][I] workspace
+    float *ss;               // [grid] workspace
+    uint32_t *bar;           // [2] workspace, zero between launches
+    uint32_t *flags;
+    int32_t D, E, K, I;
+    float eps;
+};
+
+// Down-projection lane split: LPR lanes per row (a power of two <= 64),
+// cpl 16-byte chunks per lane.
+struct DownShape {
+    int lpr, cpl;
+};
+DownShape down_shape(int I, int bits);
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_gate_up(const GateUpArgs &a, int bits, hipStream_t s);
+hipError_t launch_down(const DownArgs &a, int bits, hipStream_t s);
+// Fused single-launch layer step.  Returns hipErrorNotSupported (nothing
+// launched) when the instantiation for this shape needs scratch memory: its
+// blocks could then not all be resident at once for the grid barriers.
+hipError_t launch_layer(const LayerArgs &a, int bits, hipStream_t s, int *grid);
+
+// Launch plan of the fused layer kernel for a shape (nothing launched):
+// grid 0 when the shape takes the three-launch path.
+struct LayerPlan {
+    int grid = 0, block = 0, per_cu = 0, n_cu = 0, vgprs = 0, scratch = 0;
+};
+hipError_t plan_layer(int D, int I, int bits, int n_slots, LayerPlan *p);
+int down_blocks(int D, int I, int bits);
+int gate_up_blocks_per_slot(int I);
+
+}  // namespace moe

@@ -1,0 +1,241 @@
+// moe_kernels.hip -- the separately launched kernels of moe_route and
+// moe_expert_forward (batch 1):
+//   k_route      router GEMV (fp32) + top-K + softmax over the selection,
+//                the top-K done by the last workgroup to finish;
+//   k_gate_up    dequantised gate/up GEMV for every selected expert and the
+//                shared expert, SwiGLU fused, h kept in the workspace;
+//   k_down       dequantised down GEMV for all slots of one output row block,
+//                weighted combine in slot order.
+// moe_layer_step runs the same building blocks fused in one persistent
+// launch (moe_layer.hip).
+#include "moe_device.h"
+
+namespace moe {
+namespace {
+
+using namespace dev;
+
+// Router: one row per wave, 4 waves per block.  The last block to arrive
+// selects the top K and writes the weights.
+__global__ void __launch_bounds__(256) k_route(RouteArgs a)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    __shared__ int is_last;
+    if (row < a.E) {
+        const float acc = wave_router_row(a.router + (size_t)row * a.D, a.x, a.D, lane);
+        if (lane == 0) a.logits[row] = acc;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    __shared__ float lg[4096];
+    for (int e = tid; e < a.E; e += 256) lg[e] = a.logits[e];
+    __syncthreads();
+    if (wave == 0) {
+        int idx[kMaxTopK];
+        float vals[kMaxTopK], w[kMaxTopK];
+        wave_topk(lg, a.E, a.K, lane, idx, vals);
+        if (lane == 0) {
+            topk_weights(vals, a.K, w);
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                if (k >= a.K) continue;
+                a.topk_idx[k] = idx[k];
+                a.topk_w[k] = w[k];
+            }
+            *a.counter = 0u;
+        }
+    }
+}
+
+constexpr int kGateUpRows = 2;  // rows per wave
+
+template <int BITS, int CPL>
+__global__ void __launch_bounds__(256) k_gate_up(GateUpArgs a)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = blockIdx.x / a.blocks_per_slot;
+    const int rb = blockIdx.x - slot * a.blocks_per_slot;
+    const int i0 = (rb * 4 + wave) * kGateUpRows;
+    if (i0 >= a.I) return;
+    const int32_t e = slot < a.src.top_k && !a.src.slab ? a.topk_idx[slot] : -1;
+    const uint8_t *blob = blob_of(a.src, slot, e, a.flags);
+    float *h = a.h + (size_t)slot * a.I;
+    if (!blob) {
+        if (lane < kGateUpRows && i0 + lane < a.I) h[i0 + lane] = 0.f;
+        return;
+    }
+    wave_gate_up<BITS, CPL, kGateUpRows>(blob, a.x, a.D, a.I, i0, lane, h);
+}
+
+// Down + combine: one block per RW output rows, one wave per slot.  Partial
+// rows meet in LDS and are summed in slot order (routed 0..K-1, then shared).
+// Layer mode adds the residual, keeps a per-block sum of squares, and the
+// last block to arrive applies RMSNorm to every row.
+template <int BITS, int LPR, int CPL, int STEPS>
+__global__ void __launch_bounds__(64 * kMaxSlots) k_down(DownArgs a)
+{
+    constexpr int RPS = 64 / LPR;
+    constexpr int RW = RPS * STEPS;
+    static_assert(RW <= 64, "one wave finishes the rows");
+    const int tid = threadIdx.x, lane = tid & 63, k = tid >> 6;
+    const int o0 = blockIdx.x * RW;
+    __shared__ float part[kMaxSlots][RW];
+    __shared__ int is_last;
+    __shared__ float inv_s;
+
+    const int32_t e = k < a.src.top_k && !a.src.slab ? a.topk_idx[k] : -1;
+    const uint8_t *blob = blob_of(a.src, k, e, a.flags);
+    const float wk = k < a.src.top_k ? a.topk_w[k] : 1.f;
+    float out[STEPS];
+    wave_down<BITS, LPR, CPL, STEPS>(blob, a.h + (size_t)k * a.I, a.D, a.I, o0, lane, out);
+    if (lane % LPR == 0) {
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) part[k][s * RPS + lane / LPR] = blob ? wk * out[s] : 0.f;
+    }
+    __syncthreads();
+    if (k == 0) {
+        const int o = o0 + lane;
+        float v = 0.f;
+        if (lane < RW && o < a.D) {
+            float c = 0.f;
+            for (int j = 0; j < a.src.n_slots; ++j) c += part[j][lane];
+            if (a.mode == 0) {
+                a.y[o] = c;
+            } else {
+                const float r = a.resid[o] + c;
+                a.resid[o] = r;
+                v = r * r;
+            }
+        }
+        if (a.mode == 1) {
+            v = group_sum<64>(v);
+            if (lane == 0) a.ss[blockIdx.x] = v;
+        }
+    }
+    if (a.mode == 0) return;
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (k == 0) {
+        float t = 0.f;
+        for (int b = lane; b < (int)gridDim.x; b += 64) t += a.ss[b];
+        t = group_sum<64>(t);
+        if (lane == 0) {
+            inv_s = 1.f / sqrtf(t / (float)a.D + a.eps);
+            *a.counter = 0u;
+        }
+    }
+    __syncthreads();
+    const float inv = inv_s;
+    for (int o = tid; o < a.D; o += blockDim.x) a.x[o] = a.resid[o] * inv * a.gamma[o];
+}
+
+template <int BITS, int CPL>
+hipError_t gate_up_cpl(const GateUpArgs &a, hipStream_t s)
+{
+    dim3 grid(a.blocks_per_slot * a.src.n_slots);
+    hipLaunchKernelGGL((k_gate_up<BITS, CPL>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t gate_up_bits(const GateUpArgs &a, hipStream_t s)
+{
+    const int cpl = (a.D * BITS / 128 + 63) / 64;  // hidden <= 8192: 4-bit <= 4, 2-bit <= 2
+    if (cpl <= 1) return gate_up_cpl<BITS, 1>(a, s);
+    if constexpr (BITS == 2) return gate_up_cpl<BITS, 2>(a, s);
+    else {
+        if (cpl <= 2) return gate_up_cpl<BITS, 2>(a, s);
+        return gate_up_cpl<BITS, 4>(a, s);
+    }
+}
+
+template <int BITS, int LPR, int CPL, int STEPS>
+hipError_t down_launch(const DownArgs &a, hipStream_t s)
+{
+    constexpr int RW = (64 / LPR) * STEPS;
+    dim3 grid((a.D + RW - 1) / RW);
+    hipLaunchKernelGGL((k_down<BITS, LPR, CPL, STEPS>), grid, dim3(64 * a.src.n_slots), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BITS, int LPR>
+hipError_t down_lpr(const DownArgs &a, int cpl, hipStream_t s)
+{
+    constexpr int STEPS = (16 * LPR / 64) < 1 ? 1 : ((16 * LPR / 64) > 8 ? 8 : (16 * LPR / 64));
+    if (cpl <= 1) return down_launch<BITS, LPR, 1, STEPS>(a, s);
+    return down_launch<BITS, LPR, 2, STEPS>(a, s);
+}
+
+template <int BITS>
+hipError_t down_bits(const DownArgs &a, hipStream_t s)
+{
+    const DownShape d = down_shape(a.I, BITS);
+    switch (d.lpr) {
+    case 1: return down_lpr<BITS, 1>(a, d.cpl, s);
+    case 2: return down_lpr<BITS, 2>(a, d.cpl, s);
+    case 4: return down_lpr<BITS, 4>(a, d.cpl, s);
+    case 8: return down_lpr<BITS, 8>(a, d.cpl, s);
+    case 16: return down_lpr<BITS, 16>(a, d.cpl, s);
+    case 32: return down_lpr<BITS, 32>(a, d.cpl, s);
+    default: return down_lpr<BITS, 64>(a, d.cpl, s);
+    }
+}
+
+}  // namespace
+
+DownShape down_shape(int I, int bits)
+{
+    const int nchunks = I * bits / 128;
+    int lpr = 1;
+    while (lpr * 2 <= nchunks && lpr < 64) lpr *= 2;
+    DownShape d;
+    d.lpr = lpr;
+    d.cpl = (nchunks + lpr - 1) / lpr;
+    return d;
+}
+
+int gate_up_blocks_per_slot(int I) { return (I + 4 * kGateUpRows - 1) / (4 * kGateUpRows); }
+
+int down_blocks(int D, int I, int bits)
+{
+    const DownShape d = down_shape(I, bits);
+    int steps = 16 * d.lpr / 64;
+    steps = steps < 1 ? 1 : (steps > 8 ? 8 : steps);
+    const int rw = (64 / d.lpr) * steps;
+    return (D + rw - 1) / rw;
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_route, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up(const GateUpArgs &a, int bits, hipStream_t s)
+{
+    return bits == 4 ? gate_up_bits<4>(a, s) : gate_up_bits<2>(a, s);
+}
+
+hipError_t launch_down(const DownArgs &a, int bits, hipStream_t s)
+{
+    return bits == 4 ? down_bits<4>(a, s) : down_bits<2>(a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,213 @@
+/*
+ * moe.h -- C ABI of libmoe: the per-token sparse MoE block of a
+ * "streaming experts" decode engine, on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the pages' statement of the per-layer problem (the
+ * Flash-MoE engine as described on toolarium.ru and hakusoku.com):
+ *   route    -- the router picks K of E experts per token and layer
+ *               (toolarium.ru, "Mixture of Experts и почему SSD достаточно";
+ *               softmax/topK step in hakusoku.com, "パイプライン概要");
+ *   fetch    -- the K selected experts' weights are brought to the GPU
+ *               (toolarium.ru, "Flash-MoE: чистый C, Metal и никакого
+ *               Python": parallel reads of ~6.75 MB per expert);
+ *   forward  -- dequantised expert FFNs (gate, up, SwiGLU, down) for the
+ *               selected experts plus the shared expert, weighted combine,
+ *               residual add and RMSNorm in one pass whose output feeds the
+ *               next layer (hakusoku.com, "主要技術"; toolarium.ru,
+ *               "Оптимизации, которые сработали").
+ *
+ * Conventions (all calls):
+ *  - Status: MOE_OK (0) or a negative MOE_E* code.  On an error nothing has
+ *    been enqueued.  moe_last_error() gives a message for the calling thread.
+ *  - Memory: every buffer belongs to the caller.  The library allocates and
+ *    frees nothing.  Pointers are device pointers unless marked "host".
+ *  - Asynchrony: calls enqueue work on the given HIP stream (passed as
+ *    void*, a hipStream_t; NULL = the legacy default stream) and return;
+ *    results are valid once the stream has been synchronised.  No call
+ *    synchronises the device, except where stated.
+ *  - Dtypes: activations, router weights, gamma and routing weights are fp32;
+ *    expert weights are packed unsigned codes with bf16 group scale/bias
+ *    inside the canonical blob (below); indices are int32.
+ *  - Validation happens on the host before anything is enqueued: non-NULL
+ *    pointers, 16-byte aligned for activations, weights and blobs and 4-byte
+ *    aligned for topk_idx / topk_w / logits, a 256-byte aligned workspace,
+ *    bits in {2,4}, group == 64, hidden and
+ *    inter multiples of 64 (hidden <= 8192, inter <= 4096), 1 <= top_k <=
+ *    min(n_experts, 8), n_experts <= 4096, 1 <= n_tokens <= 64, and
+ *    blob_bytes == moe_blob_bytes(...).
+ *  - Device-side faults: an expert index outside [0, n_experts) met on the
+ *    device sets bit MOE_DEVERR_EXPERT_RANGE in workspace word 0 and that
+ *    expert's contribution is skipped; a grid-wide wait inside a fused layer
+ *    step that does not complete within a few seconds sets
+ *    MOE_DEVERR_BARRIER_TIMEOUT and the kernel runs to its end (its results
+ *    are then invalid).  Word 0 is only ever OR-ed into.
+ *  - Thread safety: calls are reentrant.  Two calls that share a workspace
+ *    must be ordered on one stream (they reuse its scratch and counters).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* bad shape, pointer or alignment; nothing enqueued  */
+#define MOE_EUNSUPPORTED (-2)  /* valid request that this build does not implement    */
+#define MOE_EHIP (-3)          /* HIP runtime error; moe_last_error() has the text    */
+#define MOE_ESTATE (-4)        /* streamer misuse: bad slot, layer or id, no arena    */
+
+#define MOE_DEVERR_EXPERT_RANGE 1u   /* an expert index outside [0, n_experts) */
+#define MOE_DEVERR_BARRIER_TIMEOUT 2u /* a grid-wide wait of a fused layer step timed out */
+
+/*
+ * Canonical expert blob (one contiguous byte range per expert; the unit the
+ * pages stream, about 6.75 MB per expert at 4-bit, toolarium.ru "Flash-MoE:
+ * чистый C, Metal и никакого Python"):
+ *
+ *   [gate.q | up.q | down.q | gate.sb | up.sb | down.sb]
+ *
+ * gate and up: [inter rows][hidden cols]; down: [hidden rows][inter cols];
+ * all row-major.  q regions: element c of a row is held at bit offset c*bits
+ * of that row, in little-endian 32-bit words, lowest bits first; codes are
+ * unsigned in [0, 2^bits).  sb regions: one 32-bit word per group of 64
+ * consecutive columns of a row: bf16 scale in bits 0..15, bf16 bias in bits
+ * 16..31.  The dequantised weight is w = q*scale + bias (toolarium.ru,
+ * "Оптимизации, которые сработали": nibble*scale + bias).
+ *
+ * Returns 3*hidden*inter*bits/8 + 3*hidden*inter/group*4, or 0 for invalid
+ * arguments.  hidden=4096, inter=1024, bits=4, group=64 gives 7,077,888 B.
+ */
+size_t moe_blob_bytes(int32_t hidden, int32_t inter, int32_t bits, int32_t group);
+
+/* One MoE layer.  Plain data, owned by the caller. */
+typedef struct moe_layer_desc {
+    int32_t hidden;        /* D */
+    int32_t n_experts;     /* E routed experts */
+    int32_t top_k;         /* K selected per token */
+    int32_t inter;         /* I, expert intermediate size */
+    int32_t n_shared;      /* 0 or 1 always-active shared expert (hakusoku.com, "モデルアーキテクチャ") */
+    int32_t bits;          /* 4 or 2 */
+    int32_t group;         /* 64 */
+    float rms_eps;         /* RMSNorm epsilon, inside the square root */
+    const float *router_w; /* [E][D] fp32 row-major */
+    const float *gamma;    /* [D] fp32 RMSNorm weight */
+    /* Resident mode: E canonical blobs, blob_bytes apart, expert e at
+     * experts + e*blob_bytes, and the shared blob at `shared`.
+     * Streamed mode: experts == NULL and slab != NULL: slab holds top_k+1
+     * blobs, blob_bytes apart: slot k = the token's k-th selected expert,
+     * slot top_k = the shared expert (streamed mode needs n_tokens == 1). */
+    const uint8_t *experts;
+    const uint8_t *shared;
+    const uint8_t *slab;
+    uint64_t blob_bytes;   /* must equal moe_blob_bytes(hidden, inter, bits, group) */
+} moe_layer_desc;
+
+/* Workspace bytes that moe_route / moe_expert_forward / moe_layer_step need
+ * for this layer shape and token count (0 for an invalid descriptor).
+ * The caller zero-fills a workspace once after allocating it; every call
+ * leaves its internal counters at zero again when its kernels finish. */
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens);
+
+/* Human-readable text of a status code; static storage. */
+const char *moe_strerror(int status);
+/* Text of the calling thread's most recent error; thread-local storage. */
+const char *moe_last_error(void);
+
+/*
+ * Routing (toolarium.ru, "Mixture of Experts и почему SSD достаточно";
+ * hakusoku.com, "パイプライン概要": softmax over the router logits, top-K).
+ * For each token t:
+ *   logits[t][e] = sum_d router_w[e][d] * x[t][d]
+ *   topk_idx[t][0..K) = the K largest logits in descending order, the lower
+ *                       expert index first on an exact tie
+ *   topk_w[t][k] = softmax over all E logits renormalised over the K
+ *                  selected (= exp(l_k - l_max) / sum_j exp(l_j - l_max))
+ * x: [T][D]; topk_idx: [T][K] int32; topk_w: [T][K]; logits: [T][E] or
+ * NULL (then kept in the workspace).
+ */
+int moe_route(const moe_layer_desc *desc, const float *x, int32_t n_tokens, int32_t *topk_idx,
+              float *topk_w, float *logits, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Expert forward and combine, no residual (hakusoku.com, "主要技術": 4/2-bit
+ * dequant matvec, SwiGLU, MoE combine):
+ *   E_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)),  silu(z) = z / (1 + exp(-z))
+ *   y[t] = sum_k topk_w[t][k] * E_{topk_idx[t][k]}(x[t]) + S(x[t])
+ * where S is the shared expert (weight 1; absent when n_shared == 0).
+ * x, y: [T][D]; topk_idx, topk_w: [T][K] as produced by moe_route (or any
+ * caller-chosen routing).
+ */
+int moe_expert_forward(const moe_layer_desc *desc, const float *x, int32_t n_tokens,
+                       const int32_t *topk_idx, const float *topk_w, float *y, void *workspace,
+                       size_t ws_bytes, void *stream);
+
+/*
+ * One whole layer: route, expert forward and combine, then residual add and
+ * RMSNorm fused (toolarium.ru, "Оптимизации, которые сработали": combine +
+ * residual + normalisation in one GPU kernel; hakusoku.com, "主要技術": the
+ * result goes straight to the next layer):
+ *   c = moe_expert_forward(route(x))
+ *   resid <- resid + c
+ *   x <- resid / sqrt(mean_d(resid^2) + rms_eps) * gamma
+ * resid, x: [T][D], in/out, must not overlap.  topk_idx/topk_w: [T][K]
+ * outputs (the routing used).
+ */
+int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n_tokens,
+                   int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * How moe_layer_step will run this layer on the current device (queries the
+ * device, enqueues nothing).  out[7] (host) receives: fused (1 when the step
+ * is one persistent launch with grid-wide barriers, 0 when it is three
+ * launches: route, gate/up, down + norm), grid blocks, block threads, blocks
+ * per CU the device reports for the fused kernel, CU count, VGPRs per lane,
+ * scratch bytes per lane.
+ */
+int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out);
+
+/*
+ * Host-to-HBM expert streaming (toolarium.ru, "Flash-MoE: чистый C, Metal и
+ * никакого Python": per layer, the selected experts' weights are read in
+ * parallel and handed to the GPU; hakusoku.com, "パイプライン概要": the K=4
+ * reads sit between routing and the expert forward).
+ *
+ * The expert weights live in pinned host memory; two device slab slots of
+ * slab_blobs blobs each receive one layer's selections while the other slot
+ * is being computed on.
+ */
+typedef struct moe_streamer {
+    const uint8_t *host_arena;  /* host, pinned: routed blobs, blob_bytes apart */
+    const uint8_t *host_shared; /* host, pinned: shared blobs, blob_bytes apart, or NULL */
+    uint64_t blob_bytes;
+    int32_t n_experts;          /* E */
+    int32_t n_layers;
+    /* Physical blobs in the arenas.  (layer, e) lives at arena blob
+     * (layer*E + e) mod arena_blobs and layer's shared blob at shared blob
+     * layer mod shared_blobs; arena_blobs = n_layers*E means no aliasing. */
+    int64_t arena_blobs;
+    int64_t shared_blobs;
+    uint8_t *slab[2];           /* device: two slots of slab_blobs blobs */
+    int32_t slab_blobs;         /* blobs per slot (top_k + 1) */
+} moe_streamer;
+
+/*
+ * Enqueue host->device copies of layer `layer`'s experts expert_ids[0..n_ids)
+ * (host array, read before the call returns) into slab[slot] blobs 0..n_ids,
+ * plus, when with_shared != 0, the layer's shared blob into blob
+ * slab_blobs-1 of the slot, all on copy_stream; then record done_event
+ * (a hipEvent_t, may be NULL) on copy_stream.  Ids out of range, n_ids >
+ * slab_blobs - (with_shared != 0), a bad slot or layer, or a missing arena
+ * return MOE_ESTATE before anything is enqueued.  The caller orders the
+ * copy after the last kernel that read the slot (e.g. hipStreamWaitEvent).
+ */
+int moe_stream_prefetch(const moe_streamer *s, int32_t layer, const int32_t *expert_ids, int32_t n_ids,
+                        int32_t slot, int32_t with_shared, void *copy_stream, void *done_event);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -38,7 +38,7 @@ def build(force: bool = False) -> None:
         os.replace(_HOST_SO + ".tmp", _HOST_SO)
     if force or not os.path.exists(_DEV_SO):
         subprocess.check_call(
-            ["hipcc", "-O3", "--offload-arch=gfx950", "-fPIC", "-shared",
+            ["hipcc", "-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              os.path.join(_HERE, "seedgen_dev.hip"), "-o", _DEV_SO + ".tmp"])
         os.replace(_DEV_SO + ".tmp", _DEV_SO)

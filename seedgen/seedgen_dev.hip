@@ -4,8 +4,8 @@
 // that multi-GB expert arenas need not cross PCIe.  It holds no MoE
 // arithmetic: SplitMix64 outputs (Steele, Lea, Flood, OOPSLA 2014) used
 // counter-style, uniform draws rounded to bf16.  Every fp32 step of the
-// uniform mapping is an explicitly rounded multiply or add, matching the
-// host's -ffp-contract=off build.
+// uniform mapping is a separately rounded multiply and add (contraction off
+// here and in the build flags), matching the host's -ffp-contract=off build.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +39,7 @@ __device__ inline uint32_t bf16_rne(float f)
 
 __device__ inline float unif24(uint32_t u24, float lo, float width)
 {
+#pragma clang fp contract(off)
     float t = __fmul_rn((float)u24, 1.0f / 16777216.0f);
     return __fadd_rn(lo, __fmul_rn(t, width));
 }

@@ -1,0 +1,102 @@
+"""The C ABI: libmoe.so loads, exports every symbol include/moe.h declares,
+and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_weight_streaming_amd as ews
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_matches_binding():
+    assert _declared() == sorted(ews.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(ews._SO)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_blob_bytes():
+    assert ews.moe_blob_bytes(4096, 1024, 4, 64) == 7077888
+    assert ews.moe_blob_bytes(4096, 1024, 2, 64) == 3932160
+    assert ews.moe_blob_bytes(256, 128, 4, 64) == 55296
+    assert ews.moe_blob_bytes(4096, 1024, 3, 64) == 0
+    assert ews.moe_blob_bytes(4096, 1000, 4, 64) == 0
+    assert ews.moe_blob_bytes(4096, 1024, 4, 32) == 0
+
+
+def _desc(**kw):
+    base = dict(hidden=256, n_experts=16, top_k=2, inter=128, n_shared=1, bits=4, router_w=4096, gamma=8192,
+                experts=16384, shared=32768)
+    base.update(kw)
+    return ews.make_desc(**base)
+
+
+def test_workspace_bytes():
+    d = _desc()
+    n = ews.moe_workspace_bytes(d, 1)
+    assert n > 0 and n % 256 == 0
+    assert ews.moe_workspace_bytes(_desc(bits=3), 1) == 0
+    assert ews.moe_workspace_bytes(_desc(top_k=17), 1) == 0
+    assert ews.moe_workspace_bytes(_desc(top_k=9, n_experts=32), 1) == 0
+    assert ews.moe_workspace_bytes(d, 0) == 0
+
+
+@pytest.mark.parametrize("bad", [dict(bits=3), dict(group=32), dict(hidden=100), dict(inter=0), dict(top_k=0),
+                                 dict(top_k=17), dict(n_shared=2), dict(router_w=4097), dict(gamma=None),
+                                 dict(experts=16385), dict(shared=None), dict(blob_bytes=12345),
+                                 dict(experts=None, slab=None), dict(n_experts=5000)])
+def test_bad_descriptor_rejected(bad):
+    d = _desc(**bad)
+    L = ews.lib()
+    rc = L.moe_route(ctypes.byref(d), 65536, 1, 65536, 65536, None, 65536 * 4, 1 << 20, None)
+    assert rc == ews.MOE_EINVAL, (bad, rc, ews.moe_last_error())
+    assert ews.moe_last_error()
+
+
+def test_bad_buffers_rejected():
+    d = _desc()
+    L = ews.lib()
+    ws = ews.moe_workspace_bytes(d, 1)
+    assert L.moe_route(ctypes.byref(d), None, 1, 65536, 65536, None, 1 << 20, ws, None) == ews.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), 65540, 1, 65536, 65536, None, 1 << 20, ws, None) == ews.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), 65536, 1, 65536, 65536, None, (1 << 20) + 16, ws, None) == ews.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), 65536, 1, 65536, 65536, None, 1 << 20, ws - 1, None) == ews.MOE_EINVAL
+    assert L.moe_route(ctypes.byref(d), 65536, 0, 65536, 65536, None, 1 << 20, ws, None) == ews.MOE_EINVAL
+    assert L.moe_expert_forward(ctypes.byref(d), 65536, 1, 65536, 65536, None, 1 << 20, ws, None) == ews.MOE_EINVAL
+    # resid and x overlapping
+    assert L.moe_layer_step(ctypes.byref(d), 65536, 65536 + 512, 1, 4096, 4096, 1 << 20, ws, None) == ews.MOE_EINVAL
+    assert L.moe_layer_step(None, 65536, 1 << 19, 1, 4096, 4096, 1 << 20, ws, None) == ews.MOE_EINVAL
+
+
+def test_streamer_misuse_rejected():
+    st = ews.Streamer()
+    L = ews.lib()
+    ids = (ctypes.c_int32 * 4)(0, 1, 2, 3)
+    ip = ctypes.cast(ids, ctypes.c_void_p)
+    assert L.moe_stream_prefetch(ctypes.byref(st), 0, ip, 4, 0, 1, None, None) == ews.MOE_ESTATE  # no arena
+    st.host_arena, st.host_shared, st.blob_bytes = 4096, 8192, 7077888
+    st.n_experts, st.n_layers, st.arena_blobs, st.shared_blobs, st.slab_blobs = 512, 60, 30720, 60, 5
+    st.slab[0], st.slab[1] = 1 << 20, 1 << 21
+    assert L.moe_stream_prefetch(ctypes.byref(st), 0, ip, 4, 2, 1, None, None) == ews.MOE_ESTATE  # slot
+    assert L.moe_stream_prefetch(ctypes.byref(st), 60, ip, 4, 0, 1, None, None) == ews.MOE_ESTATE  # layer
+    assert L.moe_stream_prefetch(ctypes.byref(st), 0, ip, 5, 0, 1, None, None) == ews.MOE_ESTATE   # too many
+    bad = (ctypes.c_int32 * 4)(0, 1, 512, 3)
+    assert L.moe_stream_prefetch(ctypes.byref(st), 0, ctypes.cast(bad, ctypes.c_void_p), 4, 0, 1, None,
+                                 None) == ews.MOE_ESTATE
+    assert L.moe_stream_prefetch(None, 0, ip, 4, 0, 1, None, None) == ews.MOE_ESTATE
+
+
+def test_strerror():
+    for s in (0, -1, -2, -3, -4):
+        assert ews.moe_strerror(s)

@@ -95,6 +95,8 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
                            ? (size_t)moe::kMaxLayerBlocks
                            : (size_t)moe::down_blocks(d->hidden, d->inter, d->bits);
     off = round_up(off + nss * 4, 256);
+    L.slots = off;
+    off = round_up(off + (size_t)moe::kMaxLayerBlocks * moe::kSlotWords * 4, 256);
     L.total = off;
     return L;
 }
@@ -150,7 +152,7 @@ int enqueue_forward(const moe_layer_desc *d, const float *x, const int32_t *idx,
     g.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
     g.D = d->hidden;
     g.I = d->inter;
-    g.blocks_per_slot = moe::gate_up_blocks_per_slot(d->inter);
+    g.blocks_per_slot = moe::gate_up_blocks_per_slot(d->inter, d->top_k + d->n_shared);
     hipError_t e = moe::launch_gate_up(g, d->bits, s);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
 
@@ -188,7 +190,8 @@ int enqueue_layer(const moe_layer_desc *d, float *resid, float *x, int32_t *idx,
     a.logits = reinterpret_cast<float *>(ws + L.logits);
     a.h = reinterpret_cast<float *>(ws + L.h);
     a.ss = reinterpret_cast<float *>(ws + L.ss);
-    a.bar = reinterpret_cast<uint32_t *>(ws + L.bar);
+    a.hdr = reinterpret_cast<uint32_t *>(ws + L.hdr);
+    a.slots = reinterpret_cast<uint32_t *>(ws + L.slots);
     a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
     a.D = d->hidden;
     a.E = d->n_experts;

@@ -11,17 +11,19 @@ namespace moe {
 constexpr int kGroup = 64;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxSlots = kMaxTopK + 1;  // routed + shared
-constexpr int kMaxLayerBlocks = 4096;    // grid cap of the fused layer kernel
+constexpr int kMaxLayerBlocks = 1024;    // grid cap of the fused layer kernel
+constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
 
 // Workspace layout (byte offsets), all 64-byte aligned.
 struct WsLayout {
     size_t flags = 0;        // uint32 device error bits (OR-ed)
     size_t ctr_route = 64;   // uint32 arrival counter of the route kernel
-    size_t bar = 128;        // uint32[2] grid-barrier counters of the fused layer kernel
+    size_t hdr = 128;        // uint32 grid size of the fused layer kernel last run on this workspace
     size_t ctr_down = 192;   // uint32 arrival counter of the down kernel (layer mode)
     size_t logits = 0;       // float [T][E]
     size_t h = 0;            // float [T][slots][I]
     size_t ss = 0;           // float [kMaxLayerBlocks]
+    size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the fused kernel
     size_t total = 0;
 };
 
@@ -84,7 +86,8 @@ struct LayerArgs {
     float *logits;           // [E] workspace
     float *h;                // [slots][I] workspace
     float *ss;               // [grid] workspace
-    uint32_t *bar;           // [2] workspace, zero between launches
+    uint32_t *hdr;           // workspace: grid of the last fused launch (0: none yet)
+    uint32_t *slots;         // workspace: per-block barrier epochs
     uint32_t *flags;
     int32_t D, E, K, I;
     float eps;
@@ -112,6 +115,6 @@ struct LayerPlan {
 };
 hipError_t plan_layer(int D, int I, int bits, int n_slots, LayerPlan *p);
 int down_blocks(int D, int I, int bits);
-int gate_up_blocks_per_slot(int I);
+int gate_up_blocks_per_slot(int I, int n_slots);
 
 }  // namespace moe

@@ -24,9 +24,9 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
     __shared__ int is_last;
     if (row < a.E) {
         const float acc = wave_router_row(a.router + (size_t)row * a.D, a.x, a.D, lane);
-        if (lane == 0) a.logits[row] = acc;
+        if (lane == 0) xstore(a.logits + row, acc);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -34,10 +34,9 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
     }
     __syncthreads();
     if (!is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     __shared__ float lg[4096];
-    for (int e = tid; e < a.E; e += 256) lg[e] = a.logits[e];
+    for (int e = tid; e < a.E; e += 256) lg[e] = xload(a.logits + e);
     __syncthreads();
     if (wave == 0) {
         int idx[kMaxTopK];
@@ -56,24 +55,37 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
     }
 }
 
-constexpr int kGateUpRows = 2;  // rows per wave
+constexpr int kGateUpRows = 2;  // rows per wave unit
 
+// Gate/up: blocks_per_slot blocks per slot, each staging x and its digit
+// table in LDS once and then walking its share of the slot's rows in wave
+// units of kGateUpRows rows.
 template <int BITS, int CPL>
 __global__ void __launch_bounds__(256) k_gate_up(GateUpArgs a)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = blockIdx.x / a.blocks_per_slot;
     const int rb = blockIdx.x - slot * a.blocks_per_slot;
-    const int i0 = (rb * 4 + wave) * kGateUpRows;
-    if (i0 >= a.I) return;
+    __shared__ __align__(16) float xs[8192];
+    __shared__ __align__(16) int dig[8192 / 32 * 24];
+    __shared__ float csum[8192 / 32];
+    __shared__ float red[16];
+    for (int d = threadIdx.x; d < a.D; d += blockDim.x) xs[d] = a.x[d];
+    __syncthreads();
+    const float inv = block_digit_table<BITS>(xs, a.D, dig, csum, red);
+
     const int32_t e = slot < a.src.top_k && !a.src.slab ? a.topk_idx[slot] : -1;
     const uint8_t *blob = blob_of(a.src, slot, e, a.flags);
     float *h = a.h + (size_t)slot * a.I;
-    if (!blob) {
-        if (lane < kGateUpRows && i0 + lane < a.I) h[i0 + lane] = 0.f;
-        return;
+    const int units = (a.I + kGateUpRows - 1) / kGateUpRows;
+    for (int u = rb * 4 + wave; u < units; u += a.blocks_per_slot * 4) {
+        const int i0 = u * kGateUpRows;
+        if (!blob) {
+            if (lane < kGateUpRows && i0 + lane < a.I) h[i0 + lane] = 0.f;
+            continue;
+        }
+        wave_gate_up<BITS, CPL, kGateUpRows>(blob, dig, csum, inv, a.D, a.I, i0, lane, h);
     }
-    wave_gate_up<BITS, CPL, kGateUpRows>(blob, a.x, a.D, a.I, i0, lane, h);
 }
 
 // Down + combine: one block per RW output rows, one wave per slot.  Partial
@@ -96,7 +108,7 @@ __global__ void __launch_bounds__(64 * kMaxSlots) k_down(DownArgs a)
     const uint8_t *blob = blob_of(a.src, k, e, a.flags);
     const float wk = k < a.src.top_k ? a.topk_w[k] : 1.f;
     float out[STEPS];
-    wave_down<BITS, LPR, CPL, STEPS>(blob, a.h + (size_t)k * a.I, a.D, a.I, o0, lane, out);
+    wave_down<BITS, LPR, CPL, STEPS, false>(blob, a.h + (size_t)k * a.I, a.D, a.I, o0, lane, out);
     if (lane % LPR == 0) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) part[k][s * RPS + lane / LPR] = blob ? wk * out[s] : 0.f;
@@ -112,18 +124,18 @@ __global__ void __launch_bounds__(64 * kMaxSlots) k_down(DownArgs a)
                 a.y[o] = c;
             } else {
                 const float r = a.resid[o] + c;
-                a.resid[o] = r;
+                xstore(a.resid + o, r);
                 v = r * r;
             }
         }
         if (a.mode == 1) {
             v = group_sum<64>(v);
-            if (lane == 0) a.ss[blockIdx.x] = v;
+            if (lane == 0) xstore(a.ss + blockIdx.x, v);
         }
     }
     if (a.mode == 0) return;
 
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -131,10 +143,9 @@ __global__ void __launch_bounds__(64 * kMaxSlots) k_down(DownArgs a)
     }
     __syncthreads();
     if (!is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (k == 0) {
         float t = 0.f;
-        for (int b = lane; b < (int)gridDim.x; b += 64) t += a.ss[b];
+        for (int b = lane; b < (int)gridDim.x; b += 64) t += xload(a.ss + b);
         t = group_sum<64>(t);
         if (lane == 0) {
             inv_s = 1.f / sqrtf(t / (float)a.D + a.eps);
@@ -142,8 +153,23 @@ __global__ void __launch_bounds__(64 * kMaxSlots) k_down(DownArgs a)
         }
     }
     __syncthreads();
+    // RMSNorm of every row: all loads of a thread first, then the stores
     const float inv = inv_s;
-    for (int o = tid; o < a.D; o += blockDim.x) a.x[o] = a.resid[o] * inv * a.gamma[o];
+    constexpr int kPer = 8;
+    for (int o0b = 0; o0b < a.D; o0b += (int)blockDim.x * kPer) {
+        float rv[kPer], gv[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int o = o0b + j * (int)blockDim.x + tid;
+            rv[j] = o < a.D ? xload(a.resid + o) : 0.f;
+            gv[j] = o < a.D ? a.gamma[o] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int o = o0b + j * (int)blockDim.x + tid;
+            if (o < a.D) a.x[o] = rv[j] * inv * gv[j];
+        }
+    }
 }
 
 template <int BITS, int CPL>
@@ -211,7 +237,14 @@ DownShape down_shape(int I, int bits)
     return d;
 }
 
-int gate_up_blocks_per_slot(int I) { return (I + 4 * kGateUpRows - 1) / (4 * kGateUpRows); }
+// About 512 blocks in all, each with at least one wave unit per wave.
+int gate_up_blocks_per_slot(int I, int n_slots)
+{
+    const int most = (I + 4 * kGateUpRows - 1) / (4 * kGateUpRows);
+    int b = 512 / (n_slots > 0 ? n_slots : 1);
+    if (b < 1) b = 1;
+    return b < most ? b : most;
+}
 
 int down_blocks(int D, int I, int bits)
 {

@@ -33,37 +33,43 @@ using namespace dev;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kMaxUnits = 8;  // phase-C row units per block
 
-__device__ inline void grid_sync(uint32_t *bar, uint32_t n, uint32_t nb, uint32_t *flags)
+// Grid barrier of one launch.  Every block owns a 64-byte slot holding an
+// epoch count; at barrier i a block publishes base + i in its slot and
+// waits until every slot of the grid has reached it.  The epochs carry over
+// from launch to launch (each launch adds 3), so no counter is ever reset
+// and no atomic read-modify-write is contended.  Before publishing, the
+// block waits for its own stores to complete; all data crossing a barrier
+// is stored and loaded agent-coherently (xstore / xload / xload4).
+struct GridBar {
+    uint32_t *slots;
+    uint32_t base;
+    uint32_t nb;
+    uint32_t *flags;
+};
+
+__device__ __forceinline__ void grid_sync(const GridBar &g, uint32_t i)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t target = n * nb;
+    const uint32_t target = g.base + i;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(g.slots + blockIdx.x * kSlotWords, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < 64) {
         uint32_t spins = 0;
-        while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        for (;;) {
+            bool ok = true;
+            for (uint32_t j = threadIdx.x; j < g.nb; j += 64)
+                ok &= (int32_t)(__hip_atomic_load(g.slots + j * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                target) >= 0;
+            if (__all(ok)) break;
             __builtin_amdgcn_s_sleep(1);
             if (++spins == kSpinLimit) {
-                atomicOr(flags, MOE_DEVERR_BARRIER_TIMEOUT);
+                atomicOr(g.flags, MOE_DEVERR_BARRIER_TIMEOUT);
                 break;
             }
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// Leave the launch: the last block out resets both counters for the next
-// launch on the stream (every block has finished waiting by then).
-__device__ inline void grid_exit(uint32_t *bar, uint32_t nb)
-{
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == nb - 1) {
-            __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(bar + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 template <int BITS, int GCPL, int R, int LPR, int DCPL, int STEPS, int MAXW>
@@ -78,16 +84,34 @@ __global__ void __launch_bounds__(64 * MAXW) k_layer(LayerArgs a)
     const int D = a.D, I = a.I, E = a.E, K = a.K;
     const BlobSrc &src = a.src;
 
+    using C = Codes<BITS>;
     __shared__ __align__(16) float xs[8192];
     __shared__ __align__(16) float lg[4096];
+    __shared__ __align__(16) int dig[8192 / C::CODES * C::DW];
+    __shared__ float csum[8192 / C::CODES];
+    __shared__ float red[16];
     __shared__ float part[kMaxSlots][RW];
     __shared__ float rsave[kMaxUnits][RW];
     __shared__ int sel[kMaxTopK];
     __shared__ float selw[kMaxTopK];
     __shared__ float inv_s;
 
+    // The barrier slots of a workspace belong to one grid size; a launch
+    // with another grid on the same workspace stops here.
+    const uint32_t hdr = __hip_atomic_load(a.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hdr != 0u && hdr != (uint32_t)NB) {
+        if (tid == 0 && blockIdx.x == 0) atomicOr(a.flags, MOE_DEVERR_WORKSPACE);
+        return;
+    }
+    GridBar g;
+    g.slots = a.slots;
+    g.base = __hip_atomic_load(a.slots + blockIdx.x * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g.nb = NB;
+    g.flags = a.flags;
+
     for (int d = tid; d < D; d += blockDim.x) xs[d] = a.x[d];
     __syncthreads();
+    const float xinv = block_digit_table<BITS>(xs, D, dig, csum, red);
 
     // ---- phase A: router rows + shared gate/up (routing-independent)
     const int gw = wave * NB + blockIdx.x, NW = W * NB;
@@ -97,16 +121,16 @@ __global__ void __launch_bounds__(64 * MAXW) k_layer(LayerArgs a)
     for (int u = gw; u < nA; u += NW) {
         if (u < E) {
             const float v = wave_router_row(a.router + (size_t)u * D, xs, D, lane);
-            if (lane == 0) a.logits[u] = v;
+            if (lane == 0) xstore(a.logits + u, v);
         } else {
-            wave_gate_up<BITS, GCPL, R>(blob_of(src, K, -1, a.flags), xs, D, I, (u - E) * R, lane,
+            wave_gate_up<BITS, GCPL, R>(blob_of(src, K, -1, a.flags), dig, csum, xinv, D, I, (u - E) * R, lane,
                                         a.h + (size_t)K * I);
         }
     }
-    grid_sync(a.bar, 1, NB, a.flags);
+    grid_sync(g, 1);
 
     // ---- phase B: top-K in every block, then routed gate/up
-    for (int e = tid; e < E; e += blockDim.x) lg[e] = a.logits[e];
+    for (int e = tid; e < E; e += blockDim.x) lg[e] = xload(a.logits + e);
     __syncthreads();
     if (wave == 0) {
         int idx[kMaxTopK];
@@ -132,12 +156,12 @@ __global__ void __launch_bounds__(64 * MAXW) k_layer(LayerArgs a)
         const uint8_t *blob = blob_of(src, k, sel[k], a.flags);
         float *h = a.h + (size_t)k * I;
         if (!blob) {
-            if (lane < R && i0 + lane < I) h[i0 + lane] = 0.f;
+            if (lane < R && i0 + lane < I) xstore(h + i0 + lane, 0.f);
             continue;
         }
-        wave_gate_up<BITS, GCPL, R>(blob, xs, D, I, i0, lane, h);
+        wave_gate_up<BITS, GCPL, R>(blob, dig, csum, xinv, D, I, i0, lane, h);
     }
-    grid_sync(a.bar, 2, NB, a.flags);
+    grid_sync(g, 2);
 
     // ---- phase C: down rows of every slot, combine, residual
     const int units = (D + RW - 1) / RW;
@@ -148,7 +172,7 @@ __global__ void __launch_bounds__(64 * MAXW) k_layer(LayerArgs a)
     for (int u = blockIdx.x; u < units; u += NB, ++j) {
         const int o0 = u * RW;
         float out[STEPS];
-        wave_down<BITS, LPR, DCPL, STEPS>(myblob, a.h + (size_t)wave * I, D, I, o0, lane, out);
+        wave_down<BITS, LPR, DCPL, STEPS, true>(myblob, a.h + (size_t)wave * I, D, I, o0, lane, out);
         if (lane % LPR == 0) {
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) part[wave][s * RPS + lane / LPR] = myblob ? wk * out[s] : 0.f;
@@ -169,13 +193,13 @@ __global__ void __launch_bounds__(64 * MAXW) k_layer(LayerArgs a)
         }
         __syncthreads();
     }
-    if (tid == 0) a.ss[blockIdx.x] = ssacc;
-    grid_sync(a.bar, 3, NB, a.flags);
+    if (tid == 0) xstore(a.ss + blockIdx.x, ssacc);
+    grid_sync(g, 3);
 
     // ---- phase D: RMSNorm of the block's own rows
     if (wave == 0) {
         float t = 0.f;
-        for (int b = lane; b < NB; b += 64) t += a.ss[b];
+        for (int b = lane; b < NB; b += 64) t += xload(a.ss + b);
         t = group_sum<64>(t);
         if (lane == 0) inv_s = 1.f / sqrtf(t / (float)D + a.eps);
     }
@@ -186,7 +210,8 @@ __global__ void __launch_bounds__(64 * MAXW) k_layer(LayerArgs a)
         const int o = u * RW + lane;
         if (wave == 0 && lane < RW && o < D) a.x[o] = rsave[j][lane] * inv * a.gamma[o];
     }
-    grid_exit(a.bar, NB);
+    if (tid == 0 && blockIdx.x == 0)
+        __hip_atomic_store(a.hdr, (uint32_t)NB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kGateUpRowsFused = 2;

@@ -62,6 +62,7 @@ extern "C" {
 
 #define MOE_DEVERR_EXPERT_RANGE 1u   /* an expert index outside [0, n_experts) */
 #define MOE_DEVERR_BARRIER_TIMEOUT 2u /* a grid-wide wait of a fused layer step timed out */
+#define MOE_DEVERR_WORKSPACE 4u       /* a fused layer step met a workspace last used with another grid */
 
 /*
  * Canonical expert blob (one contiguous byte range per expert; the unit the
@@ -108,8 +109,12 @@ typedef struct moe_layer_desc {
 
 /* Workspace bytes that moe_route / moe_expert_forward / moe_layer_step need
  * for this layer shape and token count (0 for an invalid descriptor).
- * The caller zero-fills a workspace once after allocating it; every call
- * leaves its internal counters at zero again when its kernels finish. */
+ * The caller zero-fills a workspace once after allocating it; the library
+ * keeps its counters consistent from call to call.  A workspace serves one
+ * layer shape (hidden, inter, bits, top_k + n_shared) on one device: the
+ * grid-barrier state of the fused layer step belongs to that shape's grid,
+ * and a fused step on a workspace last used with another grid sets
+ * MOE_DEVERR_WORKSPACE and does nothing. */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens);
 
 /* Human-readable text of a status code; static storage. */

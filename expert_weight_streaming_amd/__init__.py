@@ -42,7 +42,7 @@ class Streamer(ctypes.Structure):
 
 
 EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_last_error", "moe_route",
-           "moe_expert_forward", "moe_layer_step", "moe_layer_plan", "moe_stream_prefetch"]
+           "moe_expert_forward", "moe_layer_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch"]
 
 _lib = None
 
@@ -70,6 +70,8 @@ def lib():
         L.moe_layer_step.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, i32, vp, vp, vp, sz, vp]
         L.moe_layer_plan.restype = ctypes.c_int
         L.moe_layer_plan.argtypes = [ctypes.POINTER(LayerDesc), i32, vp]
+        L.moe_workspace_grouping.restype = ctypes.c_int
+        L.moe_workspace_grouping.argtypes = [ctypes.POINTER(LayerDesc), i32, vp]
         L.moe_stream_prefetch.restype = ctypes.c_int
         L.moe_stream_prefetch.argtypes = [ctypes.POINTER(Streamer), i32, vp, i32, i32, i32, vp, vp]
         _lib = L
@@ -143,6 +145,13 @@ def moe_layer_plan(desc, n_tokens: int = 1) -> dict:
     out = (ctypes.c_int32 * 7)()
     _check(lib().moe_layer_plan(ctypes.byref(desc), n_tokens, ctypes.cast(out, ctypes.c_void_p)))
     keys = ("fused", "grid", "block", "per_cu", "n_cu", "vgprs", "scratch")
+    return dict(zip(keys, (int(v) for v in out)))
+
+
+def moe_workspace_grouping(desc, n_tokens: int) -> dict:
+    out = (ctypes.c_size_t * 6)()
+    _check(lib().moe_workspace_grouping(ctypes.byref(desc), n_tokens, ctypes.cast(out, ctypes.c_void_p)))
+    keys = ("count", "offset", "perm", "pos", "act", "n_act")
     return dict(zip(keys, (int(v) for v in out)))
 
 

@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SO = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_abi.hip", "moe_kernels.hip", "moe_layer.hip"]
+SOURCES = ["moe_abi.hip", "moe_kernels.hip", "moe_layer.hip", "moe_batch.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

@@ -97,6 +97,29 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
     off = round_up(off + nss * 4, 256);
     L.slots = off;
     off = round_up(off + (size_t)moe::kMaxLayerBlocks * moe::kSlotWords * 4, 256);
+    if (T > 1) {
+        const size_t E = d->n_experts, K = d->top_k, D = d->hidden, I = d->inter;
+        const size_t P = (size_t)T * (K + d->n_shared);
+        const size_t cw = 128 / d->bits;  // activations per 16-byte chunk
+        auto take = [&](size_t &field, size_t bytes) {
+            field = off;
+            off = round_up(off + bytes, 256);
+        };
+        take(L.count, E * 4);
+        take(L.offset, (E + 1) * 4);
+        take(L.perm, T * K * 4);
+        take(L.pos_of_pair, T * K * 4);
+        take(L.act, E * 4);
+        take(L.n_act, 4);
+        take(L.xdig, (size_t)T * (D * 3 / 4) * 4);
+        take(L.xcsum, (size_t)T * (D / cw) * 4);
+        take(L.xinv, (size_t)T * 4);
+        take(L.hb, P * I * 4);
+        take(L.hdig, P * (I * 3 / 4) * 4);
+        take(L.hcsum, P * (I / cw) * 4);
+        take(L.hinv, P * 4);
+        take(L.y, P * D * 4);
+    }
     L.total = off;
     return L;
 }
@@ -209,6 +232,45 @@ int enqueue_layer(const moe_layer_desc *d, float *resid, float *x, int32_t *idx,
     return e == hipSuccess ? MOE_OK : hip_fail(e, "layer launch");
 }
 
+moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, int32_t *idx, float *w,
+                          float *logits, uint8_t *ws, const moe::WsLayout &L)
+{
+    moe::BatchArgs b;
+    b.src = blob_src(d);
+    b.router = d->router_w;
+    b.gamma = d->gamma;
+    b.x = x;
+    b.resid = nullptr;
+    b.xout = nullptr;
+    b.yout = nullptr;
+    b.topk_idx = idx;
+    b.topk_w = w;
+    b.logits = logits ? logits : reinterpret_cast<float *>(ws + L.logits);
+    b.count = reinterpret_cast<int32_t *>(ws + L.count);
+    b.offset = reinterpret_cast<int32_t *>(ws + L.offset);
+    b.perm = reinterpret_cast<int32_t *>(ws + L.perm);
+    b.pos_of_pair = reinterpret_cast<int32_t *>(ws + L.pos_of_pair);
+    b.act = reinterpret_cast<int32_t *>(ws + L.act);
+    b.n_act = reinterpret_cast<int32_t *>(ws + L.n_act);
+    b.xdig = reinterpret_cast<int *>(ws + L.xdig);
+    b.xcsum = reinterpret_cast<float *>(ws + L.xcsum);
+    b.xinv = reinterpret_cast<float *>(ws + L.xinv);
+    b.h = reinterpret_cast<float *>(ws + L.hb);
+    b.hdig = reinterpret_cast<int *>(ws + L.hdig);
+    b.hcsum = reinterpret_cast<float *>(ws + L.hcsum);
+    b.hinv = reinterpret_cast<float *>(ws + L.hinv);
+    b.y = reinterpret_cast<float *>(ws + L.y);
+    b.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    b.T = T;
+    b.D = d->hidden;
+    b.E = d->n_experts;
+    b.K = d->top_k;
+    b.I = d->inter;
+    b.eps = d->rms_eps;
+    b.mode = 0;
+    return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,8 +309,12 @@ int moe_route(const moe_layer_desc *desc, const float *x, int32_t n_tokens, int3
         return rc;
     if (logits && ((uintptr_t)logits & 3u)) return fail(MOE_EINVAL, "logits not 4-byte aligned");
     if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
-    if (n_tokens != 1) return fail(MOE_EUNSUPPORTED, "batched routing not built");
     const moe::WsLayout L = layout(desc, n_tokens);
+    if (n_tokens > 1) {
+        const moe::BatchArgs b = batch_args(desc, n_tokens, x, topk_idx, topk_w, logits, (uint8_t *)workspace, L);
+        hipError_t e = moe::launch_batch_route(b, 1, (hipStream_t)stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "batched route launch");
+    }
     return enqueue_route(desc, x, topk_idx, topk_w, logits, (uint8_t *)workspace, L, (hipStream_t)stream);
 }
 
@@ -261,8 +327,16 @@ int moe_expert_forward(const moe_layer_desc *desc, const float *x, int32_t n_tok
         (rc = check_ptr(y, "y")))
         return rc;
     if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
-    if (n_tokens != 1) return fail(MOE_EUNSUPPORTED, "batched expert forward not built");
     const moe::WsLayout L = layout(desc, n_tokens);
+    if (n_tokens > 1) {
+        moe::BatchArgs b = batch_args(desc, n_tokens, x, const_cast<int32_t *>(topk_idx), const_cast<float *>(topk_w),
+                                      nullptr, (uint8_t *)workspace, L);
+        b.yout = y;
+        b.mode = 0;
+        hipError_t e = moe::launch_batch_route(b, 0, (hipStream_t)stream);
+        if (e == hipSuccess) e = moe::launch_batch_experts(b, desc->bits, (hipStream_t)stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "batched expert launch");
+    }
     return enqueue_forward(desc, x, topk_idx, topk_w, y, nullptr, nullptr, (uint8_t *)workspace, L,
                            (hipStream_t)stream);
 }
@@ -279,8 +353,16 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
     if ((const uint8_t *)resid < (const uint8_t *)x + span && (const uint8_t *)x < (const uint8_t *)resid + span)
         return fail(MOE_EINVAL, "resid and x overlap");
     if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
-    if (n_tokens != 1) return fail(MOE_EUNSUPPORTED, "batched layer step not built");
     const moe::WsLayout L = layout(desc, n_tokens);
+    if (n_tokens > 1) {
+        moe::BatchArgs b = batch_args(desc, n_tokens, x, topk_idx, topk_w, nullptr, (uint8_t *)workspace, L);
+        b.resid = resid;
+        b.xout = x;
+        b.mode = 1;
+        hipError_t e = moe::launch_batch_route(b, 1, (hipStream_t)stream);
+        if (e == hipSuccess) e = moe::launch_batch_experts(b, desc->bits, (hipStream_t)stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "batched layer launch");
+    }
     return enqueue_layer(desc, resid, x, topk_idx, topk_w, (uint8_t *)workspace, L, (hipStream_t)stream);
 }
 
@@ -299,6 +381,22 @@ int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out)
     out[4] = p.n_cu;
     out[5] = p.vgprs;
     out[6] = p.scratch;
+    return MOE_OK;
+}
+
+int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t *out)
+{
+    int rc = check_desc(desc, n_tokens);
+    if (rc) return rc;
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    if (n_tokens < 2) return fail(MOE_EINVAL, "the grouping exists for n_tokens >= 2");
+    const moe::WsLayout L = layout(desc, n_tokens);
+    out[0] = L.count;
+    out[1] = L.offset;
+    out[2] = L.perm;
+    out[3] = L.pos_of_pair;
+    out[4] = L.act;
+    out[5] = L.n_act;
     return MOE_OK;
 }
 

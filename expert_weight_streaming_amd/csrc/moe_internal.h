@@ -24,6 +24,9 @@ struct WsLayout {
     size_t h = 0;            // float [T][slots][I]
     size_t ss = 0;           // float [kMaxLayerBlocks]
     size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the fused kernel
+    // batches (T > 1)
+    size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0;
+    size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
     size_t total = 0;
 };
 
@@ -93,6 +96,41 @@ struct LayerArgs {
     float eps;
 };
 
+// A batch of T > 1 tokens (moe_batch.hip).  "Positions" number the
+// (token, slot) pairs grouped by expert: routed pairs at offset[e] ..
+// offset[e]+count[e]-1 in ascending pair index, then one shared-expert
+// position per token at T*K + t.
+struct BatchArgs {
+    BlobSrc src;
+    const float *router;     // [E][D]
+    const float *gamma;      // [D]
+    const float *x;          // [T][D] input activations
+    float *resid;            // [T][D] in/out (mode 1)
+    float *xout;             // [T][D] normalised output (mode 1)
+    float *yout;             // [T][D] combine output (mode 0)
+    int32_t *topk_idx;       // [T][K]
+    float *topk_w;           // [T][K]
+    float *logits;           // [T][E]
+    int32_t *count;          // [E]
+    int32_t *offset;         // [E+1]
+    int32_t *perm;           // [T*K] position -> pair index t*K + k
+    int32_t *pos_of_pair;    // [T*K] pair index -> position (-1: invalid id)
+    int32_t *act;            // [E] active experts, ascending
+    int32_t *n_act;          // [1]
+    int *xdig;               // [T][D/chunk][DW] digit tables of x
+    float *xcsum;            // [T][D/chunk]
+    float *xinv;             // [T]
+    float *h;                // [positions][I]
+    int *hdig;               // [positions][I/chunk][DW]
+    float *hcsum;            // [positions][I/chunk]
+    float *hinv;             // [positions]
+    float *y;                // [positions][D]
+    uint32_t *flags;
+    int32_t T, D, E, K, I;
+    float eps;
+    int32_t mode;            // 0: yout = combine; 1: residual + RMSNorm
+};
+
 // Down-projection lane split: LPR lanes per row (a power of two <= 64),
 // cpl 16-byte chunks per lane.
 struct DownShape {
@@ -101,6 +139,8 @@ struct DownShape {
 DownShape down_shape(int I, int bits);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s);
+hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s);
 hipError_t launch_gate_up(const GateUpArgs &a, int bits, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, int bits, hipStream_t s);
 // Fused single-launch layer step.  Returns hipErrorNotSupported (nothing

@@ -175,6 +175,22 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
 int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out);
 
 /*
+ * Token -> expert grouping of a batched call (n_tokens >= 2).  After
+ * moe_route, moe_expert_forward or moe_layer_step on a batch, the workspace
+ * holds, as int32 arrays at the byte offsets written to out[6] (host):
+ *   out[0] count[E]        pairs routed to each expert
+ *   out[1] offset[E+1]     exclusive prefix sum of count
+ *   out[2] perm[T*K]       pair indices t*K + k grouped by expert (ascending
+ *                          expert, ascending pair index inside an expert)
+ *   out[3] pos[T*K]        inverse of perm (-1 for an out-of-range id)
+ *   out[4] act[E]          the experts with count > 0, ascending
+ *   out[5] n_act[1]        how many there are
+ * Every routed expert's rows are read once per batched step and applied to
+ * all of its tokens.  Queries the layout only; enqueues nothing.
+ */
+int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t *out);
+
+/*
  * Host-to-HBM expert streaming (toolarium.ru, "Flash-MoE: чистый C, Metal и
  * никакого Python": per layer, the selected experts' weights are read in
  * parallel and handed to the GPU; hakusoku.com, "パイプライン概要": the K=4

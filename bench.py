@@ -36,6 +36,28 @@ def algorithmic_bytes(cfg):
     return cfg.E * cfg.D * 4 + (cfg.K + cfg.n_shared) * cfg.blob_bytes
 
 
+def counted_traffic(cfg):
+    """HBM bytes per k_layer launch from the committed counter summary, or
+    None when that summary is for other kernel sources or another workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_layer_{cfg.name}_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            k, _, v = line.partition(":")
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("moe_layer.hip", "moe_device.h", "moe_internal.h"):
+        with open(os.path.join(ROOT, "expert_weight_streaming_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        log("counter summary is for other kernel sources: traffic unknown")
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def build(cfg):
     import torch
     import seedgen
@@ -110,6 +132,134 @@ def cpu_baseline(cfg, v0, seconds, check_rows):
                       f"{per_layer * 1e3:.1f} ms per layer, extrapolated to the full stack"}, outs
 
 
+def mem_available():
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return 0
+
+
+def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
+    """The host-streamed stack: every expert blob in pinned host memory,
+    K + shared blobs per layer and token copied into the double-buffered
+    slab on a side stream (moe_stream_token).  The host arena is filled from
+    the resident stack's HBM arena; the streamed output must equal, bit for
+    bit, that of the resident stack holding the same bytes.  This rewrites
+    the resident arena when the host arena is aliased: run it last."""
+    import torch
+    import seedgen
+    import expert_weight_streaming_amd as ews
+    from expert_weight_streaming_amd.stack import StreamedStack
+    bb, L, E = cfg.blob_bytes, cfg.layers, cfg.E
+    full = L * E
+    # the driver pins at most ~65 GiB in all on the machines measured so far,
+    # so the default arena is 56 GiB, aliased
+    want = (56 << 30) if arena_gb is None else int(arena_gb * 2**30)
+    room = mem_available() - 32 * 2**30
+    P = int(min(full, max(E, min(want, room) // bb)))
+    st = None
+    while st is None:
+        log(f"streamed: pinning a {P * bb / 2**30:.1f} GiB host arena ({P} of {full} blobs; host MemAvailable "
+            f"{mem_available() / 2**30:.1f} GiB)")
+        t0 = time.time()
+        try:
+            st = StreamedStack(hidden=cfg.D, n_experts=E, top_k=cfg.K, inter=cfg.I, bits=cfg.bits, layers=L,
+                               n_shared=cfg.n_shared, group=cfg.group, eps=cfg.eps, arena_blobs=P)
+        except ews.MoeError as err:
+            if P <= E:
+                raise
+            log(f"streamed: {err}; halving the arena")
+            P = max(E, P // 2)
+    log(f"streamed: pinned in {time.time() - t0:.1f} s")
+    t0 = time.time()
+    chunk = max(1, (2 << 30) // bb)
+    for p0 in range(0, P, chunk):
+        n = min(chunk, P - p0)
+        st.host_arena[p0 * bb:(p0 + n) * bb].copy_(resident.arena[p0 * bb:(p0 + n) * bb])
+    if cfg.n_shared:
+        st.host_shared.copy_(resident.shared[:st.host_shared.numel()])
+    st.router.copy_(resident.router)
+    st.gamma.copy_(resident.gamma)
+    torch.cuda.synchronize()
+    log(f"streamed: arena filled in {time.time() - t0:.1f} s")
+
+    # the link: one large copy, and the streamer's own pattern without compute
+    dev = torch.empty(min(P * bb, 4 << 30), dtype=torch.uint8, device="cuda")
+    cs = st.copy_stream
+    big = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(cs):
+            dev.copy_(st.host_arena[:dev.numel()], non_blocking=True)
+        cs.synchronize()
+        big.append(dev.numel() / (time.perf_counter() - t0) / 1e9)
+    del dev
+    ids = list(range(cfg.K))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for rep in range(2):
+        e0.record(cs)
+        for l in range(L):
+            ews.moe_stream_prefetch(st.streamer, l, [(i * 97 + l * 31) % E for i in ids], l & 1, cfg.n_shared > 0, cs)
+        e1.record(cs)
+        cs.synchronize()
+    pattern = L * st.slab_blobs * bb / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    link = max(big + [pattern])
+    log(f"streamed: H2D one large copy {max(big):.1f} GB/s, streamer pattern {pattern:.1f} GB/s")
+
+    # bitwise check of one token against the resident stack holding the same
+    # bytes: with an aliased arena, resident blob q becomes a copy of blob
+    # q mod P (the first P blobs are the ones the host arena was filled from)
+    D = cfg.D
+    for q0 in range(P, full, P):
+        n = min(P, full - q0)
+        resident.arena[q0 * bb:(q0 + n) * bb].copy_(resident.arena[:n * bb])
+    r = torch.from_numpy(v0.copy()).cuda().view(1, D)
+    want = r.clone()
+    resident.step(r, want)
+    torch.cuda.synchronize()
+    if P == full:
+        assert torch.equal(want, out0)
+    r = torch.from_numpy(v0.copy()).cuda().view(1, D)
+    x = r.clone()
+    st.step(r, x)
+    torch.cuda.synchronize()
+    identical = bool(torch.equal(x, want)) and bool(torch.equal(st.topk_idx, resident.topk_idx))
+    if not identical:
+        raise SystemExit("streamed output differs from the resident stack holding the same bytes")
+
+    xin = torch.from_numpy(seedgen.activations(cfg, 0, tokens + warmup)).cuda()
+    for t in range(warmup):
+        r.copy_(xin[t:t + 1])
+        x.copy_(xin[t:t + 1])
+        st.step(r, x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        r.copy_(xin[warmup + t:warmup + t + 1])
+        x.copy_(xin[warmup + t:warmup + t + 1])
+        st.step(r, x)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flags = int(st.workspace[:4].view(torch.int32).item())
+    tps = tokens / wall
+    per_token = L * st.slab_blobs * bb
+    gbs = per_token * tps / 1e9
+    log(f"streamed: {tokens} tokens in {wall:.3f} s = {tps:.2f} tok/s, {gbs:.1f} GB/s over the link, flags {flags}")
+    return {"workload": f"{L}-layer {cfg.bits}-bit stack, experts in pinned host RAM, K={cfg.K} + {cfg.n_shared} "
+                        f"shared blobs per layer copied host->HBM per token, fresh N(0,1) input per token",
+            "tokens": tokens, "tokens_per_s": round(tps, 3), "ms_per_token": round(wall / tokens * 1e3, 3),
+            "pcie_bytes_per_token": per_token, "pcie_gbs": round(gbs, 2),
+            "pcie_peak_measured_gbs": round(link, 2), "pcie_frac_measured": round(gbs / link, 4),
+            "h2d_large_copy_gbs": round(max(big), 2), "h2d_streamer_pattern_gbs": round(pattern, 2),
+            "arena_blobs": P, "arena_aliased": P != full, "bitwise_equal_resident": identical,
+            "device_flags": flags}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +270,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-stream", action="store_true", help="skip the host-streamed stack")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB), the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--stream-tokens", type=int, default=64)
+    ap.add_argument("--stream-arena-gb", type=float, default=None,
+                    help="host arena size (default: the whole stack when host RAM allows, else aliased)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md on sharding)",
@@ -131,6 +288,12 @@ def main():
     import seedgen
 
     cfg = seedgen.CONFIGS[args.config]
+    if args.copy_probe:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
     st = build(cfg)
     D = cfg.D
     v0 = seedgen.activation(cfg, 0)
@@ -189,28 +352,39 @@ def main():
     flags = int(st.workspace[:4].view(torch.int32).item())
     log(f"{args.steps} tokens: wall {wall * 1e3:.2f} ms, events {dev_ms:.2f} ms, flags {flags}")
 
-    k_ms, n_launch = kernel_timing(st, r, x, args.kernel_tokens)
+    # the fused layer kernel's average duration: HIP events around the timed
+    # region on the launch stream, over its layers * steps launches (the one
+    # 4-byte-per-element r <- x copy per token is included)
+    k_ms = dev_ms / (args.steps * cfg.layers)
+    n_launch = args.steps * cfg.layers
+    k_ms_eager, n_eager = kernel_timing(st, r, x, args.kernel_tokens)
     bytes_per_launch = algorithmic_bytes(cfg)
     achieved = bytes_per_launch / (k_ms * 1e-3) / 1e9
-    log(f"fused layer kernel: {k_ms * 1e3:.2f} us avg over {n_launch} launches, {achieved:.0f} GB/s")
+    log(f"fused layer kernel: {k_ms * 1e3:.2f} us avg over {n_launch} graph launches ({achieved:.0f} GB/s); "
+        f"{k_ms_eager * 1e3:.2f} us between events around each of {n_eager} eager launches")
+    traffic = counted_traffic(cfg)
 
     out = {
         "metric": "MoE expert-stack tokens/s (batch 1, 4-bit); dequant-GEMV HBM GB/s vs peak",
         "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"u{cfg.bits}+bf16 scale/bias, f32 accumulate", "data": "synthetic (seeded, random weights)",
+        "dtype": f"u{cfg.bits} codes x i8 activation digits (i32 dot), bf16 scale/bias, f32 combine", "data": "synthetic (seeded, random weights)",
         "config": {"workload": f"{cfg.layers}-layer MoE expert stack, hidden {cfg.D}, {cfg.E} experts, top-{cfg.K} "
                                f"+ {cfg.n_shared} shared, inter {cfg.I}, {cfg.bits}-bit group-{cfg.group} "
                                f"experts resident in HBM, batch {cfg.tokens}, output fed back",
                    "global_batch": cfg.tokens, "layers": cfg.layers, "graph": graph is not None,
                    "expert_bytes_resident": cfg.layers * (cfg.E + cfg.n_shared) * cfg.blob_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "k_layer (fused layer step)", "bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": round(k_ms * 1e3, 3), "launches_timed": n_launch},
+                     "avg_launch_us": round(k_ms * 1e3, 3), "launches_timed": n_launch,
+                     "avg_launch_us_eager_events": round(k_ms_eager * 1e3, 3)},
         "stack_gbs": round(bytes_per_launch * cfg.layers * value / 1e9, 1),
         "device_flags": flags,
     }
+    if not args.no_stream:
+        out["streamed"] = streamed_bench(cfg, st, out0, v0, args.stream_tokens, 2, args.stream_arena_gb)
     if not args.no_cpu:
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         import workloads as W

@@ -42,7 +42,8 @@ class Streamer(ctypes.Structure):
 
 
 EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_last_error", "moe_route",
-           "moe_expert_forward", "moe_layer_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch"]
+           "moe_expert_forward", "moe_layer_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
+           "moe_host_alloc", "moe_host_free"]
 
 _lib = None
 
@@ -74,6 +75,13 @@ def lib():
         L.moe_workspace_grouping.argtypes = [ctypes.POINTER(LayerDesc), i32, vp]
         L.moe_stream_prefetch.restype = ctypes.c_int
         L.moe_stream_prefetch.argtypes = [ctypes.POINTER(Streamer), i32, vp, i32, i32, i32, vp, vp]
+        L.moe_stream_token.restype = ctypes.c_int
+        L.moe_stream_token.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(Streamer), vp, vp, vp, vp, vp, vp,
+                                       sz, vp, vp, vp]
+        L.moe_host_alloc.restype = ctypes.c_int
+        L.moe_host_alloc.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_host_free.restype = ctypes.c_int
+        L.moe_host_free.argtypes = [vp]
         _lib = L
     return _lib
 
@@ -161,3 +169,37 @@ def moe_stream_prefetch(streamer: Streamer, layer: int, expert_ids, slot: int, w
     ev = None if done_event is None else (done_event if isinstance(done_event, int) else done_event.cuda_event)
     _check(lib().moe_stream_prefetch(ctypes.byref(streamer), layer, ctypes.cast(ids, ctypes.c_void_p),
                                      len(expert_ids), slot, 1 if with_shared else 0, _stream(copy_stream), ev))
+
+
+def moe_stream_token(descs, streamer: Streamer, resid, x, topk_idx, topk_w, host_ids, workspace, compute_stream,
+                     copy_stream, events, ws_bytes=None) -> None:
+    """descs: a ctypes array of LayerDesc (streamed form); host_ids: pinned
+    int32 tensor of K; events: five torch.cuda.Event."""
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
+    ev = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
+    _check(lib().moe_stream_token(descs, len(descs), ctypes.byref(streamer), _ptr(resid), _ptr(x), _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(host_ids), _ptr(workspace), ws_bytes, _stream(compute_stream),
+                                  _stream(copy_stream), ctypes.cast(ev, ctypes.c_void_p)))
+
+
+class HostArena:
+    """Pinned host memory from moe_host_alloc, exposed as a CPU uint8 tensor
+    (`.tensor`) for filling and checking; freed when the object goes."""
+
+    def __init__(self, nbytes: int):
+        import numpy as np
+        import torch
+        p = ctypes.c_void_p()
+        _check(lib().moe_host_alloc(nbytes, ctypes.byref(p)))
+        self.ptr, self.nbytes = int(p.value), int(nbytes)
+        arr = np.ctypeslib.as_array((ctypes.c_uint8 * self.nbytes).from_address(self.ptr))
+        self.tensor = torch.from_numpy(arr)
+
+    def data_ptr(self) -> int:
+        return self.ptr
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            self.tensor = None
+            lib().moe_host_free(self.ptr)
+            self.ptr = None

@@ -437,4 +437,85 @@ int moe_stream_prefetch(const moe_streamer *st, int32_t layer, const int32_t *ex
     return MOE_OK;
 }
 
+int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_streamer *st, float *resid, float *x,
+                     int32_t *topk_idx, float *topk_w, int32_t *host_ids, void *workspace, size_t ws_bytes,
+                     void *compute_stream, void *copy_stream, void *const *events)
+{
+    if (!layers || n_layers < 1) return fail(MOE_EINVAL, "no layers");
+    if (!st || !st->slab[0] || !st->slab[1]) return fail(MOE_ESTATE, "streamer has no slab");
+    if (n_layers > st->n_layers) return fail(MOE_ESTATE, "%d layers but the streamer holds %d", n_layers, st->n_layers);
+    if (!host_ids || !events || !topk_idx || !topk_w) return fail(MOE_EINVAL, "NULL host_ids, events or routing buffers");
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return fail(MOE_EINVAL, "event %d is NULL", i);
+    const int K = layers[0].top_k;
+    const int with_shared = layers[0].n_shared;
+    if (st->slab_blobs != K + with_shared) return fail(MOE_ESTATE, "slab holds %d blobs, the layers need %d", st->slab_blobs, K + with_shared);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (layers[l].experts) return fail(MOE_EINVAL, "layer %d is not a streamed layer (experts != NULL)", l);
+        if (layers[l].top_k != K || layers[l].n_shared != with_shared)
+            return fail(MOE_EINVAL, "layer %d has another top_k / n_shared", l);
+        moe_layer_desc d = layers[l];
+        d.slab = st->slab[0];
+        if (int rc = check_desc(&d, 1)) return rc;
+        if (d.blob_bytes != st->blob_bytes || d.n_experts != st->n_experts)
+            return fail(MOE_ESTATE, "layer %d does not match the streamer's blob size / expert count", l);
+    }
+    if (int rc = check_ws(&layers[0], 1, workspace, ws_bytes)) return rc;
+    hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
+    hipEvent_t route_done = (hipEvent_t)events[0];
+    hipEvent_t copy_done[2] = {(hipEvent_t)events[1], (hipEvent_t)events[2]};
+    hipEvent_t compute_done[2] = {(hipEvent_t)events[3], (hipEvent_t)events[4]};
+    hipError_t e;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const int s = l & 1;
+        moe_layer_desc d = layers[l];
+        d.slab = st->slab[s];
+        int32_t *idx = topk_idx + (size_t)l * K;
+        float *w = topk_w + (size_t)l * K;
+        // 1. routing, and its selections to the host (the one device->host wait per layer)
+        int rc = moe_route(&d, x, 1, idx, w, nullptr, workspace, ws_bytes, compute_stream);
+        if (rc) return rc;
+        if ((e = hipMemcpyAsync(host_ids, idx, (size_t)K * 4, hipMemcpyDeviceToHost, cs)) != hipSuccess)
+            return hip_fail(e, "selection copy");
+        if ((e = hipEventRecord(route_done, cs)) != hipSuccess) return hip_fail(e, "event record");
+        if ((e = hipEventSynchronize(route_done)) != hipSuccess) return hip_fail(e, "selection wait");
+        // 2. the selected experts into slot s, after the kernel that last read it (layer l-2)
+        if (l >= 2 && (e = hipStreamWaitEvent(ps, compute_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
+        rc = moe_stream_prefetch(st, l, host_ids, K, s, l == 0 ? with_shared : 0, copy_stream, copy_done[s]);
+        if (rc) return rc;
+        // 3. the layer itself once its weights have landed
+        if ((e = hipStreamWaitEvent(cs, copy_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
+        rc = moe_layer_step(&d, resid, x, 1, idx, w, workspace, ws_bytes, compute_stream);
+        if (rc) return rc;
+        if ((e = hipEventRecord(compute_done[s], cs)) != hipSuccess) return hip_fail(e, "event record");
+        // 4. the next layer's shared expert needs no routing: queue it behind this layer's copies
+        if (with_shared && l + 1 < n_layers) {
+            const int s1 = (l + 1) & 1;
+            if (l >= 1 && (e = hipStreamWaitEvent(ps, compute_done[s1], 0)) != hipSuccess) return hip_fail(e, "wait");
+            rc = moe_stream_prefetch(st, l + 1, nullptr, 0, s1, 1, copy_stream, nullptr);
+            if (rc) return rc;
+        }
+    }
+    return MOE_OK;
+}
+
+int moe_host_alloc(size_t bytes, void **out)
+{
+    if (!out) return fail(MOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (bytes == 0) return fail(MOE_EINVAL, "zero-byte host arena");
+    void *p = nullptr;
+    hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "pinned host allocation");
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_host_free(void *p)
+{
+    if (!p) return MOE_OK;
+    hipError_t e = hipHostFree(p);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "pinned host free");
+}
+
 }  // extern "C"

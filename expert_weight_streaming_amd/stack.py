@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (make_desc, moe_blob_bytes, moe_layer_step, moe_workspace_bytes)
+from . import (HostArena, make_desc, moe_blob_bytes, moe_layer_step, moe_workspace_bytes)
 
 
 class ResidentStack:
@@ -73,3 +73,74 @@ class ResidentStack:
         torch.cuda.current_stream().wait_stream(s)
         self.graph = g
         return g
+
+
+class StreamedStack:
+    """Expert stack whose expert weights live in pinned host memory.
+
+    Routers and gammas stay in HBM; per token and layer the K selected
+    experts and the shared expert are copied host->device into one of two
+    slab slots (moe_stream_token, hakusoku.com, "パイプライン概要": routing,
+    then the experts' reads, then the forward).  arena_blobs < layers *
+    n_experts aliases expert (l, e) onto host blob (l * E + e) mod
+    arena_blobs: the bytes moved per token are unchanged, only the host
+    footprint shrinks.
+    """
+
+    def __init__(self, *, hidden, n_experts, top_k, inter, bits, layers, n_shared=1, group=64, eps=1e-6,
+                 arena_blobs=None, device="cuda"):
+        from . import LayerDesc, Streamer
+        self.D, self.E, self.K, self.I = hidden, n_experts, top_k, inter
+        self.bits, self.group, self.layers, self.n_shared, self.eps = bits, group, layers, n_shared, eps
+        self.bb = moe_blob_bytes(hidden, inter, bits, group)
+        self.P = layers * n_experts if arena_blobs is None else int(arena_blobs)
+        if not 0 < self.P <= layers * n_experts:
+            raise ValueError(f"arena_blobs {self.P} outside 1..{layers * n_experts}")
+        dev = torch.device(device)
+        # moe_host_alloc, not torch's pinned allocator (which rounds every
+        # request up to a power of two)
+        self._arena = HostArena(self.P * self.bb)
+        self._shared = HostArena(max(1, layers * n_shared) * self.bb)
+        self.host_arena, self.host_shared = self._arena.tensor, self._shared.tensor
+        self.router = torch.empty(layers, n_experts, hidden, dtype=torch.float32, device=dev)
+        self.gamma = torch.ones(layers, hidden, dtype=torch.float32, device=dev)
+        self.slab_blobs = top_k + n_shared
+        self.slab = torch.empty(2, self.slab_blobs * self.bb, dtype=torch.uint8, device=dev)
+        st = Streamer()
+        st.host_arena, st.host_shared = self._arena.ptr, self._shared.ptr
+        st.blob_bytes, st.n_experts, st.n_layers = self.bb, n_experts, layers
+        st.arena_blobs, st.shared_blobs = self.P, max(1, layers * n_shared) if n_shared else 0
+        st.slab[0], st.slab[1] = self.slab[0].data_ptr(), self.slab[1].data_ptr()
+        st.slab_blobs = self.slab_blobs
+        self.streamer = st
+        descs = [make_desc(hidden=hidden, n_experts=n_experts, top_k=top_k, inter=inter, n_shared=n_shared, bits=bits,
+                           group=group, rms_eps=eps, router_w=self.router[l], gamma=self.gamma[l], experts=None,
+                           shared=None, slab=self.slab[0], blob_bytes=self.bb) for l in range(layers)]
+        self.descs = (LayerDesc * layers)(*descs)
+        self.ws_bytes = moe_workspace_bytes(descs[0], 1)
+        self.workspace = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.topk_idx = torch.zeros(layers, 1, top_k, dtype=torch.int32, device=dev)
+        self.topk_w = torch.zeros(layers, 1, top_k, dtype=torch.float32, device=dev)
+        self.host_ids = torch.zeros(top_k, dtype=torch.int32, pin_memory=True)
+        self.copy_stream = torch.cuda.Stream(device=dev)
+        # events are created on their first record
+        self.events = [torch.cuda.Event() for _ in range(5)]
+        for e in self.events:
+            e.record(self.copy_stream)
+        self.copy_stream.synchronize()
+
+    def host_blob(self, l: int, e: int) -> torch.Tensor:
+        """The host bytes that expert (l, e) streams from."""
+        p = (l * self.E + e) % self.P
+        return self.host_arena[p * self.bb:(p + 1) * self.bb]
+
+    def host_shared_blob(self, l: int) -> torch.Tensor:
+        return self.host_shared[l * self.bb:(l + 1) * self.bb]
+
+    def step(self, resid, x, stream=None):
+        """One token (resid, x: [1][D] device) through every layer; returns
+        when the last layer is enqueued on `stream`."""
+        from . import moe_stream_token
+        cs = torch.cuda.current_stream() if stream is None else stream
+        moe_stream_token(self.descs, self.streamer, resid, x, self.topk_idx, self.topk_w, self.host_ids,
+                         self.workspace, cs, self.copy_stream, self.events)

@@ -228,6 +228,45 @@ typedef struct moe_streamer {
 int moe_stream_prefetch(const moe_streamer *s, int32_t layer, const int32_t *expert_ids, int32_t n_ids,
                         int32_t slot, int32_t with_shared, void *copy_stream, void *done_event);
 
+/*
+ * Page-locked host memory for the streamer's arenas (hipHostMalloc): the
+ * device's copy engines read it directly, so moe_stream_prefetch's copies
+ * run asynchronously at link speed.  moe_host_alloc stores the address in
+ * *out (NULL on failure) and returns MOE_EINVAL for bytes == 0 or out ==
+ * NULL, MOE_EHIP when the runtime cannot pin that much.  The caller owns
+ * the memory and releases it with moe_host_free (NULL is a no-op) after
+ * every copy from it has completed.
+ */
+int moe_host_alloc(size_t bytes, void **out);
+int moe_host_free(void *p);
+
+/*
+ * One decode token through n_layers streamed layers (the per-layer pipeline
+ * of hakusoku.com, "パイプライン概要": routing, then the selected experts'
+ * reads, then the expert forward with combine, residual and norm; the
+ * expert work is queued without the host waiting for it, as the pages'
+ * deferred command buffer).  For layer l, slot s = l mod 2:
+ *   1. moe_route on compute_stream; the K selections are copied to
+ *      host_ids (pinned host, K int32) and the host waits for them;
+ *   2. moe_stream_prefetch of those experts into slab slot s on
+ *      copy_stream, after the layer that last read the slot (l-2);
+ *   3. compute_stream waits for the copies, then moe_layer_step reads the
+ *      slot (the step recomputes the same routing bit for bit);
+ *   4. the shared expert of layer l+1 (independent of routing) is queued on
+ *      copy_stream right behind layer l's copies, so the link stays busy
+ *      while the host waits for layer l+1's routing.
+ * layers: host array of n_layers descriptors in streamed form (experts ==
+ * NULL; their slab field is replaced by st->slab[l mod 2]); all share top_k
+ * and n_shared, and st->slab_blobs == top_k + n_shared.  resid, x: [D]
+ * device, in/out.  topk_idx, topk_w: device [n_layers][K] outputs.
+ * events: five hipEvent_t (route_done, copy_done[2], compute_done[2]).
+ * Returns after the last layer has been enqueued; the caller synchronises
+ * compute_stream for the result.
+ */
+int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_streamer *st, float *resid,
+                     float *x, int32_t *topk_idx, float *topk_w, int32_t *host_ids, void *workspace,
+                     size_t ws_bytes, void *compute_stream, void *copy_stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

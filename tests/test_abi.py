@@ -100,3 +100,45 @@ def test_streamer_misuse_rejected():
 def test_strerror():
     for s in (0, -1, -2, -3, -4):
         assert ews.moe_strerror(s)
+
+
+def test_stream_token_misuse_rejected():
+    """moe_stream_token validates everything before enqueueing anything."""
+    L = ews.lib()
+    D, E, K, I = 256, 16, 2, 128
+    bb = ews.moe_blob_bytes(D, I, 4, 64)
+    st = ews.Streamer()
+    st.host_arena, st.host_shared, st.blob_bytes = 4096, 8192, bb
+    st.n_experts, st.n_layers, st.arena_blobs, st.shared_blobs, st.slab_blobs = E, 2, 2 * E, 2, K + 1
+    st.slab[0], st.slab[1] = 1 << 20, 1 << 21
+    mk = lambda **kw: ews.make_desc(**{**dict(hidden=D, n_experts=E, top_k=K, inter=I, n_shared=1, bits=4,
+                                               router_w=1 << 12, gamma=1 << 13, slab=1 << 20), **kw})
+    descs = (ews.LayerDesc * 2)(mk(), mk())
+    ev = (ctypes.c_void_p * 5)(*([1 << 4] * 5))
+    evp = ctypes.cast(ev, ctypes.c_void_p)
+    ws = 1 << 16
+    args = lambda d, n, s, e: (d, n, s, 1 << 8, 1 << 9, 1 << 10, 1 << 11, 1 << 14, ws, 1 << 30, None, None, e)
+    assert L.moe_stream_token(*args(descs, 0, ctypes.byref(st), evp)) == ews.MOE_EINVAL       # no layers
+    assert L.moe_stream_token(*args(descs, 3, ctypes.byref(st), evp)) == ews.MOE_ESTATE       # > streamer layers
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), None)) == ews.MOE_EINVAL      # events
+    bad_ev = (ctypes.c_void_p * 5)(1, 1, None, 1, 1)
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), ctypes.cast(bad_ev, ctypes.c_void_p))) \
+        == ews.MOE_EINVAL
+    resident = (ews.LayerDesc * 2)(mk(), mk(experts=1 << 20))
+    assert L.moe_stream_token(*args(resident, 2, ctypes.byref(st), evp)) == ews.MOE_EINVAL    # not streamed
+    other_k = (ews.LayerDesc * 2)(mk(), mk(top_k=3))
+    assert L.moe_stream_token(*args(other_k, 2, ctypes.byref(st), evp)) == ews.MOE_EINVAL
+    st.slab_blobs = K
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp)) == ews.MOE_ESTATE       # slab size
+    st.slab_blobs = K + 1
+    small_ws = args(descs, 2, ctypes.byref(st), evp)
+    small_ws = small_ws[:9] + (256,) + small_ws[10:]
+    assert L.moe_stream_token(*small_ws) == ews.MOE_EINVAL                                    # workspace
+
+
+def test_host_alloc_rejects_bad_arguments():
+    L = ews.lib()
+    p = ctypes.c_void_p()
+    assert L.moe_host_alloc(0, ctypes.byref(p)) == ews.MOE_EINVAL
+    assert L.moe_host_alloc(16, None) == ews.MOE_EINVAL
+    assert L.moe_host_free(None) == ews.MOE_OK

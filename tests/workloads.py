@@ -90,3 +90,44 @@ def check_layer(ref: LayerRef, r_in, x_in, gpu_sel, gpu_w, gpu_r, gpu_x, stats=N
     if stats is not None:
         stats["layers"] = stats.get("layers", 0) + 1
     return res
+
+
+def build_streamed(cfg, layers=None, arena_blobs=None):
+    """A StreamedStack whose host arena holds the seeded blobs: host blob p
+    is expert (p // E, p % E); expert (l, e) streams host blob
+    (l * E + e) mod arena_blobs."""
+    import torch
+    from expert_weight_streaming_amd.stack import StreamedStack
+    L = layers or cfg.layers
+    st = StreamedStack(hidden=cfg.D, n_experts=cfg.E, top_k=cfg.K, inter=cfg.I, bits=cfg.bits, layers=L,
+                       n_shared=cfg.n_shared, group=cfg.group, eps=cfg.eps, arena_blobs=arena_blobs)
+    s = torch.cuda.current_stream().cuda_stream
+    tmp = torch.empty(cfg.E * st.bb, dtype=torch.uint8, device="cuda")
+    for p0 in range(0, st.P, cfg.E):
+        n = min(cfg.E, st.P - p0)
+        seedgen.dev_blobs(cfg, p0 // cfg.E, 0, n, tmp.data_ptr(), s)
+        st.host_arena[p0 * st.bb:(p0 + n) * st.bb].copy_(tmp[:n * st.bb])
+    for l in range(L):
+        if cfg.n_shared:
+            seedgen.dev_blobs(cfg, l, seedgen.SHARED_ID, 1, tmp.data_ptr(), s)
+            st.host_shared_blob(l).copy_(tmp[:st.bb])
+        st.router[l].copy_(torch.from_numpy(seedgen.router(cfg, l)))
+    torch.cuda.synchronize()
+    return st
+
+
+def resident_twin(st):
+    """A ResidentStack holding exactly the bytes a StreamedStack streams."""
+    import torch
+    from expert_weight_streaming_amd.stack import ResidentStack
+    rs = ResidentStack(hidden=st.D, n_experts=st.E, top_k=st.K, inter=st.I, bits=st.bits, layers=st.layers,
+                       n_shared=st.n_shared, group=st.group, eps=st.eps)
+    for l in range(st.layers):
+        for e in range(st.E):
+            rs.arena[(l * st.E + e) * st.bb:(l * st.E + e + 1) * st.bb].copy_(st.host_blob(l, e))
+        if st.n_shared:
+            rs.shared[l * st.bb:(l + 1) * st.bb].copy_(st.host_shared_blob(l))
+    rs.router.copy_(st.router)
+    rs.gamma.copy_(st.gamma)
+    torch.cuda.synchronize()
+    return rs

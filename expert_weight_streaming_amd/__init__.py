@@ -42,7 +42,7 @@ class Streamer(ctypes.Structure):
 
 
 EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_last_error", "moe_route",
-           "moe_expert_forward", "moe_layer_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
+           "moe_expert_forward", "moe_layer_step", "moe_stack_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
            "moe_host_alloc", "moe_host_free"]
 
 _lib = None
@@ -69,6 +69,8 @@ def lib():
         L.moe_expert_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_layer_step.restype = ctypes.c_int
         L.moe_layer_step.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_stack_step.restype = ctypes.c_int
+        L.moe_stack_step.argtypes = [ctypes.POINTER(LayerDesc), i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer_plan.restype = ctypes.c_int
         L.moe_layer_plan.argtypes = [ctypes.POINTER(LayerDesc), i32, vp]
         L.moe_workspace_grouping.restype = ctypes.c_int
@@ -146,6 +148,13 @@ def moe_expert_forward(desc, x, n_tokens, topk_idx, topk_w, y, workspace, stream
 def moe_layer_step(desc, resid, x, n_tokens, topk_idx, topk_w, workspace, stream=None, ws_bytes=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
     _check(lib().moe_layer_step(ctypes.byref(desc), _ptr(resid), _ptr(x), n_tokens, _ptr(topk_idx), _ptr(topk_w),
+                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_stack_step(descs, resid, x, topk_idx, topk_w, workspace, record=None, stream=None, ws_bytes=None) -> None:
+    """descs: a ctypes array of LayerDesc."""
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().moe_stack_step(descs, len(descs), _ptr(resid), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(record),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
 
 

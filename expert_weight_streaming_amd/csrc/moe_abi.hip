@@ -97,6 +97,8 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
     off = round_up(off + nss * 4, 256);
     L.slots = off;
     off = round_up(off + (size_t)moe::kMaxLayerBlocks * moe::kSlotWords * 4, 256);
+    L.rbuf = off;
+    off = round_up(off + (size_t)d->hidden * 4, 256);
     if (T > 1) {
         const size_t E = d->n_experts, K = d->top_k, D = d->hidden, I = d->inter;
         const size_t P = (size_t)T * (K + d->n_shared);
@@ -199,37 +201,84 @@ int enqueue_forward(const moe_layer_desc *d, const float *x, const int32_t *idx,
     return e == hipSuccess ? MOE_OK : hip_fail(e, "down launch");
 }
 
-int enqueue_layer(const moe_layer_desc *d, float *resid, float *x, int32_t *idx, float *w, uint8_t *ws,
-                  const moe::WsLayout &L, hipStream_t s)
+moe::StackLayer stack_layer(const moe_layer_desc *d)
 {
-    moe::LayerArgs a;
-    a.src = blob_src(d);
-    a.router = d->router_w;
-    a.gamma = d->gamma;
-    a.resid = resid;
-    a.x = x;
-    a.topk_idx = idx;
-    a.topk_w = w;
-    a.logits = reinterpret_cast<float *>(ws + L.logits);
-    a.h = reinterpret_cast<float *>(ws + L.h);
-    a.ss = reinterpret_cast<float *>(ws + L.ss);
-    a.hdr = reinterpret_cast<uint32_t *>(ws + L.hdr);
-    a.slots = reinterpret_cast<uint32_t *>(ws + L.slots);
-    a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
-    a.D = d->hidden;
-    a.E = d->n_experts;
-    a.K = d->top_k;
-    a.I = d->inter;
-    a.eps = d->rms_eps;
-    int grid = 0;
-    hipError_t e = moe::launch_layer(a, d->bits, s, &grid);
-    if (e == hipErrorNotSupported) {
-        // no scratch-free fused kernel for this shape: three launches
-        int rc = enqueue_route(d, x, idx, w, nullptr, ws, L, s);
-        if (rc) return rc;
-        return enqueue_forward(d, x, idx, w, nullptr, resid, x, ws, L, s);
+    moe::StackLayer y;
+    y.router = d->router_w;
+    y.gamma = d->gamma;
+    y.experts = d->experts;
+    y.shared = d->experts ? d->shared : nullptr;
+    y.slab = d->experts ? nullptr : d->slab;
+    return y;
+}
+
+hipError_t stack_plan_or_launch(const moe::StackArgs *a, const moe_layer_desc *d, hipStream_t s, moe::LayerPlan *p)
+{
+    const int S = d->top_k + d->n_shared;
+    return d->bits == 4 ? moe::stack_bits4(a, d->hidden, d->n_experts, d->inter, S, s, p)
+                        : moe::stack_bits2(a, d->hidden, d->n_experts, d->inter, S, s, p);
+}
+
+// n layers of one token (batch 1).  Persistent launches of up to
+// kMaxStackLayers layers each; shapes without a resident-grid plan take
+// three launches per layer (route, gate/up, down with residual and norm).
+// record (optional): [n+1][2][D] (r, x) entering every layer and the output.
+int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, int32_t *idx, float *w, float *record,
+                  uint8_t *ws, const moe::WsLayout &L, hipStream_t s)
+{
+    const moe_layer_desc *d = &ds[0];
+    const int D = d->hidden, K = d->top_k;
+    for (int32_t l0 = 0; l0 < n; l0 += moe::kMaxStackLayers) {
+        const int cnt = n - l0 < moe::kMaxStackLayers ? n - l0 : moe::kMaxStackLayers;
+        moe::StackArgs a;
+        for (int j = 0; j < cnt; ++j) a.layer[j] = stack_layer(&ds[l0 + j]);
+        a.resid = resid;
+        a.x = x;
+        a.topk_idx = idx + (size_t)l0 * K;
+        a.topk_w = w + (size_t)l0 * K;
+        a.record = record ? record + (size_t)l0 * 2 * D : nullptr;
+        a.logits = reinterpret_cast<float *>(ws + L.logits);
+        a.h = reinterpret_cast<float *>(ws + L.h);
+        a.rbuf = reinterpret_cast<float *>(ws + L.rbuf);
+        a.ss = reinterpret_cast<float *>(ws + L.ss);
+        a.hdr = reinterpret_cast<uint32_t *>(ws + L.hdr);
+        a.slots = reinterpret_cast<uint32_t *>(ws + L.slots);
+        a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+        a.blob_bytes = d->blob_bytes;
+        a.n_layers = cnt;
+        a.D = D;
+        a.E = d->n_experts;
+        a.K = K;
+        a.I = d->inter;
+        a.n_slots = K + d->n_shared;
+        a.eps = d->rms_eps;
+        moe::LayerPlan p;
+        hipError_t e = stack_plan_or_launch(&a, d, s, &p);
+        if (e == hipSuccess) continue;
+        if (e != hipErrorNotSupported) return hip_fail(e, "stack launch");
+        // no resident-grid plan for this shape: three launches per layer
+        for (int j = 0; j < cnt; ++j) {
+            const moe_layer_desc *dj = &ds[l0 + j];
+            int32_t *ij = idx + (size_t)(l0 + j) * K;
+            float *wj = w + (size_t)(l0 + j) * K;
+            if (record) {
+                float *rj = record + (size_t)(l0 + j) * 2 * D;
+                if ((e = hipMemcpyAsync(rj, resid, (size_t)D * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+                    (e = hipMemcpyAsync(rj + D, x, (size_t)D * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+                    return hip_fail(e, "record copy");
+            }
+            int rc = enqueue_route(dj, x, ij, wj, nullptr, ws, L, s);
+            if (rc) return rc;
+            if ((rc = enqueue_forward(dj, x, ij, wj, nullptr, resid, x, ws, L, s))) return rc;
+        }
+        if (record) {
+            float *rn = record + (size_t)(l0 + cnt) * 2 * D;
+            if ((e = hipMemcpyAsync(rn, resid, (size_t)D * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+                (e = hipMemcpyAsync(rn + D, x, (size_t)D * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+                return hip_fail(e, "record copy");
+        }
     }
-    return e == hipSuccess ? MOE_OK : hip_fail(e, "layer launch");
+    return MOE_OK;
 }
 
 moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, int32_t *idx, float *w,
@@ -363,7 +412,34 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
         if (e == hipSuccess) e = moe::launch_batch_experts(b, desc->bits, (hipStream_t)stream);
         return e == hipSuccess ? MOE_OK : hip_fail(e, "batched layer launch");
     }
-    return enqueue_layer(desc, resid, x, topk_idx, topk_w, (uint8_t *)workspace, L, (hipStream_t)stream);
+    return enqueue_stack(desc, 1, resid, x, topk_idx, topk_w, nullptr, (uint8_t *)workspace, L, (hipStream_t)stream);
+}
+
+int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
+                   float *topk_w, float *record, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!layers || n_layers < 1) return fail(MOE_EINVAL, "no layers");
+    int rc = check_desc(&layers[0], 1);
+    if (rc) return rc;
+    const moe_layer_desc *d = &layers[0];
+    for (int32_t l = 1; l < n_layers; ++l) {
+        const moe_layer_desc *e = &layers[l];
+        if ((rc = check_desc(e, 1))) return rc;
+        if (e->hidden != d->hidden || e->n_experts != d->n_experts || e->top_k != d->top_k || e->inter != d->inter ||
+            e->n_shared != d->n_shared || e->bits != d->bits || e->rms_eps != d->rms_eps)
+            return fail(MOE_EINVAL, "layer %d differs in shape or rms_eps from layer 0", l);
+    }
+    if ((rc = check_ptr(resid, "resid")) || (rc = check_ptr(x, "x")) || (rc = check_ptr4(topk_idx, "topk_idx")) ||
+        (rc = check_ptr4(topk_w, "topk_w")))
+        return rc;
+    if (record && !aligned16(record)) return fail(MOE_EINVAL, "record not 16-byte aligned");
+    const size_t span = (size_t)d->hidden * 4;
+    if ((const uint8_t *)resid < (const uint8_t *)x + span && (const uint8_t *)x < (const uint8_t *)resid + span)
+        return fail(MOE_EINVAL, "resid and x overlap");
+    if ((rc = check_ws(d, 1, workspace, ws_bytes))) return rc;
+    const moe::WsLayout L = layout(d, 1);
+    return enqueue_stack(layers, n_layers, resid, x, topk_idx, topk_w, record, (uint8_t *)workspace, L,
+                         (hipStream_t)stream);
 }
 
 int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out)
@@ -372,7 +448,7 @@ int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out)
     if (rc) return rc;
     if (!out) return fail(MOE_EINVAL, "out is NULL");
     moe::LayerPlan p;
-    hipError_t e = moe::plan_layer(desc->hidden, desc->inter, desc->bits, desc->top_k + desc->n_shared, &p);
+    hipError_t e = stack_plan_or_launch(nullptr, desc, nullptr, &p);
     if (e != hipSuccess) return hip_fail(e, "layer plan");
     out[0] = p.grid > 0 && n_tokens == 1 ? 1 : 0;
     out[1] = p.grid;

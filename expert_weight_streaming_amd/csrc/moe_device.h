@@ -28,19 +28,44 @@ namespace dev {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Sum / max over groups of W consecutive lanes (W a power of two <= 64).
+// Sum / max over groups of W consecutive lanes (W a power of two <= 64),
+// the result in every lane of the group.  Inside a row of 16 lanes the
+// steps are DPP moves (two quad permutations, the half-row and the row
+// mirror: each pairs a lane with one of the other half of its group), 32
+// lanes swap halves through ds_swizzle, and the full wave reads lanes 0 and
+// 32 as scalars.  Every lane of a group adds the same operands, so the
+// result is bit-identical across the group.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ float fdpp(float v, float identity)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two <= 64");
+    if constexpr (W >= 2) v += fdpp<0xB1>(v, 0.f);   // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += fdpp<0x4E>(v, 0.f);   // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += fdpp<0x141>(v, 0.f);  // row_half_mirror
+    if constexpr (W >= 16) v += fdpp<0x140>(v, 0.f); // row_mirror
+    if constexpr (W >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16
+    if constexpr (W == 64)
+        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
     return v;
 }
 template <int W>
 __device__ __forceinline__ float group_max(float v)
 {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two <= 64");
+    if constexpr (W >= 2) v = fmaxf(v, fdpp<0xB1>(v, -INFINITY));
+    if constexpr (W >= 4) v = fmaxf(v, fdpp<0x4E>(v, -INFINITY));
+    if constexpr (W >= 8) v = fmaxf(v, fdpp<0x141>(v, -INFINITY));
+    if constexpr (W >= 16) v = fmaxf(v, fdpp<0x140>(v, -INFINITY));
+    if constexpr (W >= 32) v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+    if constexpr (W == 64)
+        v = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
     return v;
 }
 
@@ -68,19 +93,27 @@ __device__ __forceinline__ void fixed_scale(float amax, float &mul, float &inv)
     inv = ldexpf(1.f, -k);
 }
 
-// The three signed base-256 digits of round(v * mul), each in [-128, 127].
-__device__ __forceinline__ void digits3(float v, float mul, int &d0, int &d1, int &d2)
+// The three signed base-256 digits of xi = round(v * mul) (|xi| < 2^22):
+// xi = d0 + 256 d1 + 65536 d2 with d0, d1 in [-128, 127] (sign-extended low
+// bytes) and |d2| <= 64.  Four values at once, as three packed digit words
+// (byte j of word p: digit p of value j).  d0 is the low byte of xi;
+// y = xi - d0 holds d1 in its byte 1; z = y - 256 d1 holds d2 in its byte 2;
+// the bytes are gathered with byte permutes.
+__device__ __forceinline__ void digit_words(float a, float b, float c, float d, float mul, int &w0, int &w1, int &w2)
 {
-    const int xi = __float2int_rn(v * mul);
-    d0 = ((xi + 128) & 255) - 128;
-    const int x1 = (xi - d0) >> 8;
-    d1 = ((x1 + 128) & 255) - 128;
-    d2 = (x1 - d1) >> 8;
-}
-
-__device__ __forceinline__ int pack4(int a, int b, int c, int d)
-{
-    return (a & 255) | ((b & 255) << 8) | ((c & 255) << 16) | (int)((uint32_t)d << 24);
+    const int xa = __float2int_rn(a * mul), xb = __float2int_rn(b * mul);
+    const int xc = __float2int_rn(c * mul), xd = __float2int_rn(d * mul);
+    const int ya = xa - __builtin_amdgcn_sbfe(xa, 0, 8), yb = xb - __builtin_amdgcn_sbfe(xb, 0, 8);
+    const int yc = xc - __builtin_amdgcn_sbfe(xc, 0, 8), yd = xd - __builtin_amdgcn_sbfe(xd, 0, 8);
+    const int za = ya - (__builtin_amdgcn_sbfe(ya, 8, 8) << 8), zb = yb - (__builtin_amdgcn_sbfe(yb, 8, 8) << 8);
+    const int zc = yc - (__builtin_amdgcn_sbfe(yc, 8, 8) << 8), zd = yd - (__builtin_amdgcn_sbfe(yd, 8, 8) << 8);
+    // v_perm_b32(hi, lo, sel): selector bytes 0-3 pick lo's bytes, 4-7 hi's
+    w0 = (int)__builtin_amdgcn_perm(__builtin_amdgcn_perm(xd, xc, 0x0c0c0400u), __builtin_amdgcn_perm(xb, xa, 0x0c0c0400u),
+                                    0x05040100u);
+    w1 = (int)__builtin_amdgcn_perm(__builtin_amdgcn_perm(yd, yc, 0x0c0c0501u), __builtin_amdgcn_perm(yb, ya, 0x0c0c0501u),
+                                    0x05040100u);
+    w2 = (int)__builtin_amdgcn_perm(__builtin_amdgcn_perm(zd, zc, 0x0c0c0602u), __builtin_amdgcn_perm(zb, za, 0x0c0c0602u),
+                                    0x05040100u);
 }
 
 // Digit words of word k, sub s of one chunk from the chunk's activations
@@ -94,11 +127,9 @@ __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
     for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int s = 0; s < C::SUBS; ++s) {
-            int d[4][3];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) digits3(v[k * C::PER_WORD + s + C::SUBS * j], mul, d[j][0], d[j][1], d[j][2]);
-#pragma unroll
-            for (int p = 0; p < 3; ++p) dg[(k * C::SUBS + s) * 3 + p] = pack4(d[0][p], d[1][p], d[2][p], d[3][p]);
+            const float *u = v + k * C::PER_WORD + s;
+            int *o = dg + (k * C::SUBS + s) * 3;
+            digit_words(u[0], u[C::SUBS], u[2 * C::SUBS], u[3 * C::SUBS], mul, o[0], o[1], o[2]);
         }
 }
 
@@ -121,6 +152,34 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
             a2 = __builtin_amdgcn_sdot4(m, d[2], a2, false);
         }
     return fmaf((float)a2, 65536.f, fmaf((float)a1, 256.f, (float)a0));
+}
+
+// csum[c] = sum of the fp32 values of chunk c of x, for c < nc: four lanes
+// per chunk, each summing a quarter in order, then the four quarters.
+// Called by whole waves of the block (blockDim a multiple of 64).
+template <int BITS>
+__device__ __forceinline__ void chunk_sums(const float *x, int nc, float *csum)
+{
+    using C = Codes<BITS>;
+    constexpr int Q = C::CODES / 4;
+    const int nt = blockDim.x;
+    for (int t0 = 0; t0 < 4 * nc; t0 += nt) {
+        const int t = t0 + (int)threadIdx.x, c = t >> 2;
+        float sum = 0.f;
+        if (c < nc) {
+            const float4 *v = reinterpret_cast<const float4 *>(x + c * C::CODES + (t & 3) * Q);
+#pragma unroll
+            for (int j = 0; j < Q / 4; ++j) {
+                const float4 f = v[j];
+                sum += f.x;
+                sum += f.y;
+                sum += f.z;
+                sum += f.w;
+            }
+        }
+        sum = group_sum<4>(sum);
+        if (c < nc && (t & 3) == 0) csum[c] = sum;
+    }
 }
 
 // Block-cooperative fixed-point digit table of an activation vector x[0..n)
@@ -147,18 +206,10 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
         const int c = t / (4 * C::SUBS), r = t - c * 4 * C::SUBS;
         const int k = r / C::SUBS, s = r - k * C::SUBS;
         const float *v = x + c * C::CODES + k * C::PER_WORD + s;
-        int d[4][3];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) digits3(v[C::SUBS * j], mul, d[j][0], d[j][1], d[j][2]);
         int *o = dig + c * C::DW + (k * C::SUBS + s) * 3;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) o[p] = pack4(d[0][p], d[1][p], d[2][p], d[3][p]);
+        digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[1], o[2]);
     }
-    for (int c = tid; c < n / C::CODES; c += nt) {
-        float sum = 0.f;
-        for (int j = 0; j < C::CODES; ++j) sum += x[c * C::CODES + j];
-        csum[c] = sum;
-    }
+    chunk_sums<BITS>(x, n / C::CODES, csum);
     __syncthreads();
     return inv;
 }
@@ -227,40 +278,83 @@ __device__ __forceinline__ float wave_router_row(const float *row, const float *
     return group_sum<64>(acc0 + acc1);
 }
 
-// One wave: R consecutive intermediate rows i0.. of one expert's gate and up
-// matrices; lane l owns 16-byte chunks l, l+64, ... of every row.  The
-// activation arrives as a digit table (block_digit_table, in LDS) with its
-// per-chunk sums and fixed-point step inv.  All weight loads are issued
-// first.  Writes h[i] = silu(g_i) * u_i, silu(z) = z / (1 + exp(-z)).
+// Weight loads go through buffer instructions: the blob base sits in a
+// scalar resource, the row offset in a scalar register and the lane's
+// offset in one vector register (its constant part in the instruction), so
+// a wave's many loads in flight cost data registers only.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t blob_rsrc(const void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Gate/up rows, split into the loads and the arithmetic so that a caller can
+// issue a unit's loads long before its activation is ready.  One wave owns R
+// consecutive intermediate rows i0.. of one expert's gate and up matrices;
+// lane l holds 16-byte chunks l, l+64, ... of every row and the scale/bias
+// word of each chunk's group.  A NULL blob or a row/chunk outside the
+// matrix loads zeros.
 template <int BITS, int CPL, int R>
-__device__ __forceinline__ void wave_gate_up(const uint8_t *blob, const int *dig, const float *csum, float inv, int D,
-                                             int I, int i0, int lane, float *h)
+struct GuRegs {
+    uint4 q[CPL][R][2];
+    uint32_t sb[CPL][R][2];
+};
+
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void gu_load(GuRegs<BITS, CPL, R> &g, const uint8_t *blob, int D, int I, int i0, int lane)
 {
     using C = Codes<BITS>;
     const int nchunks = D * BITS / 128;
-    const uint64_t mat_q = (uint64_t)I * D * BITS / 8;
-    const uint64_t row_q = (uint64_t)D * BITS / 8;
-    const uint64_t sb0 = 3 * mat_q;
-    const uint64_t mat_sb = (uint64_t)I * (D / kGroup) * 4;
-    const int gpr = D / kGroup;
-
-    uint4 q[CPL][R][2];
-    uint32_t sb[CPL][R][2];
+    const uint32_t mat_q = (uint32_t)I * D * BITS / 8;
+    const uint32_t row_q = (uint32_t)D * BITS / 8;
+    const uint32_t sb0 = 3 * mat_q;
+    const uint32_t mat_sb = (uint32_t)I * (D / kGroup) * 4;
+    const uint32_t row_sb = (uint32_t)(D / kGroup) * 4;
 #pragma unroll
     for (int m = 0; m < CPL; ++m)
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int mat = 0; mat < 2; ++mat) {
-                const int i = i0 + r, c = lane + 64 * m;
-                const bool ok = i < I && c < nchunks;
-                q[m][r][mat] = ok ? *reinterpret_cast<const uint4 *>(blob + mat * mat_q + (uint64_t)i * row_q + (uint64_t)c * 16)
-                                  : make_uint4(0, 0, 0, 0);
-                sb[m][r][mat] = ok ? *reinterpret_cast<const uint32_t *>(
-                                         blob + sb0 + mat * mat_sb + ((uint64_t)i * gpr + (uint64_t)c * C::CODES / kGroup) * 4)
-                                   : 0u;
+                g.q[m][r][mat] = make_uint4(0, 0, 0, 0);
+                g.sb[m][r][mat] = 0u;
             }
+    if (!blob) return;
+    const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob);
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lane + 64 * m;
+        if (c >= nchunks) continue;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = i0 + r;
+            if (i >= I) continue;
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                g.q[m][r][mat] = bload16(rs, (uint32_t)c * 16, mat * mat_q + (uint32_t)i * row_q);
+                g.sb[m][r][mat] = bload4(rs, (uint32_t)(c * C::CODES / kGroup) * 4, sb0 + mat * mat_sb + (uint32_t)i * row_sb);
+            }
+        }
+    }
+}
 
+// The arithmetic: the activation arrives as a digit table (block_digit_table,
+// in LDS) with its per-chunk sums and fixed-point step inv.  Writes
+// h[i] = silu(g_i) * u_i, silu(z) = z / (1 + exp(-z)), agent-coherently.
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void gu_finish(const GuRegs<BITS, CPL, R> &g, const int *dig, const float *csum, float inv,
+                                          int D, int I, int i0, int lane, float *h)
+{
+    using C = Codes<BITS>;
+    const int nchunks = D * BITS / 128;
     float acc[R][2];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
@@ -288,18 +382,141 @@ __device__ __forceinline__ void wave_gate_up(const uint8_t *blob, const int *dig
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int mat = 0; mat < 2; ++mat) {
-                const float qx = qdot<BITS>(q[m][r][mat], dg);
-                acc[r][mat] = fmaf(bf16_lo(sb[m][r][mat]) * inv, qx, acc[r][mat]);
-                acc[r][mat] = fmaf(bf16_hi(sb[m][r][mat]), cs, acc[r][mat]);
+                const float qx = qdot<BITS>(g.q[m][r][mat], dg);
+                acc[r][mat] = fmaf(bf16_lo(g.sb[m][r][mat]) * inv, qx, acc[r][mat]);
+                acc[r][mat] = fmaf(bf16_hi(g.sb[m][r][mat]), cs, acc[r][mat]);
             }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const float g = group_sum<64>(acc[r][0]);
+        const float gg = group_sum<64>(acc[r][0]);
         const float u = group_sum<64>(acc[r][1]);
         const int i = i0 + r;
-        if (lane == 0 && i < I) xstore(h + i, g / (1.f + expf(-g)) * u);
+        if (lane == 0 && i < I) xstore(h + i, gg / (1.f + expf(-gg)) * u);
     }
+}
+
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void wave_gate_up(const uint8_t *blob, const int *dig, const float *csum, float inv, int D,
+                                             int I, int i0, int lane, float *h)
+{
+    GuRegs<BITS, CPL, R> g;
+    gu_load<BITS, CPL, R>(g, blob, D, I, i0, lane);
+    gu_finish<BITS, CPL, R>(g, dig, csum, inv, D, I, i0, lane, h);
+}
+
+// Down rows, split the same way: one wave owns 64/LPR consecutive output
+// rows o0.. of one expert's down matrix, LPR lanes per row, lane chunk
+// lc + LPR*m of its row (lc = lane % LPR).
+template <int BITS, int CPL>
+struct DnRegs {
+    uint4 q[CPL];
+    uint32_t sb[CPL];
+};
+
+template <int BITS, int LPR, int CPL>
+__device__ __forceinline__ void dn_load(DnRegs<BITS, CPL> &d, const uint8_t *blob, int D, int I, int o0, int lane)
+{
+    using C = Codes<BITS>;
+    const int nchunks = I * BITS / 128;
+    const int o = o0 + lane / LPR, lc = lane % LPR;
+    const uint32_t mat_q = (uint32_t)I * D * BITS / 8;
+    const uint32_t row_q = (uint32_t)I * BITS / 8;
+    const uint32_t sbd = 3 * mat_q + 2 * ((uint32_t)D * (I / kGroup) * 4);
+    const uint32_t row_sb = (uint32_t)(I / kGroup) * 4;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        d.q[m] = make_uint4(0, 0, 0, 0);
+        d.sb[m] = 0u;
+    }
+    if (!blob) return;
+    const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob);
+    // the wave's rows are o0 .. o0 + 64/LPR - 1: one scalar base, the lane's
+    // row and chunk in the vector offset
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lc + LPR * m;
+        if (o < D && c < nchunks) {
+            d.q[m] = bload16(rs, (uint32_t)(lane / LPR) * row_q + (uint32_t)c * 16, 2 * mat_q + (uint32_t)o0 * row_q);
+            d.sb[m] = bload4(rs, (uint32_t)(lane / LPR) * row_sb + (uint32_t)(c * C::CODES / kGroup) * 4,
+                             sbd + (uint32_t)o0 * row_sb);
+        }
+    }
+}
+
+// A lane's share of the row sums of a dn_load unit against a digit table
+// of h (LDS: hdig/hcsum of this expert's slot, fixed-point step hinv); the
+// row's sum is the sum over its LPR lanes.
+template <int BITS, int LPR, int CPL>
+__device__ __forceinline__ float dn_part(const DnRegs<BITS, CPL> &d, const int *hdig, const float *hcsum, float hinv,
+                                         int I, int lane)
+{
+    using C = Codes<BITS>;
+    const int nchunks = I * BITS / 128;
+    const int lc = lane % LPR;
+    float t = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lc + LPR * m;
+        if (c < nchunks) {
+            int dg[C::DW];
+            const int4 *src = reinterpret_cast<const int4 *>(hdig + c * C::DW);
+#pragma unroll
+            for (int t4 = 0; t4 < C::DW / 4; ++t4) {
+                const int4 v = src[t4];
+                dg[4 * t4] = v.x;
+                dg[4 * t4 + 1] = v.y;
+                dg[4 * t4 + 2] = v.z;
+                dg[4 * t4 + 3] = v.w;
+            }
+            const float qh = qdot<BITS>(d.q[m], dg);
+            t = fmaf(bf16_lo(d.sb[m]) * hinv, qh, t);
+            t = fmaf(bf16_hi(d.sb[m]), hcsum[c], t);
+        }
+    }
+    return t;
+}
+
+// Router row slice: float4 columns [c_lo, c_hi) of a row, lane l holding
+// columns c_lo + l + 64 m.
+template <int N>
+struct RtRegs {
+    float4 w[N];
+};
+
+template <int N>
+__device__ __forceinline__ void rt_load(RtRegs<N> &r, const float *row, int c_lo, int c_hi, int lane)
+{
+#pragma unroll
+    for (int m = 0; m < N; ++m) r.w[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!row) return;
+    const __amdgpu_buffer_rsrc_t rs = blob_rsrc(row);
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int c = c_lo + lane + 64 * m;
+        if (c < c_hi) {
+            const uint4 v = bload16(rs, (uint32_t)(lane + 64 * m) * 16, (uint32_t)c_lo * 16);
+            r.w[m] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+        }
+    }
+}
+
+// Per-lane partial dot of a loaded slice with x (LDS).
+template <int N>
+__device__ __forceinline__ float rt_finish(const RtRegs<N> &r, const float *x, int c_lo, int c_hi, int lane)
+{
+    const float4 *X = reinterpret_cast<const float4 *>(x);
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int c = c_lo + lane + 64 * m;
+        const float4 xv = c < c_hi ? X[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        acc0 = fmaf(r.w[m].x, xv.x, acc0);
+        acc1 = fmaf(r.w[m].y, xv.y, acc1);
+        acc0 = fmaf(r.w[m].z, xv.z, acc0);
+        acc1 = fmaf(r.w[m].w, xv.w, acc1);
+    }
+    return acc0 + acc1;
 }
 
 // One wave: STEPS x (64/LPR) consecutive rows o0.. of one expert's down
@@ -369,6 +586,61 @@ __device__ __forceinline__ void wave_down(const uint8_t *blob, const float *h, i
     for (int s = 0; s < STEPS; ++s) out[s] = group_sum<LPR>(t[s]);
 }
 
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Grid barrier of one launch.  Every block owns a 64-byte slot holding an
+// epoch count; at barrier i a block publishes base + i in its slot and
+// waits until every slot of the grid has reached it.  The epochs carry over
+// from launch to launch (each launch adds 3), so no counter is ever reset
+// and no atomic read-modify-write is contended.  Before publishing, the
+// block waits for its own stores to complete; all data crossing a barrier
+// is stored and loaded agent-coherently (xstore / xload / xload4).
+struct GridBar {
+    uint32_t *slots;
+    uint32_t base;
+    uint32_t nb;
+    uint32_t *flags;
+};
+
+// Arrival at barrier i: the block's stores complete, then one store of the
+// epoch.  Loads issued after the arrival (a prefetch) do not delay it.
+__device__ __forceinline__ void grid_arrive(const GridBar &g, uint32_t i)
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(g.slots + blockIdx.x * kSlotWords, g.base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every block has arrived at barrier i (epochs newer than the
+// target count too: a fast block may already have passed it).
+__device__ __forceinline__ void grid_wait(const GridBar &g, uint32_t i)
+{
+    const uint32_t target = g.base + i;
+    if (threadIdx.x < 64) {
+        uint32_t spins = 0;
+        for (;;) {
+            bool ok = true;
+            for (uint32_t j = threadIdx.x; j < g.nb; j += 64)
+                ok &= (int32_t)(__hip_atomic_load(g.slots + j * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                target) >= 0;
+            if (__all(ok)) break;
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins == kSpinLimit) {
+                atomicOr(g.flags, MOE_DEVERR_BARRIER_TIMEOUT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void grid_sync(const GridBar &g, uint32_t i)
+{
+    grid_arrive(g, i);
+    grid_wait(g, i);
+}
+
 // One wave: the K largest of lg[0..E) (LDS), descending, the lower index
 // first on an exact tie; idx/vals identical in every lane.  Loops run over
 // the compile-time bound so the arrays stay in registers.
@@ -416,6 +688,318 @@ __device__ __forceinline__ void topk_weights(const float (&vals)[kMaxTopK], int 
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) w[k] = k < K ? expf(vals[k] - vals[0]) / z : 0.f;
 }
+
+// Routing candidates as 64-bit keys: the logit's bits mapped to an
+// unsigned order (high word), the complement of the expert index (low
+// word).  A larger key is a larger logit, then the lower index; 0 is below
+// every real key.
+__device__ __forceinline__ uint64_t route_key(float v, int e)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(uint64_t k)
+{
+    const uint32_t ord = (uint32_t)(k >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key of a full wave, returned in every lane: DPP inside rows of
+// 16, then the row broadcasts (row 15 -> rows 1 and 3, row 31 -> rows 2 and
+// 3) leave the maximum in lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
+{
+    uint64_t o;
+    o = dpp_u64<0xB1, 0xF>(k);   // quad_perm [1,0,3,2]
+    k = o > k ? o : k;
+    o = dpp_u64<0x4E, 0xF>(k);   // quad_perm [2,3,0,1]
+    k = o > k ? o : k;
+    o = dpp_u64<0x141, 0xF>(k);  // row_half_mirror
+    k = o > k ? o : k;
+    o = dpp_u64<0x140, 0xF>(k);  // row_mirror
+    k = o > k ? o : k;
+    o = dpp_u64<0x142, 0xA>(k);  // row_bcast:15 into rows 1, 3
+    k = o > k ? o : k;
+    o = dpp_u64<0x143, 0xC>(k);  // row_bcast:31 into rows 2, 3
+    k = o > k ? o : k;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Stage one of the block top-K: every wave takes the K largest keys of its
+// elements (e = 64 w + lane + 64 NW j, j < 8) and parks them in ck[w*K + k]
+// (LDS).  E <= 512 NW.  Whole waves only.
+template <int NW>
+__device__ __forceinline__ void topk_local(const float *lg, int E, int K, uint64_t *ck)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t key[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int e = 64 * wave + lane + 64 * NW * j;
+        key[j] = e < E ? route_key(lg[e], e) : 0ull;
+    }
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) best = key[j] > best ? key[j] : best;
+        const uint64_t w = wave_max_key(best);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (key[j] == w) key[j] = 0ull;
+        if (lane == 0) ck[wave * K + k] = w;
+    }
+}
+
+// Stage two, one wave: the K largest of the NW*K parked keys, in order;
+// sel/selw (LDS) receive the indices and the routing weights.
+template <int NW>
+__device__ __forceinline__ void topk_merge(const uint64_t *ck, int K, int *sel, float *selw)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t key = lane < NW * K ? ck[lane] : 0ull;
+    int idx[kMaxTopK];
+    float vals[kMaxTopK], w[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        idx[k] = -1;
+        vals[k] = -INFINITY;
+        if (k >= K) continue;
+        const uint64_t m = wave_max_key(key);
+        idx[k] = key_index(m);
+        vals[k] = key_value(m);
+        if (key == m) key = 0ull;
+    }
+    topk_weights(vals, K, w);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            if (k >= K) continue;
+            sel[k] = idx[k];
+            selw[k] = w[k];
+        }
+    }
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Top K of lg[0..E) (LDS) for a block of NW waves, K <= NW (E <= 512 NW).
+// The K-th largest of the NW wave maxima is a lower bound T of the K-th
+// largest element, so every selected element has a key >= T.  Those
+// candidates (usually a handful) are compacted into LDS and ranked against
+// each other in one pass.  Degenerate inputs with more than 64 candidates
+// (many equal logits) take K rounds of wave maxima instead.  sel/selw (LDS)
+// receive the indices in rank order and the routing weights (softmax over
+// the selected logits, summed in rank order).  LDS scratch: cand[64],
+// wmax[NW], sk[kMaxTopK] (64-bit) and one int.  All threads of the block
+// call it; it ends with __syncthreads.
+template <int NW>
+__device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, uint64_t *cand, uint64_t *wmax,
+                                                uint64_t *sk, int *ncand, int *sel, float *selw)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t key[8];
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) key[j] = 0ull;
+    if (E <= 64 * NW) {
+        const int e = 64 * wave + lane;
+        key[0] = e < E ? route_key(lg[e], e) : 0ull;
+        best = key[0];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = 64 * wave + lane + 64 * NW * j;
+            key[j] = e < E ? route_key(lg[e], e) : 0ull;
+            best = key[j] > best ? key[j] : best;
+        }
+    }
+    const uint64_t wm = wave_max_key(best);
+    if (lane == 0) wmax[wave] = wm;
+    if (tid == 0) *ncand = 0;
+    __syncthreads();
+    // T = the K-th largest wave maximum: lane i < NW ranks maximum i
+    const uint64_t mi = lane < NW ? wmax[lane] : 0ull;
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) r += readlane_u64(mi, q) > mi;
+    const uint64_t hit = __ballot(lane < NW && r == K - 1);
+    const uint64_t T = hit ? readlane_u64(mi, __builtin_ctzll(hit)) : 0ull;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (key[j] != 0ull && key[j] >= T) {
+            const int p = atomicAdd(ncand, 1);
+            if (p < 64) cand[p] = key[j];
+        }
+    __syncthreads();
+    const int n = *ncand;
+    if (n > 64) {
+        // every wave's K largest, then the K largest of those
+        for (int k = 0; k < K; ++k) {
+            uint64_t b = key[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) b = key[j] > b ? key[j] : b;
+            const uint64_t w = wave_max_key(b);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (key[j] == w) key[j] = 0ull;
+            if (lane == 0) sk[wave * K + k] = w;
+        }
+        __syncthreads();
+    }
+    if (wave == 0) {
+        // one candidate per lane, ranked against the others
+        const int nc = n <= 64 ? n : NW * K;
+        const uint64_t mine = lane < nc ? (n <= 64 ? cand[lane] : sk[lane]) : 0ull;
+        int rank = 0;
+        for (int q = 0; q < nc; ++q) rank += readlane_u64(mine, q) > mine;
+        const bool chosen = lane < nc && rank < K;
+        // softmax over the selected logits, summed in rank order
+        const uint64_t top = readlane_u64(mine, __builtin_ctzll(__ballot(lane < nc && rank == 0)));
+        const float v0 = key_value(top);
+        const float ex = chosen ? expf(key_value(mine) - v0) : 0.f;
+        float z = 0.f;
+        for (int k = 0; k < K; ++k)
+            z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), __builtin_ctzll(__ballot(chosen && rank == k))));
+        if (chosen) {
+            sel[rank] = key_index(mine);
+            selw[rank] = ex / z;
+        }
+    }
+    __syncthreads();
+}
+
+// (v, i) pairs ordered by value, then by the lower index: true when (ov, oi)
+// comes first.
+__device__ __forceinline__ bool key_before(float ov, int oi, float v, int i)
+{
+    return ov > v || (ov == v && oi < i);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// First (v, i) of a full wave by key_before, returned in every lane.  Within
+// each row of 16 lanes: two quad permutations, the half-row mirror and the
+// row mirror (DPP, no LDS round trip); the four row winners are then read
+// as scalars.  Must be called by all 64 lanes.
+__device__ __forceinline__ void wave_argmax(float &v, int &i)
+{
+#define MOE_ARGMAX_STEP(CTRL)                                                                                           \
+    {                                                                                                                   \
+        const float ov = __int_as_float(dpp_i<CTRL>(__float_as_int(v)));                                                \
+        const int oi = dpp_i<CTRL>(i);                                                                                  \
+        if (key_before(ov, oi, v, i)) {                                                                                 \
+            v = ov;                                                                                                     \
+            i = oi;                                                                                                     \
+        }                                                                                                               \
+    }
+    MOE_ARGMAX_STEP(0xB1)   // quad_perm [1,0,3,2]
+    MOE_ARGMAX_STEP(0x4E)   // quad_perm [2,3,0,1]
+    MOE_ARGMAX_STEP(0x141)  // row_half_mirror
+    MOE_ARGMAX_STEP(0x140)  // row_mirror
+#undef MOE_ARGMAX_STEP
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (key_before(rv, ri, bv, bi)) {
+            bv = rv;
+            bi = ri;
+        }
+    }
+    v = bv;
+    i = bi;
+}
+
+// Top K of lg[0..E) (LDS) for a whole block of NW waves: every wave takes
+// the K first of its elements (e = 64 w + lane + 64 NW j) by K wave argmax
+// rounds, parks them in cv/ci (LDS, NW*K entries), and wave 0 merges them in
+// K more rounds.  Order: larger value first, the lower index on an exact
+// tie.  sel/selw (LDS) receive the indices and the routing weights.  Ends
+// with __syncthreads.  E <= 64*NW*8.
+template <int NW>
+__device__ __forceinline__ void block_topk(const float *lg, int E, int K, float *cv, int *ci, int *sel, float *selw)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t taken = 0;
+    for (int k = 0; k < K; ++k) {
+        float v = -INFINITY;
+        int i = 0x7FFFFFFF;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = 64 * wave + lane + 64 * NW * j;
+            if (e < E && !((taken >> j) & 1u) && key_before(lg[e], e, v, i)) {
+                v = lg[e];
+                i = e;
+            }
+        }
+        wave_argmax(v, i);
+        if (i != 0x7FFFFFFF && (i & 63) == lane && ((i >> 6) % NW) == wave) taken |= 1u << ((i >> 6) / NW);
+        if (lane == 0) {
+            cv[wave * K + k] = v;
+            ci[wave * K + k] = i;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float v = -INFINITY;
+        int i = 0x7FFFFFFF;
+        if (lane < NW * K) {
+            v = cv[lane];
+            i = ci[lane];
+        }
+        int idx[kMaxTopK];
+        float vals[kMaxTopK], w[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            idx[k] = -1;
+            vals[k] = -INFINITY;
+            if (k >= K) continue;
+            float bv = v;
+            int bi = i;
+            wave_argmax(bv, bi);
+            idx[k] = bi;
+            vals[k] = bv;
+            if (i == bi) {
+                v = -INFINITY;
+                i = 0x7FFFFFFF;
+            }
+        }
+        topk_weights(vals, K, w);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                if (k >= K) continue;
+                sel[k] = idx[k];
+                selw[k] = w[k];
+            }
+        }
+    }
+    __syncthreads();
+}
+
 
 }  // namespace dev
 }  // namespace moe

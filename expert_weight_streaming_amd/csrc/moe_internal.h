@@ -11,19 +11,20 @@ namespace moe {
 constexpr int kGroup = 64;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxSlots = kMaxTopK + 1;  // routed + shared
-constexpr int kMaxLayerBlocks = 1024;    // grid cap of the fused layer kernel
+constexpr int kMaxLayerBlocks = 1024;    // grid cap of the persistent stack kernel
 constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
 
 // Workspace layout (byte offsets), all 64-byte aligned.
 struct WsLayout {
     size_t flags = 0;        // uint32 device error bits (OR-ed)
     size_t ctr_route = 64;   // uint32 arrival counter of the route kernel
-    size_t hdr = 128;        // uint32 grid size of the fused layer kernel last run on this workspace
+    size_t hdr = 128;        // uint32 grid size of the persistent stack kernel last run on this workspace
     size_t ctr_down = 192;   // uint32 arrival counter of the down kernel (layer mode)
     size_t logits = 0;       // float [T][E]
     size_t h = 0;            // float [T][slots][I]
     size_t ss = 0;           // float [kMaxLayerBlocks]
-    size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the fused kernel
+    size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the stack kernel
+    size_t rbuf = 0;         // float [D] residual stream handed between layers of one stack launch
     // batches (T > 1)
     size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0;
     size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
@@ -78,23 +79,6 @@ struct DownArgs {
     int32_t mode;            // 0: y = combine; 1: resid += combine, x = RMSNorm(resid)
 };
 
-struct LayerArgs {
-    BlobSrc src;
-    const float *router;     // [E][D]
-    const float *gamma;      // [D]
-    float *resid;            // [D] in/out
-    float *x;                // [D] in/out
-    int32_t *topk_idx;       // [K] out
-    float *topk_w;           // [K] out
-    float *logits;           // [E] workspace
-    float *h;                // [slots][I] workspace
-    float *ss;               // [grid] workspace
-    uint32_t *hdr;           // workspace: grid of the last fused launch (0: none yet)
-    uint32_t *slots;         // workspace: per-block barrier epochs
-    uint32_t *flags;
-    int32_t D, E, K, I;
-    float eps;
-};
 
 // A batch of T > 1 tokens (moe_batch.hip).  "Positions" number the
 // (token, slot) pairs grouped by expert: routed pairs at offset[e] ..
@@ -143,17 +127,80 @@ hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s);
 hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s);
 hipError_t launch_gate_up(const GateUpArgs &a, int bits, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, int bits, hipStream_t s);
-// Fused single-launch layer step.  Returns hipErrorNotSupported (nothing
-// launched) when the instantiation for this shape needs scratch memory: its
-// blocks could then not all be resident at once for the grid barriers.
-hipError_t launch_layer(const LayerArgs &a, int bits, hipStream_t s, int *grid);
 
-// Launch plan of the fused layer kernel for a shape (nothing launched):
-// grid 0 when the shape takes the three-launch path.
+// Launch plan of the persistent stack kernel for a shape (nothing
+// launched): grid 0 when the shape takes the three-launch path.
 struct LayerPlan {
     int grid = 0, block = 0, per_cu = 0, n_cu = 0, vgprs = 0, scratch = 0;
 };
-hipError_t plan_layer(int D, int I, int bits, int n_slots, LayerPlan *p);
+
+// One launch for a whole stack of layers (batch 1), moe_stack.hip.
+constexpr int kMaxStackLayers = 64;
+constexpr int kStackThreads = 512;
+
+struct StackLayer {
+    const float *router;     // [E][D]
+    const float *gamma;      // [D]
+    const uint8_t *experts;  // resident arena of E blobs, or NULL (streamed)
+    const uint8_t *shared;   // resident shared blob, or NULL
+    const uint8_t *slab;     // streamed: slot k = selection k, slot K = shared
+};
+
+struct StackArgs {
+    StackLayer layer[kMaxStackLayers];
+    float *resid;            // [D] in/out
+    float *x;                // [D] in/out
+    int32_t *topk_idx;       // [n_layers][K] out
+    float *topk_w;           // [n_layers][K] out
+    float *record;           // [n_layers+1][2][D] (r, x) entering each layer and the output, or NULL
+    float *logits;           // workspace [E]
+    float *h;                // workspace [slots][I]
+    float *rbuf;             // workspace [D]
+    float *ss;               // workspace [grid]
+    uint32_t *hdr;           // workspace: grid of the last persistent launch (0: none yet)
+    uint32_t *slots;         // workspace: per-block barrier epochs
+    uint32_t *flags;
+    uint64_t blob_bytes;
+    int32_t n_layers, D, E, K, I, n_slots;
+    float eps;
+};
+
+// Dynamic LDS of the stack kernel (byte offsets, 16-byte aligned).
+struct StackLds {
+    uint32_t xs, dig, csum, u, hdig, hcsum, misc, total;
+};
+constexpr int kStackMiscWords = 256;
+__host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bits)
+{
+    const uint32_t codes = 128 / bits, dw = 4 * (8 / bits) * 3;
+    StackLds l;
+    uint32_t o = 0;
+    l.xs = o;
+    o = (o + (uint32_t)D * 4 + 15u) & ~15u;
+    l.dig = o;
+    o = (o + (uint32_t)D / codes * dw * 4 + 15u) & ~15u;
+    l.csum = o;
+    o = (o + (uint32_t)D / codes * 4 + 15u) & ~15u;
+    l.u = o;
+    const uint32_t un = (uint32_t)E > (uint32_t)(S * I) ? (uint32_t)E : (uint32_t)(S * I);
+    o = (o + un * 4 + 15u) & ~15u;
+    l.hdig = o;
+    o = (o + (uint32_t)S * ((uint32_t)I / codes) * dw * 4 + 15u) & ~15u;
+    l.hcsum = o;
+    o = (o + (uint32_t)S * ((uint32_t)I / codes) * 4 + 15u) & ~15u;
+    l.misc = o;
+    o += kStackMiscWords * 4;
+    l.total = o;
+    return l;
+}
+
+// Persistent stack launch.  hipErrorNotSupported (nothing launched) when the
+// shape has no resident-grid plan (scratch or LDS limits).
+// a == NULL: only fill the plan (grid 0: no plan, the caller takes the
+// three-launch path).
+hipError_t stack_bits4(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p);
+hipError_t stack_bits2(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p);
+
 int down_blocks(int D, int I, int bits);
 int gate_up_blocks_per_slot(int I, int n_slots);
 

@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (HostArena, make_desc, moe_blob_bytes, moe_layer_step, moe_workspace_bytes)
+from . import (HostArena, LayerDesc, make_desc, moe_blob_bytes, moe_layer_step, moe_stack_step, moe_workspace_bytes)
 
 
 class ResidentStack:
@@ -28,6 +28,7 @@ class ResidentStack:
         self.router = torch.empty(layers, n_experts, hidden, dtype=torch.float32, device=dev)
         self.gamma = torch.ones(layers, hidden, dtype=torch.float32, device=dev)
         self.descs = [self._desc(l) for l in range(layers)]
+        self.desc_array = (LayerDesc * layers)(*self.descs)
         self.ws_bytes = moe_workspace_bytes(self.descs[0], n_tokens)
         self.workspace = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
         self.topk_idx = torch.zeros(layers, n_tokens, top_k, dtype=torch.int32, device=dev)
@@ -52,7 +53,23 @@ class ResidentStack:
 
     def step(self, resid, x, record=None, stream=None):
         """All layers for one batch; record (optional) [layers+1][2][T][D]
-        receives every layer's (resid, x) input and the final output."""
+        receives every layer's (resid, x) input and the final output.  One
+        token runs as moe_stack_step (one persistent launch); a batch runs
+        layer by layer."""
+        if self.T == 1:
+            moe_stack_step(self.desc_array, resid, x, self.topk_idx, self.topk_w, self.workspace, record, stream)
+            return
+        for l in range(self.layers):
+            if record is not None:
+                record[l, 0].copy_(resid)
+                record[l, 1].copy_(x)
+            self.layer_step(l, resid, x, stream)
+        if record is not None:
+            record[self.layers, 0].copy_(resid)
+            record[self.layers, 1].copy_(x)
+
+    def step_layers(self, resid, x, record=None, stream=None):
+        """The same as step, one moe_layer_step call per layer."""
         for l in range(self.layers):
             if record is not None:
                 record[l, 0].copy_(resid)

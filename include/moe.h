@@ -165,12 +165,36 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
                    int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * How moe_layer_step will run this layer on the current device (queries the
- * device, enqueues nothing).  out[7] (host) receives: fused (1 when the step
- * is one persistent launch with grid-wide barriers, 0 when it is three
- * launches: route, gate/up, down + norm), grid blocks, block threads, blocks
- * per CU the device reports for the fused kernel, CU count, VGPRs per lane,
- * scratch bytes per lane.
+ * A stack of n_layers layers for one token (batch 1): moe_layer_step applied
+ * to layers[0], layers[1], ... in turn, each layer's (resid, x) output
+ * feeding the next (the pages' engine hands the fused combine + norm result
+ * straight to the next layer, hakusoku.com, "主要技術"; attention between
+ * layers is absent here).  Results equal those of the n separate
+ * moe_layer_step calls bit for bit; the stack runs as one persistent launch
+ * per 64 layers, which removes the per-layer launch and lets each layer's
+ * routing-independent weights (next router rows, shared expert) be fetched
+ * while the previous layer finishes.
+ * layers: host array of n_layers descriptors with the same hidden,
+ * n_experts, top_k, inter, n_shared, bits and rms_eps (MOE_EINVAL
+ * otherwise); each may be resident or streamed (its slab must then already
+ * hold the layer's selected experts in selection order, as moe_layer_step
+ * requires).  resid, x: [D] device, in/out, must not overlap.
+ * topk_idx/topk_w: [n_layers][K] device outputs.  record: NULL or device
+ * [n_layers + 1][2][D], 16-byte aligned, receiving (resid, x) entering every
+ * layer and the final output.  workspace: as moe_workspace_bytes(&layers[0],
+ * 1).
+ */
+int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
+                   float *topk_w, float *record, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * How moe_layer_step / moe_stack_step will run this shape on the current
+ * device (queries the device, enqueues nothing).  out[7] (host) receives:
+ * fused (1 when a token's layers run as one persistent launch with
+ * grid-wide barriers, 0 when each layer is three launches: route, gate/up,
+ * down + norm), grid blocks, block threads, blocks per CU the device reports
+ * for the persistent kernel, CU count, VGPRs per lane, scratch bytes per
+ * lane.
  */
 int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out);
 

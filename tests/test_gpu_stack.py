@@ -82,3 +82,41 @@ def test_graph_replay_matches_eager():
         st.step(r2, x2)
         torch.cuda.synchronize()
         assert torch.equal(r2, want[0])
+
+
+@pytest.mark.parametrize("name,bits,layers", [("tiny", 4, 6), ("tiny", 2, 5), ("layer32", 4, 4), ("tiny", 4, 70)])
+def test_stack_launch_equals_layer_by_layer(name, bits, layers):
+    """moe_stack_step (persistent launches of up to 64 layers) gives the same
+    bits as one moe_layer_step per layer, records included."""
+    base = seedgen.CONFIGS["layer"].replace(E=32) if name == "layer32" else seedgen.CONFIGS[name]
+    cfg = base.replace(bits=bits, layers=layers, seed=0x5EED00E0 + layers + bits)
+    print(f"[gpu case] stack launch vs layer steps {name} bits={bits} layers={layers}", flush=True)
+    st = W.build_stack(cfg, layers=layers)
+    v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
+    rec_a = torch.zeros(layers + 1, 2, 1, cfg.D, dtype=torch.float32, device="cuda")
+    rec_b = torch.zeros_like(rec_a)
+    for t in range(2):
+        r1, x1 = v.clone(), v.clone()
+        st.step(r1, x1, record=rec_a)
+        torch.cuda.synchronize()
+        idx1, w1 = st.topk_idx.clone(), st.topk_w.clone()
+        r2, x2 = v.clone(), v.clone()
+        st.step_layers(r2, x2, record=rec_b)
+        torch.cuda.synchronize()
+        assert int(st.workspace[:4].view(torch.int32).item()) == 0, "device error flags"
+        assert torch.equal(idx1, st.topk_idx) and torch.equal(w1, st.topk_w)
+        assert torch.equal(r1, r2) and torch.equal(x1, x2)
+        assert torch.equal(rec_a, rec_b)
+        v = x1.clone()
+
+
+def test_layer_plan_is_fused_at_the_pages_shape():
+    import expert_weight_streaming_amd as ews
+    for bits in (4, 2):
+        cfg = seedgen.CONFIGS["layer"].replace(bits=bits)
+        st = W.build_stack(cfg.replace(E=8), layers=1)
+        d = ews.make_desc(hidden=cfg.D, n_experts=cfg.E, top_k=cfg.K, inter=cfg.I, n_shared=1, bits=bits,
+                          router_w=st.router[0], gamma=st.gamma[0], experts=st.arena, shared=st.shared)
+        plan = ews.moe_layer_plan(d, 1)
+        print(bits, plan)
+        assert plan["fused"] == 1 and plan["scratch"] == 0 and plan["grid"] == plan["n_cu"]

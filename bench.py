@@ -270,7 +270,8 @@ def main():
     ap.add_argument("--steps", type=int, default=128, help="timed decode tokens")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="stack4")
-    ap.add_argument("--kernel-tokens", type=int, default=4, help="tokens of the per-launch event timing pass")
+    ap.add_argument("--kernel-tokens", type=int, default=4,
+                    help="tokens of the one-layer-per-launch event timing pass (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--no-graph", action="store_true")
@@ -361,7 +362,7 @@ def main():
     # layers; the 16 KB r <- x copy node of each replay is included)
     k_ms = dev_ms / args.steps
     n_launch = args.steps
-    k_ms_layer, n_eager = kernel_timing(st, r, x, args.kernel_tokens)
+    k_ms_layer, n_eager = kernel_timing(st, r, x, args.kernel_tokens) if args.kernel_tokens > 0 else (float("nan"), 0)
     bytes_per_launch = algorithmic_bytes(cfg) * cfg.layers
     achieved = bytes_per_launch / (k_ms * 1e-3) / 1e9
     log(f"stack kernel: {k_ms * 1e3:.2f} us per token launch ({k_ms * 1e3 / cfg.layers:.2f} us per layer, "
@@ -384,7 +385,7 @@ def main():
                      "kernel": f"k_stack (persistent, {cfg.layers} layers per launch)",
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(k_ms * 1e3, 3),
                      "launches_timed": n_launch, "us_per_layer": round(k_ms * 1e3 / cfg.layers, 3),
-                     "one_layer_launch_us_eager_events": round(k_ms_layer * 1e3, 3)},
+                     "one_layer_launch_us_eager_events": round(k_ms_layer * 1e3, 3) if n_eager else None},
         "stack_gbs": round(bytes_per_launch * cfg.layers * value / 1e9, 1),
         "device_flags": flags,
     }

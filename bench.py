@@ -264,6 +264,65 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
             "device_flags": flags}
 
 
+def resident_extra(cfg, steps, warmup):
+    """Another resident workload of the same family, timed like the headline
+    (graph replays, output fed back): the 2-bit stack at batch 1, or at a
+    batch of cfg.tokens tokens through the grouped path.  Reported next to
+    the headline, not instead of it."""
+    import numpy as np
+    import torch
+    import seedgen
+    from expert_weight_streaming_amd.stack import ResidentStack
+    T = cfg.tokens
+    st = ResidentStack(hidden=cfg.D, n_experts=cfg.E, top_k=cfg.K, inter=cfg.I, bits=cfg.bits, layers=cfg.layers,
+                       n_shared=cfg.n_shared, group=cfg.group, eps=cfg.eps, n_tokens=T)
+    s = torch.cuda.current_stream().cuda_stream
+    for l in range(cfg.layers):
+        seedgen.dev_blobs(cfg, l, 0, cfg.E, st.expert_ptr(l, 0), s)
+        if cfg.n_shared:
+            seedgen.dev_blobs(cfg, l, seedgen.SHARED_ID, 1, st.shared_ptr(l), s)
+        st.router[l].copy_(torch.from_numpy(seedgen.router(cfg, l)))
+    torch.cuda.synchronize()
+    x = torch.from_numpy(seedgen.activations(cfg, 0, T)).cuda()
+    r = x.clone()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(graph, stream=cs):
+            r.copy_(x)
+            st.step(r, x, stream=cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flags = int(st.workspace[:4].view(torch.int32).item())
+    sel = st.topk_idx.cpu().numpy()  # [L][T][K] of the last step
+    distinct = [len(np.unique(sel[l])) for l in range(cfg.layers)]
+    heavy = [int((np.bincount(sel[l].reshape(-1), minlength=cfg.E) >= 8).sum()) for l in range(cfg.layers)]
+    step_bytes = sum(cfg.E * cfg.D * 4 + (d + cfg.n_shared) * cfg.blob_bytes for d in distinct)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {"workload": f"{cfg.layers}-layer {cfg.bits}-bit stack resident in HBM, batch {T}, output fed back",
+           "tokens_per_step": T, "steps": steps, "ms_per_step": round(ms, 4), "tokens_per_s": round(T * 1e3 / ms, 2),
+           "hbm_bytes_per_step": step_bytes, "hbm_gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "device_flags": flags}
+    if T > 1:
+        out["distinct_experts_per_layer"] = round(float(np.mean(distinct)), 2)
+        out["experts_with_8plus_tokens_per_layer"] = round(float(np.mean(heavy)), 2)
+        out["note"] = "experts with 8+ tokens and the shared expert run on the int8 matrix-core grouped kernels"
+    log(f"{cfg.name}: {out['tokens_per_s']} tok/s, {ms:.3f} ms per step, {gbs:.0f} GB/s, flags {flags}")
+    del st, graph
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +335,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity check")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the host-streamed stack")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 2-bit stacks (batch 1 and batch 32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB), the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -391,6 +451,12 @@ def main():
     }
     if not args.no_stream:
         out["streamed"] = streamed_bench(cfg, st, out0, v0, args.stream_tokens, 2, args.stream_arena_gb)
+    if not args.no_extra:
+        # free the 4-bit stack (and the graph holding its buffers) first
+        del st, graph
+        torch.cuda.empty_cache()
+        out["stack2"] = resident_extra(seedgen.CONFIGS["stack2"], 128, 8)
+        out["stack2_b32"] = resident_extra(seedgen.CONFIGS["stack2_b32"], 8, 2)
     if not args.no_cpu:
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         import workloads as W

@@ -188,6 +188,10 @@ __global__ void __launch_bounds__(256) k_digits(const float *v, int len, int *di
     if (threadIdx.x == 0) inv[b] = r;
 }
 
+// Experts with at least this many tokens in a step take the matrix-core
+// kernels (k_gate_up_m, k_down_m), the others the dot-product kernels.
+constexpr int kMfmaMin = 8;
+
 // Tokens of active item a: routed expert act[a] (positions offset..+count),
 // or, for a == n_act, the shared expert (positions T*K .. T*K+T-1, token j).
 struct Item {
@@ -241,6 +245,7 @@ __global__ void __launch_bounds__(256) k_gate_up_b(BatchArgs a)
     for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
         const int ii = u / upi, i0 = (u - ii * upi) * R;
         const Item it = item_of(a, ii, nact);
+        if (it.n >= kMfmaMin) continue;  // taken by the matrix-core kernel
         uint4 q[CPL][R][2];
         uint32_t sb[CPL][R][2];
 #pragma unroll
@@ -328,6 +333,7 @@ __global__ void __launch_bounds__(256) k_down_b(BatchArgs a)
     for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
         const int ii = u / upi, o0 = (u - ii * upi) * RW;
         const Item it = item_of(a, ii, nact);
+        if (it.n >= kMfmaMin) continue;  // taken by the matrix-core kernel
         uint4 q[CPL][STEPS];
         uint32_t sb[CPL][STEPS];
 #pragma unroll
@@ -436,6 +442,196 @@ __global__ void __launch_bounds__(256) k_combine_b(BatchArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core variants for experts with at least kMfmaMin tokens: the
+// expert's weights meet its tokens as a dense contraction.  One
+// v_mfma_i32_16x16x64_i8 multiplies a 16-row x 64-code tile of masked codes
+// (A, one code per byte) by the tokens' 64 x 16 digits of one plane (B):
+// exact int32 sums over one scale group, so the bf16 scale and bias of the
+// group apply to its three plane sums exactly as in the dot-product path.
+// Lane l supplies row (A) / token (B) l % 16 and the 16 codes of K-slice
+// l / 16; A and B list a slice's codes in the same order (the masked-word
+// order of the digit table), and the C tile arrives as rows 4 (l / 16) + r,
+// token l % 16.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Masked codes of row `q` (the row's packed codes), scale group g, slice h.
+template <int BITS>
+__device__ __forceinline__ v4i mfma_a(const uint8_t *q, int g, int h)
+{
+    using C = Codes<BITS>;
+    v4i r;
+    if constexpr (BITS == 4) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(q + 32 * g + 8 * h);
+        r[0] = (int)(w.x & C::MASK);
+        r[1] = (int)((w.x >> 4) & C::MASK);
+        r[2] = (int)(w.y & C::MASK);
+        r[3] = (int)((w.y >> 4) & C::MASK);
+    } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(q + 16 * g + 4 * h);
+        r[0] = (int)(w & C::MASK);
+        r[1] = (int)((w >> 2) & C::MASK);
+        r[2] = (int)((w >> 4) & C::MASK);
+        r[3] = (int)((w >> 6) & C::MASK);
+    }
+    return r;
+}
+
+// Digit words of plane p matching mfma_a's slice h of group g, from a
+// vector's digit table.
+template <int BITS>
+__device__ __forceinline__ v4i mfma_b(const int *dig, int g, int h, int p)
+{
+    using C = Codes<BITS>;
+    const int4 *src;
+    if constexpr (BITS == 4)
+        src = reinterpret_cast<const int4 *>(dig + (2 * g + (h >> 1)) * C::DW + p * C::PW + 4 * (h & 1));
+    else
+        src = reinterpret_cast<const int4 *>(dig + g * C::DW + p * C::PW + 4 * h);
+    const int4 v = *src;
+    v4i r;
+    r[0] = v.x;
+    r[1] = v.y;
+    r[2] = v.z;
+    r[3] = v.w;
+    return r;
+}
+
+__device__ __forceinline__ float plane_sum(const v4i &c0, const v4i &c1, const v4i &c2, int r)
+{
+    return fmaf((float)c2[r], 65536.f, fmaf((float)c1[r], 256.f, (float)c0[r]));
+}
+
+// Gate/up: a wave unit is RT tiles of 16 intermediate rows of one item x
+// all its tokens (16 at a time); the tokens' digit loads serve all RT tiles.
+template <int BITS, int RT>
+__global__ void __launch_bounds__(256) k_gate_up_m(BatchArgs a)
+{
+    using C = Codes<BITS>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, h = lane >> 4;
+    const int D = a.D, I = a.I;
+    const int nact = *a.n_act;
+    const int items = nact + (a.src.n_slots > a.src.top_k ? 1 : 0);
+    const int upi = I / (16 * RT);  // I is a multiple of 64
+    const int ng = D / kGroup, nchunks = D * BITS / 128;
+    const int xdw = nchunks * C::DW;
+    const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)D * BITS / 8;
+    const uint64_t sb0 = 3 * mat_q, mat_sb = (uint64_t)I * ng * 4;
+    for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
+        const int ii = u / upi, i0 = (u - ii * upi) * 16 * RT;
+        const Item it = item_of(a, ii, nact);
+        if (it.n < kMfmaMin) continue;
+        for (int j0 = 0; j0 < it.n; j0 += 16) {
+            const int jt = j0 + r16;
+            const bool tok_ok = jt < it.n;
+            const int tok = token_of(a, it, tok_ok ? jt : j0);
+            const int *xd = a.xdig + (size_t)tok * xdw;
+            const float *xc = a.xcsum + (size_t)tok * nchunks;
+            const float inv = a.xinv[tok];
+            float acc[RT][2][4];
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[t][m][r] = 0.f;
+            for (int g = 0; g < ng; ++g) {
+                const v4i b0 = mfma_b<BITS>(xd, g, h, 0), b1 = mfma_b<BITS>(xd, g, h, 1), b2 = mfma_b<BITS>(xd, g, h, 2);
+                const float gs = BITS == 4 ? xc[2 * g] + xc[2 * g + 1] : xc[g];
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const v4i av = mfma_a<BITS>(it.blob + m * mat_q + (uint64_t)(i0 + 16 * t + r16) * row_q, g, h);
+                        const v4i z = {0, 0, 0, 0};
+                        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b0, z, 0, 0, 0);
+                        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b1, z, 0, 0, 0);
+                        const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b2, z, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = i0 + 16 * t + 4 * h + r;
+                            const uint32_t sb = *reinterpret_cast<const uint32_t *>(
+                                it.blob + sb0 + m * mat_sb + ((uint64_t)row * ng + g) * 4);
+                            acc[t][m][r] = fmaf(bf16_lo(sb) * inv, plane_sum(c0, c1, c2, r), acc[t][m][r]);
+                            acc[t][m][r] = fmaf(bf16_hi(sb), gs, acc[t][m][r]);
+                        }
+                    }
+            }
+            if (tok_ok) {
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float gg = acc[t][0][r], uu = acc[t][1][r];
+                        a.h[(size_t)(it.pos0 + jt) * I + i0 + 16 * t + 4 * h + r] = gg / (1.f + expf(-gg)) * uu;
+                    }
+            }
+        }
+    }
+}
+
+// Down: a wave unit is RT tiles of 16 output rows of one item x all its
+// positions (16 at a time), against the positions' digit tables of h.
+template <int BITS, int RT>
+__global__ void __launch_bounds__(256) k_down_m(BatchArgs a)
+{
+    using C = Codes<BITS>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, h = lane >> 4;
+    const int D = a.D, I = a.I;
+    const int nact = *a.n_act;
+    const int items = nact + (a.src.n_slots > a.src.top_k ? 1 : 0);
+    const int upi = D / (16 * RT);  // D is a multiple of 64
+    const int ng = I / kGroup, nchunks = I * BITS / 128;
+    const int hdw = nchunks * C::DW;
+    const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)I * BITS / 8;
+    const uint64_t sbd = 3 * mat_q + 2 * ((uint64_t)D * ng * 4);
+    for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
+        const int ii = u / upi, o0 = (u - ii * upi) * 16 * RT;
+        const Item it = item_of(a, ii, nact);
+        if (it.n < kMfmaMin) continue;
+        for (int j0 = 0; j0 < it.n; j0 += 16) {
+            const int jt = j0 + r16;
+            const bool ok = jt < it.n;
+            const int pos = it.pos0 + (ok ? jt : j0);
+            const int *hd = a.hdig + (size_t)pos * hdw;
+            const float *hc = a.hcsum + (size_t)pos * nchunks;
+            const float inv = a.hinv[pos];
+            float acc[RT][4];
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[t][r] = 0.f;
+            for (int g = 0; g < ng; ++g) {
+                const v4i b0 = mfma_b<BITS>(hd, g, h, 0), b1 = mfma_b<BITS>(hd, g, h, 1), b2 = mfma_b<BITS>(hd, g, h, 2);
+                const float gs = BITS == 4 ? hc[2 * g] + hc[2 * g + 1] : hc[g];
+#pragma unroll
+                for (int t = 0; t < RT; ++t) {
+                    const v4i av = mfma_a<BITS>(it.blob + 2 * mat_q + (uint64_t)(o0 + 16 * t + r16) * row_q, g, h);
+                    const v4i z = {0, 0, 0, 0};
+                    const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b0, z, 0, 0, 0);
+                    const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b1, z, 0, 0, 0);
+                    const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b2, z, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = o0 + 16 * t + 4 * h + r;
+                        const uint32_t sb = *reinterpret_cast<const uint32_t *>(it.blob + sbd + ((uint64_t)row * ng + g) * 4);
+                        acc[t][r] = fmaf(bf16_lo(sb) * inv, plane_sum(c0, c1, c2, r), acc[t][r]);
+                        acc[t][r] = fmaf(bf16_hi(sb), gs, acc[t][r]);
+                    }
+                }
+            }
+            if (ok) {
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a.y[(size_t)(it.pos0 + jt) * D + o0 + 16 * t + 4 * h + r] = acc[t][r];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 template <int BITS>
 hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 {
@@ -457,6 +653,7 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
         } else {
             hipLaunchKernelGGL((k_gate_up_b<BITS, 2, 4>), dim3(1024), dim3(256), 0, s, a);
         }
+        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_gate_up_m<BITS, 2>), dim3(1024), dim3(256), 0, s, a);
         break;
     }
     case 2:  // h digits (all positions)
@@ -483,6 +680,7 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
             MOE_DB(64)
         }
 #undef MOE_DB
+        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_down_m<BITS, 2>), dim3(1024), dim3(256), 0, s, a);
         break;
     }
     }

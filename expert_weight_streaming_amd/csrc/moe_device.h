@@ -79,7 +79,8 @@ struct Codes {
     static constexpr int PER_WORD = 32 / BITS;     // codes per word
     static constexpr int SUBS = 8 / BITS;          // masked copies per word
     static constexpr uint32_t MASK = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
-    static constexpr int DW = 4 * SUBS * 3;        // digit words per chunk
+    static constexpr int PW = 4 * SUBS;            // digit words per plane and chunk
+    static constexpr int DW = 3 * PW;              // digit words per chunk
 };
 
 // Fixed-point exponent for a vector whose largest magnitude is amax:
@@ -116,9 +117,11 @@ __device__ __forceinline__ void digit_words(float a, float b, float c, float d, 
                                     0x05040100u);
 }
 
-// Digit words of word k, sub s of one chunk from the chunk's activations
-// v[0..CODES): plane p of (k, s) holds, byte j, the digit of v[k*PER_WORD +
-// s + SUBS*j].  dg index: (k*SUBS + s)*3 + p.
+// Digit words of one chunk from the chunk's activations v[0..CODES): the
+// word of plane p for word k, sub s holds, in byte j, digit p of
+// v[k*PER_WORD + s + SUBS*j].  Plane-major: dg index p*PW + k*SUBS + s, so
+// that the four words matching four masked code words of the same code
+// word(s) sit side by side (one 16-byte load for a matrix-core operand).
 template <int BITS>
 __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
 {
@@ -128,8 +131,8 @@ __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
 #pragma unroll
         for (int s = 0; s < C::SUBS; ++s) {
             const float *u = v + k * C::PER_WORD + s;
-            int *o = dg + (k * C::SUBS + s) * 3;
-            digit_words(u[0], u[C::SUBS], u[2 * C::SUBS], u[3 * C::SUBS], mul, o[0], o[1], o[2]);
+            int *o = dg + k * C::SUBS + s;
+            digit_words(u[0], u[C::SUBS], u[2 * C::SUBS], u[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
         }
 }
 
@@ -146,10 +149,10 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
 #pragma unroll
         for (int s = 0; s < C::SUBS; ++s) {
             const int m = (int)((w[k] >> (BITS * s)) & C::MASK);
-            const int *d = dg + (k * C::SUBS + s) * 3;
+            const int *d = dg + k * C::SUBS + s;
             a0 = __builtin_amdgcn_sdot4(m, d[0], a0, false);
-            a1 = __builtin_amdgcn_sdot4(m, d[1], a1, false);
-            a2 = __builtin_amdgcn_sdot4(m, d[2], a2, false);
+            a1 = __builtin_amdgcn_sdot4(m, d[C::PW], a1, false);
+            a2 = __builtin_amdgcn_sdot4(m, d[2 * C::PW], a2, false);
         }
     return fmaf((float)a2, 65536.f, fmaf((float)a1, 256.f, (float)a0));
 }
@@ -206,8 +209,8 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
         const int c = t / (4 * C::SUBS), r = t - c * 4 * C::SUBS;
         const int k = r / C::SUBS, s = r - k * C::SUBS;
         const float *v = x + c * C::CODES + k * C::PER_WORD + s;
-        int *o = dig + c * C::DW + (k * C::SUBS + s) * 3;
-        digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[1], o[2]);
+        int *o = dig + c * C::DW + k * C::SUBS + s;
+        digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
     }
     chunk_sums<BITS>(x, n / C::CODES, csum);
     __syncthreads();

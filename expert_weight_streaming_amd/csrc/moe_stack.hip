@@ -310,8 +310,8 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             const int kw = r / C::SUBS, s = r - kw * C::SUBS;
             const float mul = hmul[kc / cpk];
             const float *v = hs + kc * C::CODES + kw * C::PER_WORD + s;
-            int *o = hdig + kc * C::DW + (kw * C::SUBS + s) * 3;
-            digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[1], o[2]);
+            int *o = hdig + kc * C::DW + kw * C::SUBS + s;
+            digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
         }
         chunk_sums<BITS>(hs, S * cpk, hcsum);
         __syncthreads();

@@ -130,3 +130,38 @@ def test_batched_expert_forward_forced_and_batch_equals_singles():
         want = want + oracle.expert(ref.shared, cfg.D, cfg.I, cfg.bits, cfg.group, x64)[1]
         W.assert_close(y[t].cpu().numpy(), want, f"batched combine token {t}")
         W.assert_close(y[t].cpu().numpy(), y1.cpu().numpy(), f"batch vs single token {t}", rel=1e-5)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_batched_matrix_core_path_hidden4096(bits):
+    """Hidden 4096, inter 1024, 32 experts, 48 skewed tokens: most selected
+    experts receive 8+ tokens (the matrix-core grouped kernels), a few fewer
+    (the dot-product kernels); every token against the oracle and against
+    the same token run alone."""
+    cfg = CFG["layer"].replace(E=32, bits=bits, seed=0x5EED00F0 + bits)
+    T = 48
+    print(f"[gpu case] matrix-core batch bits={bits}", flush=True)
+    base = seedgen.activation(cfg, 0)
+    x = (base[None, :] + 0.35 * seedgen.activations(cfg, 1, T)).astype(np.float32)
+    st = W.build_stack(cfg, layers=1, T=T)
+    rd, xd = torch.from_numpy(x.copy()).cuda(), torch.from_numpy(x.copy()).cuda()
+    st.layer_step(0, rd, xd)
+    torch.cuda.synchronize()
+    assert int(st.workspace[:4].view(torch.int32).item()) == 0
+    sel = st.topk_idx[0].cpu().numpy()
+    counts = np.bincount(sel.reshape(-1), minlength=cfg.E)
+    big, small = int((counts >= 8).sum()), int(((counts > 0) & (counts < 8)).sum())
+    print(f"experts with >= 8 tokens: {big}, with 1..7: {small}", flush=True)
+    assert big >= 2 and small >= 1, counts
+    ref = W.LayerRef(cfg, 0)
+    wts = st.topk_w[0].cpu().numpy()
+    gr, gx = rd.cpu().numpy(), xd.cpu().numpy()
+    for t in range(0, T, 5):
+        W.check_layer(ref, x[t], x[t], sel[t], wts[t], gr[t], gx[t])
+    st1 = W.build_stack(cfg, layers=1, T=1)
+    for t in (0, 17, 47):
+        r1, x1 = torch.from_numpy(x[t].copy()).cuda().view(1, -1), torch.from_numpy(x[t].copy()).cuda().view(1, -1)
+        st1.layer_step(0, r1, x1)
+        torch.cuda.synchronize()
+        assert sorted(st1.topk_idx[0, 0].cpu().tolist()) == sorted(sel[t].tolist())
+        W.assert_close(gx[t], x1[0].cpu().numpy(), f"batch vs single token {t}", rel=1e-5)

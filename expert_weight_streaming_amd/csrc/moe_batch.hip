@@ -6,16 +6,20 @@
 // every selected expert's rows are fetched once per step and applied to all
 // of that expert's tokens:
 //
-//   k_route_b      logits[t][e] for all tokens (each router row read once)
-//   k_topk_group   per-token top-K and softmax weights, then the grouping:
-//                  count[e], offset[e] (exclusive prefix sum), the pair
-//                  permutation perm[pos] = t*K + k sorted by (expert, pair
-//                  index), its inverse, and the list of active experts
+//   k_route_m      logits[t][e] for all tokens (fp32 matrix cores)
+//   k_topk_b       per-token top-K and softmax weights (one wave per token)
+//   k_group        the grouping: count[e], offset[e] (exclusive prefix
+//                  sum), the pair permutation perm[pos] = t*K + k sorted by
+//                  (expert, pair index), its inverse, and the list of active
+//                  experts
 //   k_digits       fixed-point digit tables of the tokens' activations
 //   k_gate_up_b    per active expert (and the shared expert, all tokens):
 //                  gate/up rows x that expert's tokens, SwiGLU -> h[pos]
+//                  (k_gate_up_m on the matrix cores for experts with 8+
+//                  tokens)
 //   k_digits       digit tables of h
 //   k_down_b       per active expert: down rows x its tokens' h -> y[pos]
+//                  (k_down_m for experts with 8+ tokens)
 //   k_combine_b    per token, in slot order: sum_k w_k y[pos(t,k)] + the
 //                  shared expert's y, then (layer mode) residual + RMSNorm
 //
@@ -28,116 +32,149 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
-// Router for T tokens: one row per wave, 4 rows per block; the tokens'
-// activations pass through LDS in 256-column slices.
-template <int TT>
-__global__ void __launch_bounds__(256) k_route_b(BatchArgs a)
+// Router for T tokens on the matrix cores (fp32): a block owns a tile of 16
+// router rows x 16 tokens, its four waves take every fourth 64-column block
+// of the hidden dimension, and their partial logits are added in order in
+// LDS.
+// v_mfma_f32_16x16x4f32: lane l supplies row (A) / token (B) l % 16 at
+// k = l / 16; each lane loads 4 consecutive columns, so 4 instructions
+// cover 16 columns (A and B use the same column-to-instruction map).
+typedef float v4f __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) k_route_m(BatchArgs a)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = blockIdx.x * 4 + wave;
-    constexpr int CH = 256;
-    __shared__ __align__(16) float xs[TT][CH];
-    float acc[TT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, h = lane >> 4;
+    const int D = a.D, E = a.E, T = a.T;
+    const int ttiles = (T + 15) / 16;
+    const int e0 = (blockIdx.x / ttiles) * 16, t0 = (blockIdx.x % ttiles) * 16;
+    const int row = min(e0 + r16, E - 1), tok = min(t0 + r16, T - 1);
+    const float *w = a.router + (size_t)row * D;
+    const float *x = a.x + (size_t)tok * D;
+    // wave w: the 64-column blocks w, w + 4, ... (D is a multiple of 64)
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 64 * wave; k0 < D; k0 += 256) {
+        float4 wv[4], xv[4];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-    for (int t0 = 0; t0 < a.T; t0 += TT) {
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-        for (int c0 = 0; c0 < a.D; c0 += CH) {
-            __syncthreads();
-            for (int i = tid; i < TT * CH; i += 256) {
-                const int t = i / CH, c = i - t * CH;
-                xs[t][c] = (t0 + t < a.T && c0 + c < a.D) ? a.x[(size_t)(t0 + t) * a.D + c0 + c] : 0.f;
-            }
-            __syncthreads();
-            if (row < a.E && c0 + 4 * lane < a.D) {
-                const float4 w = *reinterpret_cast<const float4 *>(a.router + (size_t)row * a.D + c0 + 4 * lane);
-#pragma unroll
-                for (int t = 0; t < TT; ++t) {
-                    const float4 v = *reinterpret_cast<const float4 *>(&xs[t][4 * lane]);
-                    acc[t] = fmaf(w.x, v.x, fmaf(w.y, v.y, fmaf(w.z, v.z, fmaf(w.w, v.w, acc[t]))));
-                }
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int k = k0 + 16 * u + 4 * h;
+            wv[u] = *reinterpret_cast<const float4 *>(w + k);
+            xv[u] = *reinterpret_cast<const float4 *>(x + k);
         }
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const float v = group_sum<64>(acc[t]);
-            if (lane == 0 && row < a.E && t0 + t < a.T) a.logits[(size_t)(t0 + t) * a.E + row] = v;
+        for (int u = 0; u < 4; ++u) {
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u].x, xv[u].x, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u].y, xv[u].y, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u].z, xv[u].z, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u].w, xv[u].w, c, 0, 0, 0);
+        }
+    }
+    __shared__ float part[4][64][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][lane][r] = c[r];
+    __syncthreads();
+    if (wave == 0) {
+        const int t = t0 + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = e0 + 4 * h + r;
+            const float v = ((part[0][lane][r] + part[1][lane][r]) + part[2][lane][r]) + part[3][lane][r];
+            if (e < E && t < T) a.logits[(size_t)t * E + e] = v;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// One block of 1024 threads: top-K of every token (unless the routing is
-// given), then the token -> expert grouping.
-__global__ void __launch_bounds__(1024) k_topk_group(BatchArgs a, int do_topk)
+// Top-K of every token: one wave per token, its logits in LDS; K rounds of
+// the wave's largest remaining key (larger logit first, the lower index on a
+// tie), then the softmax over the selected logits.
+__global__ void __launch_bounds__(256) k_topk_b(BatchArgs a)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int T = a.T, K = a.K, E = a.E, P = T * K;
-    __shared__ float lg[16][512];
-    __shared__ int s_idx[64 * kMaxTopK];
-    __shared__ int s_count[4096];
-    __shared__ int s_off[4097];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    const int E = a.E, K = a.K;
+    __shared__ float lg[4][4096];
+    if (t >= a.T) return;  // whole waves leave; no block barrier follows
+    for (int e = lane; e < E; e += 64) lg[wave][e] = a.logits[(size_t)t * E + e];
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    uint64_t taken = 0;  // bit j: element lane + 64 j selected
+    int idx[kMaxTopK];
+    float vals[kMaxTopK], w[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        idx[k] = -1;
+        vals[k] = -INFINITY;
+        if (k >= K) continue;
+        uint64_t best = 0ull;
+        for (int jj = 0, e = lane; e < E; ++jj, e += 64)
+            if (!((taken >> jj) & 1ull)) {
+                const uint64_t key = route_key(lg[wave][e], e);
+                best = key > best ? key : best;
+            }
+        const uint64_t m = wave_max_key(best);
+        const int e = key_index(m);
+        if ((e & 63) == lane) taken |= 1ull << (e >> 6);
+        idx[k] = e;
+        vals[k] = key_value(m);
+    }
+    topk_weights(vals, K, w);
+    if (lane < K) {
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            if (k == lane) {
+                a.topk_idx[(size_t)t * K + k] = idx[k];
+                a.topk_w[(size_t)t * K + k] = w[k];
+            }
+    }
+}
 
-    if (do_topk) {
-        for (int t = wave; t < T; t += 16) {
-            // logits of token t, 512 at a time into this wave's LDS row
-            int idx[kMaxTopK];
-            float vals[kMaxTopK];
-            // top-K over E in slices: keep the running best K (merge by repeated selection)
-            float bestv[kMaxTopK];
-            int besti[kMaxTopK];
+// Exclusive prefix sums of v[0..n) in place (n <= 4 * blockDim.x), plus the
+// total; one block.  Each thread sums 4 consecutive entries, then a
+// Hillis-Steele scan over the threads' sums in LDS.
+__device__ __forceinline__ int block_exscan(int *v, int n, int *part)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int loc[4], run = 0;
 #pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) {
-                bestv[k] = -INFINITY;
-                besti[k] = -1;
-            }
-            for (int e0 = 0; e0 < E; e0 += 512) {
-                const int n = E - e0 < 512 ? E - e0 : 512;
-                for (int e = lane; e < n; e += 64) lg[wave][e] = a.logits[(size_t)t * E + e0 + e];
-                __builtin_amdgcn_s_waitcnt(0);
-                __builtin_amdgcn_wave_barrier();
-                wave_topk(lg[wave], n, K, lane, idx, vals);
-                // merge this slice's K with the running K: both sorted descending
-                float mv[kMaxTopK];
-                int mi[kMaxTopK];
-                int p = 0, q = 0;
-#pragma unroll
-                for (int k = 0; k < kMaxTopK; ++k) {
-                    if (k >= K) {
-                        mv[k] = -INFINITY;
-                        mi[k] = -1;
-                        continue;
-                    }
-                    const int gi = idx[q] < 0 ? -1 : idx[q] + e0;
-                    // running entries have lower indices than this slice's: ties keep them first
-                    const bool take_run = besti[p] >= 0 && (gi < 0 || bestv[p] >= vals[q]);
-                    mv[k] = take_run ? bestv[p] : vals[q];
-                    mi[k] = take_run ? besti[p] : gi;
-                    if (take_run) ++p;
-                    else ++q;
-                }
-#pragma unroll
-                for (int k = 0; k < kMaxTopK; ++k) {
-                    bestv[k] = mv[k];
-                    besti[k] = mi[k];
-                }
-                __builtin_amdgcn_wave_barrier();
-            }
-            float w[kMaxTopK];
-            topk_weights(bestv, K, w);
-            if (lane == 0) {
-#pragma unroll
-                for (int k = 0; k < kMaxTopK; ++k) {
-                    if (k >= K) continue;
-                    a.topk_idx[(size_t)t * K + k] = besti[k];
-                    a.topk_w[(size_t)t * K + k] = w[k];
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
+    for (int q = 0; q < 4; ++q) {
+        const int i = 4 * tid + q;
+        loc[q] = run;
+        run += i < n ? v[i] : 0;
+    }
+    part[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < nt; off <<= 1) {
+        const int add = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += add;
         __syncthreads();
     }
+    const int before = tid > 0 ? part[tid - 1] : 0;
+    const int total = part[nt - 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = 4 * tid + q;
+        if (i < n) v[i] = before + loc[q];
+    }
+    __syncthreads();
+    return total;
+}
+
+// One block of 1024 threads: the token -> expert grouping of the
+// selections: count[e], offset[e] (exclusive prefix sums), the pair
+// permutation perm[pos] = t*K + k sorted by (expert, pair index), its
+// inverse, the active experts in ascending order and, among them, those
+// with at least kMfmaMin tokens (the matrix-core kernels' work list).
+__global__ void __launch_bounds__(1024) k_group(BatchArgs a)
+{
+    const int tid = threadIdx.x;
+    const int T = a.T, K = a.K, E = a.E, P = T * K;
+    __shared__ int s_idx[64 * kMaxTopK];
+    __shared__ int s_count[4096];
+    __shared__ int s_off[4096];
+    __shared__ int s_flag[4096];
+    __shared__ int s_big[4096];
+    __shared__ int part[1024];
     for (int p = tid; p < P; p += 1024) s_idx[p] = a.topk_idx[p];
     for (int e = tid; e < E; e += 1024) s_count[e] = 0;
     __syncthreads();
@@ -147,20 +184,26 @@ __global__ void __launch_bounds__(1024) k_topk_group(BatchArgs a, int do_topk)
         else atomicOr(a.flags, MOE_DEVERR_EXPERT_RANGE);
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0, nact = 0;
-        for (int e = 0; e < E; ++e) {
-            s_off[e] = run;
-            a.offset[e] = run;
-            a.count[e] = s_count[e];
-            if (s_count[e]) a.act[nact++] = e;
-            run += s_count[e];
-        }
-        s_off[E] = run;
-        a.offset[E] = run;
-        *a.n_act = nact;
+    for (int e = tid; e < E; e += 1024) {
+        s_off[e] = s_count[e];
+        s_flag[e] = s_count[e] > 0;
+        s_big[e] = s_count[e] >= kMfmaMin;
+        a.count[e] = s_count[e];
     }
     __syncthreads();
+    const int total = block_exscan(s_off, E, part);
+    const int nact = block_exscan(s_flag, E, part);
+    const int nbig = block_exscan(s_big, E, part);
+    for (int e = tid; e < E; e += 1024) {
+        a.offset[e] = s_off[e];
+        if (s_count[e]) a.act[s_flag[e]] = e;
+        if (s_count[e] >= kMfmaMin) a.big[s_big[e]] = e;
+    }
+    if (tid == 0) {
+        a.offset[E] = total;
+        *a.n_act = nact;
+        *a.n_big = nbig;
+    }
     for (int p = tid; p < P; p += 1024) {
         const int e = s_idx[p];
         if (e < 0 || e >= E) {
@@ -188,10 +231,6 @@ __global__ void __launch_bounds__(256) k_digits(const float *v, int len, int *di
     if (threadIdx.x == 0) inv[b] = r;
 }
 
-// Experts with at least this many tokens in a step take the matrix-core
-// kernels (k_gate_up_m, k_down_m), the others the dot-product kernels.
-constexpr int kMfmaMin = 8;
-
 // Tokens of active item a: routed expert act[a] (positions offset..+count),
 // or, for a == n_act, the shared expert (positions T*K .. T*K+T-1, token j).
 struct Item {
@@ -205,6 +244,26 @@ __device__ __forceinline__ Item item_of(const BatchArgs &a, int it, int nact)
     Item r;
     if (it < nact) {
         const int e = a.act[it];
+        r.blob = a.src.experts + (uint64_t)e * a.src.blob_bytes;
+        r.pos0 = a.offset[e];
+        r.n = a.count[e];
+        r.slot = 0;
+    } else {
+        r.blob = a.src.shared;
+        r.pos0 = a.T * a.K;
+        r.n = a.T;
+        r.slot = 1;
+    }
+    return r;
+}
+
+// Item ii of the matrix-core work list: expert big[ii], or the shared
+// expert for ii == n_big.
+__device__ __forceinline__ Item big_item_of(const BatchArgs &a, int ii, int nbig)
+{
+    Item r;
+    if (ii < nbig) {
+        const int e = a.big[ii];
         r.blob = a.src.experts + (uint64_t)e * a.src.blob_bytes;
         r.pos0 = a.offset[e];
         r.n = a.count[e];
@@ -394,7 +453,7 @@ __global__ void __launch_bounds__(256) k_down_b(BatchArgs a)
 // ---------------------------------------------------------------------------
 // Per token: combine in slot order (routed k = 0..K-1, then shared), then
 // (mode 1) residual + RMSNorm; one block per token.
-__global__ void __launch_bounds__(256) k_combine_b(BatchArgs a)
+__global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
 {
     const int t = blockIdx.x, tid = threadIdx.x;
     const int D = a.D, K = a.K;
@@ -407,36 +466,50 @@ __global__ void __launch_bounds__(256) k_combine_b(BatchArgs a)
     }
     __syncthreads();
     const bool has_shared = a.src.n_slots > K;
-    constexpr int PER = 32;
+    constexpr int PER = 8;  // D <= 8192
     float rv[PER];
     float ss = 0.f;
+    // the combine of the token's rows first (the outputs never alias y),
+    // summed in slot order, then residual and norm
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int o = tid + 256 * j;
-        rv[j] = 0.f;
-        if (o >= D) continue;
+        const int o = tid + 1024 * j;
         float c = 0.f;
-        for (int k = 0; k < K; ++k)
-            if (pos[k] >= 0) c += wts[k] * a.y[(size_t)pos[k] * D + o];
-        if (has_shared) c += a.y[(size_t)(a.T * K + t) * D + o];
+        if (o < D) {
+            for (int k = 0; k < K; ++k)
+                if (pos[k] >= 0) c += wts[k] * a.y[(size_t)pos[k] * D + o];
+            if (has_shared) c += a.y[(size_t)(a.T * K + t) * D + o];
+        }
+        rv[j] = c;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int o = tid + 1024 * j;
+        if (o >= D) continue;
         if (a.mode == 0) {
-            a.yout[(size_t)t * D + o] = c;
+            a.yout[(size_t)t * D + o] = rv[j];
         } else {
-            const float r = a.resid[(size_t)t * D + o] + c;
-            a.resid[(size_t)t * D + o] = r;
+            const float r = a.resid[(size_t)t * D + o] + rv[j];
             rv[j] = r;
             ss += r * r;
         }
     }
     if (a.mode == 0) return;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int o = tid + 1024 * j;
+        if (o < D) a.resid[(size_t)t * D + o] = rv[j];
+    }
     ss = group_sum<64>(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tot += red[w];
     const float inv = 1.f / sqrtf(tot / (float)D + a.eps);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int o = tid + 256 * j;
+        const int o = tid + 1024 * j;
         if (o < D) a.xout[(size_t)t * D + o] = rv[j] * inv * a.gamma[o];
     }
 }
@@ -501,132 +574,176 @@ __device__ __forceinline__ float plane_sum(const v4i &c0, const v4i &c1, const v
     return fmaf((float)c2[r], 65536.f, fmaf((float)c1[r], 256.f, (float)c0[r]));
 }
 
-// Gate/up: a wave unit is RT tiles of 16 intermediate rows of one item x
-// all its tokens (16 at a time); the tokens' digit loads serve all RT tiles.
-template <int BITS, int RT>
-__global__ void __launch_bounds__(256) k_gate_up_m(BatchArgs a)
+// One scale group's operands for a wave: the masked codes of M matrices'
+// rows (A), the digit words of the three planes (B), the lane's four output
+// rows' scale/bias words and the chunk sums of the group.
+template <int M>
+struct MfStage {
+    v4i a[M];
+    v4i b0, b1, b2;
+    uint32_t sb[M][4];
+    float gs;
+};
+
+template <int BITS, int M>
+__device__ __forceinline__ void mf_load(MfStage<M> &st, const uint8_t *const (&rowq)[M], const uint8_t *const (&sbr)[M],
+                                        uint32_t sb_stride, const int *dig, const float *cs, int g, int h)
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        st.a[m] = mfma_a<BITS>(rowq[m], g, h);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.sb[m][r] = *reinterpret_cast<const uint32_t *>(sbr[m] + (size_t)r * sb_stride + 4 * g);
+    }
+    st.b0 = mfma_b<BITS>(dig, g, h, 0);
+    st.b1 = mfma_b<BITS>(dig, g, h, 1);
+    st.b2 = mfma_b<BITS>(dig, g, h, 2);
+    st.gs = BITS == 4 ? cs[2 * g] + cs[2 * g + 1] : cs[g];
+}
+
+template <int M>
+__device__ __forceinline__ void mf_step(const MfStage<M> &st, float inv, float (&acc)[M][4])
+{
+    const v4i z = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[m], st.b0, z, 0, 0, 0);
+        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[m], st.b1, z, 0, 0, 0);
+        const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[m], st.b2, z, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc[m][r] = fmaf(bf16_lo(st.sb[m][r]) * inv, plane_sum(c0, c1, c2, r), acc[m][r]);
+            acc[m][r] = fmaf(bf16_hi(st.sb[m][r]), st.gs, acc[m][r]);
+        }
+    }
+}
+
+// A wave's share of the contraction of one 16-row tile (M matrices) with
+// one 16-vector tile: scale groups g0, g0 + gs, ... below ng, in batches of
+// NB groups whose loads are all issued before the batch's arithmetic.
+template <int BITS, int M, int NB>
+__device__ __forceinline__ void mf_tile(const uint8_t *const (&rowq)[M], const uint8_t *const (&sbr)[M], uint32_t sb_stride,
+                                        const int *dig, const float *cs, float inv, int g0, int gs, int ng, int h,
+                                        float (&acc)[M][4])
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][r] = 0.f;
+    for (int gb = g0; gb < ng; gb += NB * gs) {
+        MfStage<M> st[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (gb + b * gs < ng) mf_load<BITS, M>(st[b], rowq, sbr, sb_stride, dig, cs, gb + b * gs, h);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (gb + b * gs < ng) mf_step<M>(st[b], inv, acc);
+    }
+}
+
+// The partial tiles of the block's KS waves, added in wave order into wave
+// 0's lanes.
+template <int M, int KS>
+__device__ __forceinline__ void mf_reduce(float (&acc)[M][4], float (*part)[M][64][4])
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave > 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[wave - 1][m][lane][r] = acc[m][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[m][r] += part[w][m][lane][r];
+    }
+    __syncthreads();
+}
+
+constexpr int kMfWaves = 8;  // waves per matrix-core block (scale groups split over them)
+
+// Gate/up: a block unit is one 16-row tile of an item's gate and up
+// matrices x one tile of 16 of its tokens; the block's kMfWaves waves take
+// every kMfWaves-th scale group and their partial sums meet in LDS.
+template <int BITS>
+__global__ void __launch_bounds__(64 * kMfWaves) k_gate_up_m(BatchArgs a)
 {
     using C = Codes<BITS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, h = lane >> 4;
-    const int D = a.D, I = a.I;
-    const int nact = *a.n_act;
-    const int items = nact + (a.src.n_slots > a.src.top_k ? 1 : 0);
-    const int upi = I / (16 * RT);  // I is a multiple of 64
+    const int D = a.D, I = a.I, T = a.T;
+    const int nbig = *a.n_big;
+    const int items = nbig + (a.src.n_slots > a.src.top_k && T >= kMfmaMin ? 1 : 0);
+    const int rtiles = I / 16, ttiles = (T + 15) / 16;  // I is a multiple of 64
     const int ng = D / kGroup, nchunks = D * BITS / 128;
     const int xdw = nchunks * C::DW;
     const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)D * BITS / 8;
     const uint64_t sb0 = 3 * mat_q, mat_sb = (uint64_t)I * ng * 4;
-    for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
-        const int ii = u / upi, i0 = (u - ii * upi) * 16 * RT;
-        const Item it = item_of(a, ii, nact);
-        if (it.n < kMfmaMin) continue;
-        for (int j0 = 0; j0 < it.n; j0 += 16) {
-            const int jt = j0 + r16;
-            const bool tok_ok = jt < it.n;
-            const int tok = token_of(a, it, tok_ok ? jt : j0);
-            const int *xd = a.xdig + (size_t)tok * xdw;
-            const float *xc = a.xcsum + (size_t)tok * nchunks;
-            const float inv = a.xinv[tok];
-            float acc[RT][2][4];
+    __shared__ float part[kMfWaves - 1][2][64][4];
+    for (int u = blockIdx.x; u < items * rtiles * ttiles; u += gridDim.x) {
+        const int ii = u / (rtiles * ttiles), rem = u - ii * rtiles * ttiles;
+        const int i0 = (rem / ttiles) * 16, j0 = (rem % ttiles) * 16;
+        const Item it = big_item_of(a, ii, nbig);
+        if (j0 >= it.n) continue;  // uniform over the block
+        const int jt = j0 + r16;
+        const bool tok_ok = jt < it.n;
+        const int tok = token_of(a, it, tok_ok ? jt : j0);
+        const uint8_t *const rowq[2] = {it.blob + (uint64_t)(i0 + r16) * row_q, it.blob + mat_q + (uint64_t)(i0 + r16) * row_q};
+        const uint8_t *const sbr[2] = {it.blob + sb0 + (uint64_t)(i0 + 4 * h) * ng * 4,
+                                       it.blob + sb0 + mat_sb + (uint64_t)(i0 + 4 * h) * ng * 4};
+        float acc[2][4];
+        mf_tile<BITS, 2, 4>(rowq, sbr, ng * 4, a.xdig + (size_t)tok * xdw, a.xcsum + (size_t)tok * nchunks, a.xinv[tok], wave,
+                            kMfWaves, ng, h, acc);
+        mf_reduce<2, kMfWaves>(acc, part);
+        if (wave == 0 && tok_ok) {
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t][m][r] = 0.f;
-            for (int g = 0; g < ng; ++g) {
-                const v4i b0 = mfma_b<BITS>(xd, g, h, 0), b1 = mfma_b<BITS>(xd, g, h, 1), b2 = mfma_b<BITS>(xd, g, h, 2);
-                const float gs = BITS == 4 ? xc[2 * g] + xc[2 * g + 1] : xc[g];
-#pragma unroll
-                for (int t = 0; t < RT; ++t)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        const v4i av = mfma_a<BITS>(it.blob + m * mat_q + (uint64_t)(i0 + 16 * t + r16) * row_q, g, h);
-                        const v4i z = {0, 0, 0, 0};
-                        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b0, z, 0, 0, 0);
-                        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b1, z, 0, 0, 0);
-                        const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b2, z, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = i0 + 16 * t + 4 * h + r;
-                            const uint32_t sb = *reinterpret_cast<const uint32_t *>(
-                                it.blob + sb0 + m * mat_sb + ((uint64_t)row * ng + g) * 4);
-                            acc[t][m][r] = fmaf(bf16_lo(sb) * inv, plane_sum(c0, c1, c2, r), acc[t][m][r]);
-                            acc[t][m][r] = fmaf(bf16_hi(sb), gs, acc[t][m][r]);
-                        }
-                    }
-            }
-            if (tok_ok) {
-#pragma unroll
-                for (int t = 0; t < RT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float gg = acc[t][0][r], uu = acc[t][1][r];
-                        a.h[(size_t)(it.pos0 + jt) * I + i0 + 16 * t + 4 * h + r] = gg / (1.f + expf(-gg)) * uu;
-                    }
+            for (int r = 0; r < 4; ++r) {
+                const float gg = acc[0][r], uu = acc[1][r];
+                a.h[(size_t)(it.pos0 + jt) * I + i0 + 4 * h + r] = gg / (1.f + expf(-gg)) * uu;
             }
         }
     }
 }
 
-// Down: a wave unit is RT tiles of 16 output rows of one item x all its
-// positions (16 at a time), against the positions' digit tables of h.
-template <int BITS, int RT>
-__global__ void __launch_bounds__(256) k_down_m(BatchArgs a)
+// Down: a block unit is one 16-row tile of an item's down matrix x one tile
+// of 16 of its positions (digit tables of h), scale groups split over the
+// waves as above.
+template <int BITS>
+__global__ void __launch_bounds__(64 * kMfWaves) k_down_m(BatchArgs a)
 {
     using C = Codes<BITS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, h = lane >> 4;
-    const int D = a.D, I = a.I;
-    const int nact = *a.n_act;
-    const int items = nact + (a.src.n_slots > a.src.top_k ? 1 : 0);
-    const int upi = D / (16 * RT);  // D is a multiple of 64
+    const int D = a.D, I = a.I, T = a.T;
+    const int nbig = *a.n_big;
+    const int items = nbig + (a.src.n_slots > a.src.top_k && T >= kMfmaMin ? 1 : 0);
+    const int rtiles = D / 16, ttiles = (T + 15) / 16;  // D is a multiple of 64
     const int ng = I / kGroup, nchunks = I * BITS / 128;
     const int hdw = nchunks * C::DW;
     const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)I * BITS / 8;
     const uint64_t sbd = 3 * mat_q + 2 * ((uint64_t)D * ng * 4);
-    for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
-        const int ii = u / upi, o0 = (u - ii * upi) * 16 * RT;
-        const Item it = item_of(a, ii, nact);
-        if (it.n < kMfmaMin) continue;
-        for (int j0 = 0; j0 < it.n; j0 += 16) {
-            const int jt = j0 + r16;
-            const bool ok = jt < it.n;
-            const int pos = it.pos0 + (ok ? jt : j0);
-            const int *hd = a.hdig + (size_t)pos * hdw;
-            const float *hc = a.hcsum + (size_t)pos * nchunks;
-            const float inv = a.hinv[pos];
-            float acc[RT][4];
+    __shared__ float part[kMfWaves - 1][1][64][4];
+    for (int u = blockIdx.x; u < items * rtiles * ttiles; u += gridDim.x) {
+        const int ii = u / (rtiles * ttiles), rem = u - ii * rtiles * ttiles;
+        const int o0 = (rem / ttiles) * 16, j0 = (rem % ttiles) * 16;
+        const Item it = big_item_of(a, ii, nbig);
+        if (j0 >= it.n) continue;  // uniform over the block
+        const int jt = j0 + r16;
+        const bool ok = jt < it.n;
+        const int pos = it.pos0 + (ok ? jt : j0);
+        const uint8_t *const rowq[1] = {it.blob + 2 * mat_q + (uint64_t)(o0 + r16) * row_q};
+        const uint8_t *const sbr[1] = {it.blob + sbd + (uint64_t)(o0 + 4 * h) * ng * 4};
+        float acc[1][4];
+        mf_tile<BITS, 1, 8>(rowq, sbr, ng * 4, a.hdig + (size_t)pos * hdw, a.hcsum + (size_t)pos * nchunks, a.hinv[pos], wave,
+                            kMfWaves, ng, h, acc);
+        mf_reduce<1, kMfWaves>(acc, part);
+        if (wave == 0 && ok) {
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[t][r] = 0.f;
-            for (int g = 0; g < ng; ++g) {
-                const v4i b0 = mfma_b<BITS>(hd, g, h, 0), b1 = mfma_b<BITS>(hd, g, h, 1), b2 = mfma_b<BITS>(hd, g, h, 2);
-                const float gs = BITS == 4 ? hc[2 * g] + hc[2 * g + 1] : hc[g];
-#pragma unroll
-                for (int t = 0; t < RT; ++t) {
-                    const v4i av = mfma_a<BITS>(it.blob + 2 * mat_q + (uint64_t)(o0 + 16 * t + r16) * row_q, g, h);
-                    const v4i z = {0, 0, 0, 0};
-                    const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b0, z, 0, 0, 0);
-                    const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b1, z, 0, 0, 0);
-                    const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b2, z, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = o0 + 16 * t + 4 * h + r;
-                        const uint32_t sb = *reinterpret_cast<const uint32_t *>(it.blob + sbd + ((uint64_t)row * ng + g) * 4);
-                        acc[t][r] = fmaf(bf16_lo(sb) * inv, plane_sum(c0, c1, c2, r), acc[t][r]);
-                        acc[t][r] = fmaf(bf16_hi(sb), gs, acc[t][r]);
-                    }
-                }
-            }
-            if (ok) {
-#pragma unroll
-                for (int t = 0; t < RT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) a.y[(size_t)(it.pos0 + jt) * D + o0 + 16 * t + 4 * h + r] = acc[t][r];
-            }
+            for (int r = 0; r < 4; ++r) a.y[(size_t)(it.pos0 + jt) * D + o0 + 4 * h + r] = acc[0][r];
         }
     }
 }
@@ -653,7 +770,7 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
         } else {
             hipLaunchKernelGGL((k_gate_up_b<BITS, 2, 4>), dim3(1024), dim3(256), 0, s, a);
         }
-        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_gate_up_m<BITS, 2>), dim3(1024), dim3(256), 0, s, a);
+        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_gate_up_m<BITS>), dim3(1024), dim3(64 * kMfWaves), 0, s, a);
         break;
     }
     case 2:  // h digits (all positions)
@@ -680,7 +797,7 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
             MOE_DB(64)
         }
 #undef MOE_DB
-        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_down_m<BITS, 2>), dim3(1024), dim3(256), 0, s, a);
+        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_down_m<BITS>), dim3(1024), dim3(64 * kMfWaves), 0, s, a);
         break;
     }
     }
@@ -692,12 +809,13 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s)
 {
     if (do_topk) {
-        if (a.T <= 8) hipLaunchKernelGGL(k_route_b<8>, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(k_route_b<32>, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_route_m, dim3(((a.E + 15) / 16) * ((a.T + 15) / 16)), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_topk_b, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_topk_group, dim3(1), dim3(1024), 0, s, a, do_topk);
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
@@ -707,7 +825,7 @@ hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s)
         hipError_t e = bits == 4 ? batch_bits<4>(a, stage, s) : batch_bits<2>(a, stage, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_combine_b, dim3(a.T), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_combine_b, dim3(a.T), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 

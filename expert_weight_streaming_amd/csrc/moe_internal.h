@@ -13,6 +13,9 @@ constexpr int kMaxTopK = 8;
 constexpr int kMaxSlots = kMaxTopK + 1;  // routed + shared
 constexpr int kMaxLayerBlocks = 1024;    // grid cap of the persistent stack kernel
 constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
+// In a batch, experts with at least this many tokens take the matrix-core
+// grouped kernels, the others the dot-product ones.
+constexpr int kMfmaMin = 8;
 
 // Workspace layout (byte offsets), all 64-byte aligned.
 struct WsLayout {
@@ -26,7 +29,7 @@ struct WsLayout {
     size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the stack kernel
     size_t rbuf = 0;         // float [D] residual stream handed between layers of one stack launch
     // batches (T > 1)
-    size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0;
+    size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0, big = 0, n_big = 0;
     size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
     size_t total = 0;
 };
@@ -101,6 +104,8 @@ struct BatchArgs {
     int32_t *pos_of_pair;    // [T*K] pair index -> position (-1: invalid id)
     int32_t *act;            // [E] active experts, ascending
     int32_t *n_act;          // [1]
+    int32_t *big;            // [E] experts with at least kMfmaMin tokens, ascending
+    int32_t *n_big;          // [1]
     int *xdig;               // [T][D/chunk][DW] digit tables of x
     float *xcsum;            // [T][D/chunk]
     float *xinv;             // [T]

@@ -176,6 +176,8 @@ def moe_stream_prefetch(streamer: Streamer, layer: int, expert_ids, slot: int, w
                         done_event=None) -> None:
     ids = (ctypes.c_int32 * len(expert_ids))(*[int(e) for e in expert_ids])
     ev = None if done_event is None else (done_event if isinstance(done_event, int) else done_event.cuda_event)
+    if done_event is not None and not ev:
+        raise ValueError("done_event has no HIP event yet: record it once before handing it over")
     _check(lib().moe_stream_prefetch(ctypes.byref(streamer), layer, ctypes.cast(ids, ctypes.c_void_p),
                                      len(expert_ids), slot, 1 if with_shared else 0, _stream(copy_stream), ev))
 
@@ -185,6 +187,8 @@ def moe_stream_token(descs, streamer: Streamer, resid, x, topk_idx, topk_w, host
     """descs: a ctypes array of LayerDesc (streamed form); host_ids: pinned
     int32 tensor of K; events: five torch.cuda.Event."""
     ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
+    if any(not e.cuda_event for e in events):
+        raise ValueError("every event must have been recorded once (its HIP event is created lazily)")
     ev = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
     _check(lib().moe_stream_token(descs, len(descs), ctypes.byref(streamer), _ptr(resid), _ptr(x), _ptr(topk_idx),
                                   _ptr(topk_w), _ptr(host_ids), _ptr(workspace), ws_bytes, _stream(compute_stream),

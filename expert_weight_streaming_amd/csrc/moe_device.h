@@ -157,6 +157,24 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
     return fmaf((float)a2, 65536.f, fmaf((float)a1, 256.f, (float)a0));
 }
 
+// Block barrier for LDS traffic only: unlike __syncthreads it does not wait
+// for the wave's outstanding global loads (prefetches may stay in flight).
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Block barrier: LDS-only (LDS_SYNC) or a full __syncthreads.
+template <bool LDS_SYNC>
+__device__ __forceinline__ void bsync()
+{
+    if constexpr (LDS_SYNC) lds_barrier();
+    else __syncthreads();
+}
+
 // csum[c] = sum of the fp32 values of chunk c of x, for c < nc: four lanes
 // per chunk, each summing a quarter in order, then the four quarters.
 // Called by whole waves of the block (blockDim a multiple of 64).
@@ -189,7 +207,7 @@ __device__ __forceinline__ void chunk_sums(const float *x, int nc, float *csum)
 // (n a multiple of the chunk width): dig[c*DW + ...] as chunk_digits lays
 // out chunk c, csum[c] = sum of the chunk's fp32 values; returns 2^-k.
 // `red` is LDS scratch of 16 floats.  Ends with __syncthreads.
-template <int BITS>
+template <int BITS, bool LDS_SYNC = false>
 __device__ __forceinline__ float block_digit_table(const float *x, int n, int *dig, float *csum, float *red)
 {
     using C = Codes<BITS>;
@@ -198,7 +216,7 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
     for (int i = tid; i < n; i += nt) m = fmaxf(m, fabsf(x[i]));
     m = group_max<64>(m);
     if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
+    bsync<LDS_SYNC>();
     float amax = 0.f;
     for (int w = 0; w < (nt >> 6); ++w) amax = fmaxf(amax, red[w]);
     float mul, inv;
@@ -213,7 +231,7 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
         digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
     }
     chunk_sums<BITS>(x, n / C::CODES, csum);
-    __syncthreads();
+    bsync<LDS_SYNC>();
     return inv;
 }
 
@@ -812,7 +830,7 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
 // the selected logits, summed in rank order).  LDS scratch: cand[64],
 // wmax[NW], sk[kMaxTopK] (64-bit) and one int.  All threads of the block
 // call it; it ends with __syncthreads.
-template <int NW>
+template <int NW, bool LDS_SYNC = false>
 __device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, uint64_t *cand, uint64_t *wmax,
                                                 uint64_t *sk, int *ncand, int *sel, float *selw)
 {
@@ -836,7 +854,7 @@ __device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, u
     const uint64_t wm = wave_max_key(best);
     if (lane == 0) wmax[wave] = wm;
     if (tid == 0) *ncand = 0;
-    __syncthreads();
+    bsync<LDS_SYNC>();
     // T = the K-th largest wave maximum: lane i < NW ranks maximum i
     const uint64_t mi = lane < NW ? wmax[lane] : 0ull;
     int r = 0;
@@ -850,7 +868,7 @@ __device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, u
             const int p = atomicAdd(ncand, 1);
             if (p < 64) cand[p] = key[j];
         }
-    __syncthreads();
+    bsync<LDS_SYNC>();
     const int n = *ncand;
     if (n > 64) {
         // every wave's K largest, then the K largest of those
@@ -864,7 +882,7 @@ __device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, u
                 if (key[j] == w) key[j] = 0ull;
             if (lane == 0) sk[wave * K + k] = w;
         }
-        __syncthreads();
+        bsync<LDS_SYNC>();
     }
     if (wave == 0) {
         // one candidate per lane, ranked against the others
@@ -885,7 +903,7 @@ __device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, u
             selw[rank] = ex / z;
         }
     }
-    __syncthreads();
+    bsync<LDS_SYNC>();
 }
 
 // (v, i) pairs ordered by value, then by the lower index: true when (ov, oi)

@@ -22,10 +22,11 @@
 // and holds them in registers across barriers:
 //   - the next layer's router rows are issued between arriving at the
 //     layer's last barrier and waiting for it, the shared expert's gate/up
-//     rows likewise at the first barrier (arrival waits for the block's
-//     stores, which must not queue behind a prefetch);
-//   - the routed down rows are issued right after the top-K, next to the
-//     routed gate/up rows, and consumed after the following barrier.
+//     rows likewise at the first barrier, the routed down rows at the
+//     second (so that the routed gate/up rows before it have the memory
+//     system to themselves).
+// Arrival waits for the block's stores, which must not queue behind a
+// prefetch, so every prefetch is issued after an arrival.
 // With one unit of work per wave at the pages' shape (hidden 4096, 512
 // experts, K=4 + shared, inter 1024: 2048 waves), every phase is a single
 // round of loads.  Larger shapes loop; the first unit is the prefetched one.
@@ -253,8 +254,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         gu_load<BITS, GCPL, 1>(ga, wave > 0 && su0 < I ? sh : nullptr, D, I, su0, lane);
         grid_wait(g, bar);
 
-        // ---- phase B: top-K, then the routed gate/up rows; the down rows of
-        // every slot are requested here and used after the next barrier
+        // ---- phase B: top-K, then the routed gate/up rows
         for (int e = tid; e < E; e += NT) lg[e] = xload(A->logits + e);
         __syncthreads();
         block_topk_fast<NWB>(lg, E, K, cand, wmax, sk, ncand, sel, selw);
@@ -269,10 +269,6 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             const int k = gw / upe;
             gu_load<BITS, GCPL, 2>(gb, gw < K * upe ? blob_k(k) : nullptr, D, I, (gw - k * upe) * 2, lane);
         }
-        DnRegs<BITS, DCPL> dn[MAXS];
-#pragma unroll
-        for (int k = 0; k < MAXS; ++k)
-            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? blob_k(k) : nullptr, D, I, gw * RPU, lane);
         // the shared expert's gate/up rows (loaded at barrier 1) while the
         // routed rows are in flight
         if (S > K && wave > 0) {
@@ -287,7 +283,14 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             if (j > 0) gu_load<BITS, GCPL, 2>(gb, blob_k(k), D, I, i0, lane);
             gu_finish<BITS, GCPL, 2>(gb, dig, csum, xinv, D, I, i0, lane, A->h + (size_t)k * I);
         }
-        grid_sync(g, ++bar);
+        // barrier 2; the down rows of every slot (needed right after it)
+        // stream in while the block waits
+        grid_arrive(g, ++bar);
+        DnRegs<BITS, DCPL> dn[MAXS];
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k)
+            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? blob_k(k) : nullptr, D, I, gw * RPU, lane);
+        grid_wait(g, bar);
 
         // ---- phase C: h of every slot into LDS and its digit tables
         const int cpk = I / C::CODES;  // h chunks per slot

@@ -20,9 +20,11 @@ def test_prefetch_copies_selected_blobs():
     st = W.build_streamed(cfg, layers=3, arena_blobs=37)
     cs = st.copy_stream
     ids = [5, 0, 15][:cfg.K]
+    ev = torch.cuda.Event()
+    ev.record(cs)  # creates the HIP event
     for l, slot in ((0, 0), (2, 1), (1, 0)):
         st.slab.fill_(0xAB)
-        ev = torch.cuda.Event()
+        cs.wait_stream(torch.cuda.current_stream())  # the fill before the copies
         ews.moe_stream_prefetch(st.streamer, l, ids, slot, True, cs, ev)
         ev.synchronize()
         got = st.slab[slot].cpu()
@@ -31,6 +33,8 @@ def test_prefetch_copies_selected_blobs():
         assert torch.equal(got[(st.slab_blobs - 1) * st.bb:], st.host_shared_blob(l)), l
         # the other slot is untouched
         assert bool((st.slab[1 - slot].cpu() == 0xAB).all())
+    with pytest.raises(ValueError):
+        ews.moe_stream_prefetch(st.streamer, 0, [0], 0, False, cs, torch.cuda.Event())  # never recorded
     with pytest.raises(ews.MoeError):
         ews.moe_stream_prefetch(st.streamer, 0, [cfg.E], 0, False, cs)
     with pytest.raises(ews.MoeError):

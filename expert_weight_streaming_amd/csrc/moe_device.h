@@ -157,6 +157,76 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
     return fmaf((float)a2, 65536.f, fmaf((float)a1, 256.f, (float)a0));
 }
 
+// Digit table of one chunk built in registers, with a fixed-point step of
+// its own.  A chunk's CODES values are held as float4 by G = CODES/4
+// consecutive lanes (lane f of the chunk holds values 4f..4f+3, float4 q
+// of the vector); the word of plane p for code word k, sub s holds values
+// k*PER_WORD + s + SUBS*j, which lie in the SUBS lanes of word k, so those
+// lanes trade components through quad DPP and lane f writes word f of
+// every plane.  The chunk's largest magnitude (step inv = 2^-k with
+// max * 2^k < 2^22) and its fp32 sum come from DPP reductions over the G
+// lanes; lane 0 of the chunk writes csum[c] and cinv[c].  All 64 lanes
+// call it; lanes past the end (whole chunks) pass valid = false and write
+// nothing.
+template <int BITS>
+__device__ __forceinline__ void chunk_digits_lane(float4 v, int q, bool valid, int *dig, float *csum, float *cinv)
+{
+    using C = Codes<BITS>;
+    constexpr int G = C::CODES / 4;
+    static_assert(C::SUBS == C::PER_WORD / 4, "one sub per lane of a code word");
+    if (!valid) v = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float m = group_max<G>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float sum = group_sum<G>((v.x + v.y) + (v.z + v.w));
+    float mul, inv;
+    fixed_scale(m, mul, inv);
+    const int lane = threadIdx.x & 63;
+    float a, b, c, d;
+    if constexpr (BITS == 4) {
+        // pair (p = 0, 1): word p takes components p and p+2 of both lanes
+        const int p = lane & 1;
+        const float s0 = fdpp<0xB1>(p ? v.x : v.y, 0.f);
+        const float s1 = fdpp<0xB1>(p ? v.z : v.w, 0.f);
+        a = p ? s0 : v.x;
+        b = p ? s1 : v.z;
+        c = p ? v.y : s0;
+        d = p ? v.w : s1;
+    } else {
+        // quad (p = 0..3): word p takes component p of lanes 0..3 in order;
+        // in round r lane p reads lane (p + r) & 3, which sends component
+        // (its lane - r) & 3
+        const int p = lane & 3;
+        auto comp = [&](int i) {
+            const float lo = (i & 1) ? v.y : v.x, hi = (i & 1) ? v.w : v.z;
+            return (i & 2) ? hi : lo;
+        };
+        const float own = comp(p);
+        const float r1 = fdpp<0x39>(comp((p - 1) & 3), 0.f);  // quad_perm [1,2,3,0]
+        const float r2 = fdpp<0x4E>(comp((p - 2) & 3), 0.f);  // quad_perm [2,3,0,1]
+        const float r3 = fdpp<0x93>(comp((p - 3) & 3), 0.f);  // quad_perm [3,0,1,2]
+        auto from = [&](int j) {
+            const int r = (j - p) & 3;
+            return r == 0 ? own : r == 1 ? r1 : r == 2 ? r2 : r3;
+        };
+        a = from(0);
+        b = from(1);
+        c = from(2);
+        d = from(3);
+    }
+    int w0, w1, w2;
+    digit_words(a, b, c, d, mul, w0, w1, w2);
+    if (valid) {
+        const int ch = q / G, f = q - ch * G;
+        int *o = dig + ch * C::DW + f;
+        o[0] = w0;
+        o[C::PW] = w1;
+        o[2 * C::PW] = w2;
+        if (f == 0) {
+            csum[ch] = sum;
+            cinv[ch] = inv;
+        }
+    }
+}
+
 // Block barrier for LDS traffic only: unlike __syncthreads it does not wait
 // for the wave's outstanding global loads (prefetches may stay in flight).
 __device__ __forceinline__ void lds_barrier()
@@ -426,6 +496,56 @@ __device__ __forceinline__ void wave_gate_up(const uint8_t *blob, const int *dig
     gu_finish<BITS, CPL, R>(g, dig, csum, inv, D, I, i0, lane, h);
 }
 
+// As gu_finish against a digit table with one fixed-point step per chunk
+// (cinv[c], chunk_digits_lane), returning h of the unit's rows in every
+// lane instead of storing it.
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void gu_finish_c(const GuRegs<BITS, CPL, R> &g, const int *dig, const float *csum,
+                                            const float *cinv, int D, int lane, float (&h)[R])
+{
+    using C = Codes<BITS>;
+    const int nchunks = D * BITS / 128;
+    float acc[R][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lane + 64 * m;
+        int dg[C::DW];
+        float cs = 0.f, ci = 0.f;
+        if (c < nchunks) {
+            const int4 *src = reinterpret_cast<const int4 *>(dig + c * C::DW);
+#pragma unroll
+            for (int t = 0; t < C::DW / 4; ++t) {
+                const int4 v = src[t];
+                dg[4 * t] = v.x;
+                dg[4 * t + 1] = v.y;
+                dg[4 * t + 2] = v.z;
+                dg[4 * t + 3] = v.w;
+            }
+            cs = csum[c];
+            ci = cinv[c];
+        } else {
+#pragma unroll
+            for (int t = 0; t < C::DW; ++t) dg[t] = 0;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                const float qx = qdot<BITS>(g.q[m][r][mat], dg);
+                acc[r][mat] = fmaf(bf16_lo(g.sb[m][r][mat]) * ci, qx, acc[r][mat]);
+                acc[r][mat] = fmaf(bf16_hi(g.sb[m][r][mat]), cs, acc[r][mat]);
+            }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float gg = group_sum<64>(acc[r][0]);
+        const float u = group_sum<64>(acc[r][1]);
+        h[r] = gg / (1.f + expf(-gg)) * u;
+    }
+}
+
 // Down rows, split the same way: one wave owns 64/LPR consecutive output
 // rows o0.. of one expert's down matrix, LPR lanes per row, lane chunk
 // lc + LPR*m of its row (lc = lane % LPR).
@@ -492,6 +612,37 @@ __device__ __forceinline__ float dn_part(const DnRegs<BITS, CPL> &d, const int *
             }
             const float qh = qdot<BITS>(d.q[m], dg);
             t = fmaf(bf16_lo(d.sb[m]) * hinv, qh, t);
+            t = fmaf(bf16_hi(d.sb[m]), hcsum[c], t);
+        }
+    }
+    return t;
+}
+
+// As dn_part against a digit table of h with one fixed-point step per chunk.
+template <int BITS, int LPR, int CPL>
+__device__ __forceinline__ float dn_part_c(const DnRegs<BITS, CPL> &d, const int *hdig, const float *hcsum,
+                                           const float *hcinv, int I, int lane)
+{
+    using C = Codes<BITS>;
+    const int nchunks = I * BITS / 128;
+    const int lc = lane % LPR;
+    float t = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lc + LPR * m;
+        if (c < nchunks) {
+            int dg[C::DW];
+            const int4 *src = reinterpret_cast<const int4 *>(hdig + c * C::DW);
+#pragma unroll
+            for (int t4 = 0; t4 < C::DW / 4; ++t4) {
+                const int4 v = src[t4];
+                dg[4 * t4] = v.x;
+                dg[4 * t4 + 1] = v.y;
+                dg[4 * t4 + 2] = v.z;
+                dg[4 * t4 + 3] = v.w;
+            }
+            const float qh = qdot<BITS>(d.q[m], dg);
+            t = fmaf(bf16_lo(d.sb[m]) * hcinv[c], qh, t);
             t = fmaf(bf16_hi(d.sb[m]), hcsum[c], t);
         }
     }
@@ -662,6 +813,45 @@ __device__ __forceinline__ void grid_sync(const GridBar &g, uint32_t i)
     grid_wait(g, i);
 }
 
+// Split arrival for blocks whose waves have different jobs: only the
+// waves that store (`stores`, wave-uniform) wait for their stores; every
+// wave then meets at an LDS-only block barrier, so waves holding weight
+// loads in flight keep them in flight; thread 0 publishes the epoch.
+__device__ __forceinline__ void grid_arrive_split(const GridBar &g, uint32_t i, bool stores)
+{
+    if (stores) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    lds_barrier();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(g.slots + blockIdx.x * kSlotWords, g.base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for barrier i: wave 0 (which must hold no loads, or its polls would
+// queue behind them) polls, then an LDS-only block barrier releases the
+// block.
+__device__ __forceinline__ void grid_wait_split(const GridBar &g, uint32_t i)
+{
+    const uint32_t target = g.base + i;
+    if (threadIdx.x < 64) {
+        uint32_t spins = 0;
+        for (;;) {
+            bool ok = true;
+            for (uint32_t j = threadIdx.x; j < g.nb; j += 64)
+                ok &= (int32_t)(__hip_atomic_load(g.slots + j * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                target) >= 0;
+            if (__all(ok)) break;
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins == kSpinLimit) {
+                atomicOr(g.flags, MOE_DEVERR_BARRIER_TIMEOUT);
+                break;
+            }
+        }
+    }
+    lds_barrier();
+}
+
 // One wave: the K largest of lg[0..E) (LDS), descending, the lower index
 // first on an exact tie; idx/vals identical in every lane.  Loops run over
 // the compile-time bound so the arrays stay in registers.
@@ -810,6 +1000,154 @@ __device__ __forceinline__ void topk_merge(const uint64_t *ck, int K, int *sel, 
             sel[k] = idx[k];
             selw[k] = w[k];
         }
+    }
+}
+
+// Wave-wide maximum / minimum of an unsigned value (DPP inside rows, the
+// row halves via swizzle, then lanes 0 and 32), returned in every lane.
+__device__ __forceinline__ uint32_t udpp_max(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+    return max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+}
+__device__ __forceinline__ uint32_t udpp_min(uint32_t v)
+{
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0xB1, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x4E, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x141, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x140, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+    return min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+}
+
+// Top K of logits[0..E) (E <= 64 * KPL) by one wave, from the logits
+// themselves (agent-coherent loads, lane l holding elements l + 64 j).
+// Order: the larger logit (the float's bits mapped to an unsigned order,
+// as route_key does), then the lower index.  Each lane keeps its best
+// element (the lowest j on equal bits); a round takes the wave's largest
+// order value, the lowest index among the lanes holding it, and that lane
+// moves to its next best.  sel/selw (LDS) receive the indices in rank order
+// and the routing weights (lanes k < K write).
+template <int KPL>
+__device__ __forceinline__ void wave_topk_global(const float *logits, int E, int K, int *sel, float *selw, int lane)
+{
+    // every load in flight before the first use (clamped indices, masked
+    // afterwards)
+    uint32_t ord[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) ord[j] = __float_as_uint(xload(logits + min(lane + 64 * j, E - 1)));
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const uint32_t u = ord[j];
+        const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+        ord[j] = lane + 64 * j < E ? (o ? o : 1u) : 0u;  // 0 marks "no element"
+    }
+    uint32_t bo = 0u;
+    int bj = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+        if (ord[j] > bo) {
+            bo = ord[j];
+            bj = j;
+        }
+    int idx[kMaxTopK];
+    float vals[kMaxTopK], w[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        idx[k] = 0;
+        vals[k] = -INFINITY;
+        if (k >= K) continue;
+        const uint32_t m = udpp_max(bo);
+        const uint64_t cand = __ballot(bo == m);
+        int e;
+        if (__popcll(cand) == 1) {
+            const int wl = __builtin_ctzll(cand);
+            e = __builtin_amdgcn_readlane(bj, wl) * 64 + wl;
+        } else {
+            e = (int)udpp_min(bo == m ? (uint32_t)(bj * 64 + lane) : 0xFFFFFFFFu);
+        }
+        idx[k] = e;
+        vals[k] = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+        if (lane == (e & 63)) {
+            const int jw = e >> 6;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j)
+                if (j == jw) ord[j] = 0u;
+            bo = 0u;
+            bj = 0;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j)
+                if (ord[j] > bo) {
+                    bo = ord[j];
+                    bj = j;
+                }
+        }
+    }
+    topk_weights(vals, K, w);
+    int mi = 0;
+    float mw = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (lane == k) {
+            mi = idx[k];
+            mw = w[k];
+        }
+    if (lane < K) {
+        sel[lane] = mi;
+        selw[lane] = mw;
+    }
+}
+
+// Top K of lg[0..E) (LDS, E <= 64 * KPL) by one wave on its own, so every
+// wave of a block derives the same selection without a block barrier.
+// Lane l holds the keys of elements l + 64 j; each of the K rounds takes
+// the wave's largest key, and the one lane that held it moves to its next
+// largest.  sel[k] / selw[k] (LDS, written by lanes k < K) receive the
+// indices in rank order and the routing weights.
+template <int KPL>
+__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *sel, float *selw, int lane)
+{
+    uint64_t key[KPL];
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int e = lane + 64 * j;
+        key[j] = e < E ? route_key(lg[e], e) : 0ull;
+        best = key[j] > best ? key[j] : best;
+    }
+    int idx[kMaxTopK];
+    float vals[kMaxTopK], w[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        idx[k] = 0;
+        vals[k] = -INFINITY;
+        if (k >= K) continue;
+        const uint64_t m = wave_max_key(best);
+        idx[k] = key_index(m);
+        vals[k] = key_value(m);
+        if (best == m) {
+            uint64_t nb = 0ull;
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) nb = (key[j] < m && key[j] > nb) ? key[j] : nb;
+            best = nb;
+        }
+    }
+    topk_weights(vals, K, w);
+    int mi = 0;
+    float mw = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+        if (lane == k) {
+            mi = idx[k];
+            mw = w[k];
+        }
+    if (lane < K) {
+        sel[lane] = mi;
+        selw[lane] = mw;
     }
 }
 

@@ -172,29 +172,35 @@ struct StackArgs {
 
 // Dynamic LDS of the stack kernel (byte offsets, 16-byte aligned).
 struct StackLds {
-    uint32_t xs, dig, csum, u, hdig, hcsum, misc, total;
+    uint32_t xs, rs, dig, csum, xcinv, u, hdig, hcsum, hcinv, shst, misc, total;
 };
 constexpr int kStackMiscWords = 256;
+// LDS of the stack kernel: x (fp32) and r of the layer, x's digit table
+// with per-chunk sums and steps, a region shared by the router partials
+// (phase A), the logits (B) and the combined rows (C), h's digit tables,
+// the shared expert's staged h rows, and small scalars.
 __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bits)
 {
     const uint32_t codes = 128 / bits, dw = 4 * (8 / bits) * 3;
+    const uint32_t xc = (uint32_t)D / codes, hc = (uint32_t)S * ((uint32_t)I / codes);
     StackLds l;
     uint32_t o = 0;
-    l.xs = o;
-    o = (o + (uint32_t)D * 4 + 15u) & ~15u;
-    l.dig = o;
-    o = (o + (uint32_t)D / codes * dw * 4 + 15u) & ~15u;
-    l.csum = o;
-    o = (o + (uint32_t)D / codes * 4 + 15u) & ~15u;
-    l.u = o;
-    const uint32_t un = (uint32_t)E > (uint32_t)(S * I) ? (uint32_t)E : (uint32_t)(S * I);
-    o = (o + un * 4 + 15u) & ~15u;
-    l.hdig = o;
-    o = (o + (uint32_t)S * ((uint32_t)I / codes) * dw * 4 + 15u) & ~15u;
-    l.hcsum = o;
-    o = (o + (uint32_t)S * ((uint32_t)I / codes) * 4 + 15u) & ~15u;
-    l.misc = o;
-    o += kStackMiscWords * 4;
+    auto take = [&](uint32_t &f, uint32_t bytes) {
+        f = o;
+        o = (o + bytes + 15u) & ~15u;
+    };
+    take(l.xs, (uint32_t)D * 4);
+    take(l.rs, (uint32_t)D * 4);
+    take(l.dig, xc * dw * 4);
+    take(l.csum, xc * 4);
+    take(l.xcinv, xc * 4);
+    const uint32_t un = (uint32_t)D > 2u * (uint32_t)E + 8u ? (uint32_t)D : 2u * (uint32_t)E + 8u;
+    take(l.u, un * 4);
+    take(l.hdig, hc * dw * 4);
+    take(l.hcsum, hc * 4);
+    take(l.hcinv, hc * 4);
+    take(l.shst, ((uint32_t)I + 8u) * 4);
+    take(l.misc, kStackMiscWords * 4);
     l.total = o;
     return l;
 }

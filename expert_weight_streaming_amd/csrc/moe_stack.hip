@@ -7,35 +7,42 @@
 // one launch of one 512-thread block per CU, and a layer is three phases
 // separated by grid barriers:
 //
-//   A  x_l = RMSNorm(r_l) * gamma_{l-1} (every block, from the residual rows
-//      the previous layer published), its digit table, router rows
-//                                                            -> barrier
-//   B  top-K in every block (no broadcast round trip), the shared expert's
-//      gate/up rows beside the top-K's final merge, then the routed
-//      experts' gate/up rows                                 -> barrier
-//   C  h of every slot and its digit tables in LDS; down rows of all slots,
-//      combined in slot order, plus the residual; per-block sum of squares
-//                                                            -> barrier
+//   A  x_l = RMSNorm(r_l) * gamma_{l-1} in every block, from the residual
+//      rows the previous layer published, with its digit table; the
+//      router rows                                           -> barrier 1
+//   B  top-K in every wave (no broadcast round trip); the routed experts'
+//      gate/up rows                                          -> barrier 2
+//   C  h of every slot as digit tables; down rows of all slots, combined in
+//      slot order, plus the residual; per-block sum of squares -> barrier 3
 //
-// The weights a phase reads never depend on that phase's activations, so
-// each wave issues its weight loads as early as the data dependencies allow
-// and holds them in registers across barriers:
-//   - the next layer's router rows are issued between arriving at the
-//     layer's last barrier and waiting for it, the shared expert's gate/up
-//     rows likewise at the first barrier, the routed down rows at the
-//     second (so that the routed gate/up rows before it have the memory
-//     system to themselves).
-// Arrival waits for the block's stores, which must not queue behind a
-// prefetch, so every prefetch is issued after an arrival.
-// With one unit of work per wave at the pages' shape (hidden 4096, 512
-// experts, K=4 + shared, inter 1024: 2048 waves), every phase is a single
-// round of loads.  Larger shapes loop; the first unit is the prefetched one.
+// The waves of a block have two jobs.  A wave's loads complete in the
+// order they were issued, so a wave holding megabytes of weight loads in
+// flight cannot also make the small, latency-critical reads (the residual,
+// the logits, h) or wait for its own stores without waiting for those
+// weights first.  So:
+//   - activation waves (0..3) make every such read and every global store:
+//     the residual and x's digit table, the logits and the top-K, the
+//     routed gate/up rows (loaded right after the top-K, nothing else in
+//     flight) and h, h's digit tables, r' = r + c and the block's sum of
+//     squares, and they poll the barriers;
+//   - weight waves (4..7) only load weights and hand results over in LDS:
+//     the router rows, the shared expert's gate/up rows (computed in the
+//     shadow of barrier 1, so off the critical path), and the down rows of
+//     every slot, issued right after the top-K together with the next
+//     layer's router and shared gate/up rows, so that the memory system
+//     streams the layer's weights back to back while the block computes.
+// Arrival at a grid barrier waits only for the activation waves' stores;
+// every block barrier inside a layer is LDS-only.
+//
+// Digit tables are built in registers with one fixed-point step per
+// 16-byte code chunk (chunk_digits_lane): no block-wide maximum, no LDS
+// pass over the activations.
 //
 // Arithmetic per layer is that of moe_layer_step's definition: every sum
-// runs in a fixed order (no float atomics), every block derives the same
-// RMS factor from the same partial sums in the same order, so results are
-// deterministic and a stack launch equals the same layers launched one by
-// one, bit for bit.
+// runs in a fixed order (no float atomics), every block and every wave
+// derives the same RMS factor from the same partial sums in the same order
+// and the same top-K from the same logits, so results are deterministic and
+// a stack launch equals the same layers launched one by one, bit for bit.
 #include "moe_device.h"
 
 #ifndef MOE_STACK_BITS
@@ -49,28 +56,14 @@ using namespace dev;
 
 constexpr int NT = kStackThreads;  // threads per block
 constexpr int NWB = NT / 64;       // waves per block
-constexpr int RN = 4;              // router float4 per lane and round
-constexpr int RSL = 4;             // waves per router row
-constexpr int RPB = NWB / RSL;     // router rows per block and round
-
-// The RMS factor from this thread's share t of the per-block partial sums
-// of squares (thread q holds blocks q, q + NT, ...): every block adds the
-// same values in the same order, so every block gets the same factor.
-// Uses red[0..NWB).
-__device__ __forceinline__ float rms_inv(float t, int D, float eps, float *red)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    t = group_sum<64>(t);
-    if (lane == 0) red[wave] = t;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWB; ++w) tot += red[w];
-    __syncthreads();
-    return 1.f / sqrtf(tot / (float)D + eps);
-}
-
-constexpr int RV = 4;  // residual float4 per thread: D / 4 <= RV * NT
+constexpr int NX = 4;              // activation waves
+constexpr int NWW = NWB - NX;      // weight waves
+constexpr int NXT = NX * 64;       // activation threads
+constexpr int RN = 8;              // router float4 per lane and load round
+constexpr int RSLW = 2;            // weight waves per router row
+constexpr int RPBW = NWW / RSLW;   // router rows per block and round
+constexpr int XV = 4;              // float4 per activation lane and round
+constexpr int KPL = 8;             // top-K keys per lane: E <= 512
 
 // Values that the compiler must not keep live across the layer loop: a
 // persistent kernel's loop body would otherwise have every lane-dependent
@@ -100,11 +93,371 @@ __device__ __forceinline__ StackLayer layer_of(KArgs A, int l)
     return y;
 }
 
-template <int BITS, int GCPL, int LPR, int DCPL, int MAXS>
-__global__ void __launch_bounds__(NT) k_stack(StackArgs args)
+// The total of the NB per-block partial sums of squares, by one wave:
+// lane l adds blocks 4l..4l+3 (+256 i for larger grids) in order, then the
+// lanes; every wave of every block adds the same values in the same order,
+// so all of them derive the same RMS factor.  rms_issue starts the first
+// load (so that other loads can follow it into flight), rms_factor waits.
+__device__ __forceinline__ float4 rms_issue(const float *ss, int lane)
+{
+    return xload4(ss, 4 * lane);
+}
+__device__ __forceinline__ float rms_factor(float4 v, const float *ss, int NB, int D, float eps, int lane)
+{
+    float t = 0.f;
+    for (int i = 0; 256 * i < NB; ++i) {
+        if (i > 0) v = xload4(ss, 256 * i + 4 * lane);
+        const int q = 256 * i + 4 * lane;
+        t += q < NB ? v.x : 0.f;
+        t += q + 1 < NB ? v.y : 0.f;
+        t += q + 2 < NB ? v.z : 0.f;
+        t += q + 3 < NB ? v.w : 0.f;
+    }
+    t = group_sum<64>(t);
+    return 1.f / sqrtf(t / (float)D + eps);
+}
+
+// Per-layer LDS views.
+struct Views {
+    float *xs, *rs, *csum, *xcinv, *u, *hcsum, *hcinv, *shst, *misc;
+    int *dig, *hdig;
+};
+template <int BITS>
+__device__ __forceinline__ Views views(unsigned char *smem, int D, int E, int I, int S)
+{
+    const StackLds lo = stack_lds(D, E, I, S, BITS);
+    Views v;
+    v.xs = reinterpret_cast<float *>(smem + lo.xs);
+    v.rs = reinterpret_cast<float *>(smem + lo.rs);
+    v.dig = reinterpret_cast<int *>(smem + lo.dig);
+    v.csum = reinterpret_cast<float *>(smem + lo.csum);
+    v.xcinv = reinterpret_cast<float *>(smem + lo.xcinv);
+    v.u = reinterpret_cast<float *>(smem + lo.u);  // router partials (A), logits (B), combined rows (C)
+    v.hdig = reinterpret_cast<int *>(smem + lo.hdig);
+    v.hcsum = reinterpret_cast<float *>(smem + lo.hcsum);
+    v.hcinv = reinterpret_cast<float *>(smem + lo.hcinv);
+    v.shst = reinterpret_cast<float *>(smem + lo.shst);
+    v.misc = reinterpret_cast<float *>(smem + lo.misc);
+    return v;
+}
+
+// Slot k's blob of layer Ly under the selection sel (LDS).
+__device__ __forceinline__ const uint8_t *slot_blob(KArgs A, const StackLayer &Ly, const int *sel, int k)
+{
+    const uint64_t bb = A->blob_bytes;
+    if (Ly.slab) return Ly.slab + (uint64_t)k * bb;
+    if (k >= A->K) return Ly.shared;
+    const int e = __builtin_amdgcn_readfirstlane(sel[k]);
+    if (e < 0 || e >= A->E) {
+        atomicOr(A->flags, MOE_DEVERR_EXPERT_RANGE);
+        return nullptr;
+    }
+    return Ly.experts + (uint64_t)e * bb;
+}
+__device__ __forceinline__ const uint8_t *shared_blob(KArgs A, const StackLayer &Ly)
+{
+    if (A->n_slots <= A->K) return nullptr;
+    return Ly.slab ? Ly.slab + (uint64_t)A->K * A->blob_bytes : Ly.shared;
+}
+
+// Activation waves (0..NX-1).  Every block barrier below has a partner in
+// w_role, in the same order.
+template <int BITS, int GCPL, int RX, int LPR>
+__device__ __forceinline__ void x_role(unsigned char *smem, GridBar &g, uint32_t &bar)
+{
+    constexpr int RPU = 64 / LPR;
+    const int n_layers = kargs()->n_layers;
+    for (int l = 0; l < n_layers; ++l) {
+        KArgs A = kargs();
+        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int NB = gridDim.x, b = blockIdx.x;
+        const int D = A->D, E = A->E, K = A->K, I = A->I, S = A->n_slots;
+        const StackLayer Ly = layer_of(A, l);
+        const Views v = views<BITS>(smem, D, E, I, S);
+        int *sel = reinterpret_cast<int *>(v.misc);  // the block's selection [8]
+        float *selw = v.misc + 8;                     // and its weights [8]
+
+        // ---- phase A: x_l, r_l and x_l's digit table
+        {
+            float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (l > 0) s4 = rms_issue(A->ss, lane);
+            const float4 *gm = l > 0 ? reinterpret_cast<const float4 *>(A->layer[l - 1].gamma) : nullptr;
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 *r_src = reinterpret_cast<const float4 *>(A->resid);
+            const float4 *x_src = reinterpret_cast<const float4 *>(A->x);
+            float4 rv[XV], gv[XV];
+#define MOE_ISSUE(Q0)                                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < XV; ++j)                                                                      \
+    {                                                                                                                   \
+        const int q = (Q0) + tid + j * NXT;                                                                             \
+        const bool ok = q < D / 4;                                                                                      \
+        rv[j] = z4;                                                                                                     \
+        gv[j] = z4;                                                                                                     \
+        if (ok && l == 0) {                                                                                             \
+            rv[j] = r_src[q];                                                                                           \
+            gv[j] = x_src[q];                                                                                           \
+        } else if (ok) {                                                                                                \
+            rv[j] = xload4(A->rbuf, 4 * q);                                                                             \
+            gv[j] = gm[q];                                                                                              \
+        }                                                                                                               \
+    }
+            MOE_ISSUE(0)
+            const float inv = l > 0 ? rms_factor(s4, A->ss, NB, D, A->eps, lane) : 1.f;
+            for (int q0 = 0; q0 < D / 4; q0 += NXT * XV) {
+                if (q0 > 0) {
+                    MOE_ISSUE(q0)
+                }
+#pragma unroll
+                for (int j = 0; j < XV; ++j) {
+                    const int q = q0 + tid + j * NXT;
+                    const bool ok = q < D / 4;
+                    const float4 r = rv[j], gq = gv[j];
+                    const float4 xv = l == 0 ? gq
+                                             : make_float4(r.x * inv * gq.x, r.y * inv * gq.y, r.z * inv * gq.z,
+                                                           r.w * inv * gq.w);
+                    if (ok) {
+                        reinterpret_cast<float4 *>(v.xs)[q] = xv;
+                        reinterpret_cast<float4 *>(v.rs)[q] = r;
+                        if (A->record && b == 0) {
+                            reinterpret_cast<float4 *>(A->record + (size_t)l * 2 * D)[q] = r;
+                            reinterpret_cast<float4 *>(A->record + (size_t)l * 2 * D + D)[q] = xv;
+                        }
+                    }
+                    chunk_digits_lane<BITS>(xv, q, ok, v.dig, v.csum, v.xcinv);
+                }
+            }
+#undef MOE_ISSUE
+        }
+        lds_barrier();  // (1) x ready for the router
+        lds_barrier();  // (2) router partials ready
+        {
+            const int nr = b < E ? (E - b + NB * RPBW - 1) / (NB * RPBW) : 0;
+            for (int t = tid; t < nr * RPBW; t += NXT) {
+                const int j = t / RPBW, rr = t - j * RPBW;
+                const int e = b + NB * (RPBW * j + rr);
+                if (e < E) {
+                    float s = v.u[j * NWW + rr * RSLW];
+#pragma unroll
+                    for (int q = 1; q < RSLW; ++q) s += v.u[j * NWW + rr * RSLW + q];
+                    xstore(A->logits + e, s);
+                }
+            }
+        }
+        grid_arrive_split(g, ++bar, true);
+        grid_wait_split(g, bar);
+
+        // ---- phase B: the shared expert's h (staged by the weight waves in
+        // the barrier's shadow), logits, top-K, routed gate/up rows
+        if (wave == 0) {
+            wave_topk_global<KPL>(A->logits, E, K, sel, selw, lane);
+            if (b == 0 && lane < K) {
+                A->topk_idx[l * K + lane] = sel[lane];
+                A->topk_w[l * K + lane] = selw[lane];
+            }
+        }
+        lds_barrier();  // (4) the selection
+        // routed gate/up rows, RX rows per unit: unit wave*NB + b for every
+        // wave of the block, then further units on the activation waves
+        const int upe = (I + RX - 1) / RX;
+        for (int u = wave * NB + b, j = 0; u < K * upe; u += (j == 0 ? NWB : NX) * NB, ++j) {
+            const int k = u / upe, i0 = (u - k * upe) * RX;
+            GuRegs<BITS, GCPL, RX> gb;
+            gu_load<BITS, GCPL, RX>(gb, slot_blob(A, Ly, sel, k), D, I, i0, lane);
+            float hv[RX];
+            gu_finish_c<BITS, GCPL, RX>(gb, v.dig, v.csum, v.xcinv, D, lane, hv);
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < RX; ++r)
+                    if (i0 + r < I) xstore(A->h + (size_t)k * I + i0 + r, hv[r]);
+            }
+        }
+        grid_arrive_split(g, ++bar, true);
+        grid_wait_split(g, bar);
+
+        // ---- phase C: h of every slot as digit tables
+        {
+            const int n4 = S * I / 4;
+            for (int q0 = 0; q0 < n4; q0 += NXT * XV) {
+                float4 hv[XV];
+#pragma unroll
+                for (int j = 0; j < XV; ++j) {
+                    const int q = q0 + tid + j * NXT;
+                    hv[j] = q < n4 ? xload4(A->h, 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < XV; ++j) {
+                    const int q = q0 + tid + j * NXT;
+                    chunk_digits_lane<BITS>(hv[j], q, q < n4, v.hdig, v.hcsum, v.hcinv);
+                }
+            }
+        }
+        lds_barrier();  // (7) h tables ready for the down rows
+        lds_barrier();  // (8) combined rows ready
+        // the block's rows (units b + NB*m): r' = r + c, published with the
+        // block's sum of squares
+        if (wave == 0) {
+            const int nd = (D + RPU - 1) / RPU;
+            float ssacc = 0.f;
+            for (int t = lane;; t += 64) {
+                const int m = t / RPU, rr = t - m * RPU;
+                const int u = b + NB * m;
+                if (u >= nd) break;
+                const int o = u * RPU + rr;
+                if (o < D) {
+                    const float rn = v.rs[o] + v.u[o];
+                    xstore(A->rbuf + o, rn);
+                    ssacc = fmaf(rn, rn, ssacc);
+                }
+            }
+            ssacc = group_sum<64>(ssacc);
+            if (lane == 0) xstore(A->ss + b, ssacc);
+        }
+        grid_arrive_split(g, ++bar, true);
+        grid_wait_split(g, bar);
+    }
+}
+
+// Weight waves (NX..NWB-1): weight loads, the router and down arithmetic
+// and the shared expert's gate/up rows; results go to LDS only, so these
+// waves never wait for a store and their weight loads stay in flight
+// across barriers.
+template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
+__device__ __forceinline__ void w_role(unsigned char *smem, GridBar &g, uint32_t &bar)
 {
     using C = Codes<BITS>;
-    constexpr int RPU = 64 / LPR;  // down rows per wave unit
+    constexpr int RPU = 64 / LPR;
+
+    // one layer ahead: this wave's slice of the layer's first round of
+    // router rows (row b + NB*rs, slice sw) and its first shared gate/up row
+    RtRegs<RN> ra;
+    GuRegs<BITS, GCPL, 1> ga;
+    auto prefetch = [&](KArgs A, int l) {
+        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
+        const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) - NX;
+        const int NB = gridDim.x, b = blockIdx.x;
+        const int D = A->D, E = A->E, I = A->I;
+        const int nc4 = D / 4, Q = (nc4 + RSLW - 1) / RSLW, rs = wv / RSLW, sw = wv % RSLW;
+        const StackLayer Ly = layer_of(A, l);
+        const int e = b + NB * rs;
+        rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
+        const int su = wv * NB + b;
+        gu_load<BITS, GCPL, 1>(ga, su < I ? shared_blob(A, Ly) : nullptr, D, I, su, lane);
+    };
+    prefetch(kargs(), 0);
+
+    const int n_layers = kargs()->n_layers;
+    for (int l = 0; l < n_layers; ++l) {
+        KArgs A = kargs();
+        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wv = wave - NX;
+        const int NB = gridDim.x, b = blockIdx.x;
+        const int D = A->D, E = A->E, K = A->K, I = A->I, S = A->n_slots;
+        const StackLayer Ly = layer_of(A, l);
+        const Views v = views<BITS>(smem, D, E, I, S);
+        int *sel = reinterpret_cast<int *>(v.misc);  // the block's selection [8]
+        float *selw = v.misc + 8;                     // and its weights [8]
+        const int cpk = I / C::CODES;
+        const int nd = (D + RPU - 1) / RPU;
+
+        // ---- phase A: router rows, RSLW waves per row, RPBW rows per block
+        // and round
+        lds_barrier();  // (1)
+        {
+            const int nr = b < E ? (E - b + NB * RPBW - 1) / (NB * RPBW) : 0;
+            const int nc4 = D / 4, Q = (nc4 + RSLW - 1) / RSLW, rsr = wv / RSLW, sw = wv % RSLW;
+            for (int j = 0; j < nr; ++j) {
+                const int e = b + NB * (RPBW * j + rsr);
+                float acc = 0.f;
+                for (int c0 = 0; c0 < Q; c0 += 64 * RN) {
+                    const int c_lo = sw * Q + c0, c_hi = min(nc4, sw * Q + Q);
+                    if (j > 0 || c0 > 0) rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, c_lo, c_hi, lane);
+                    acc += rt_finish<RN>(ra, v.xs, c_lo, c_hi, lane);
+                }
+                acc = group_sum<64>(acc);
+                if (lane == 0) v.u[j * NWW + wv] = acc;
+            }
+        }
+        lds_barrier();  // (2)
+        grid_arrive_split(g, ++bar, false);
+        // in barrier 1's shadow: the shared expert's gate/up rows (units
+        // b + NB*m, m = wv + NWW*j); their loads are the last in flight, and
+        // the stores are waited for at barrier 2
+        if (const uint8_t *sh = shared_blob(A, Ly)) {
+            for (int u = wv * NB + b, j = 0; u < I; u += NB * NWW, ++j) {
+                if (j > 0) gu_load<BITS, GCPL, 1>(ga, sh, D, I, u, lane);
+                float hv[1];
+                gu_finish_c<BITS, GCPL, 1>(ga, v.dig, v.csum, v.xcinv, D, lane, hv);
+                if (lane == 0) xstore(A->h + (size_t)K * I + u, hv[0]);
+            }
+        }
+        grid_wait_split(g, bar);
+
+        // ---- phase B: one unit of routed gate/up rows (the layer's gate/up
+        // rows have the memory system to themselves)
+        lds_barrier();  // (4) the selection
+        {
+            const int upe = (I + RX - 1) / RX;
+            const int u = wave * NB + b;
+            if (u < K * upe) {
+                const int k = u / upe, i0 = (u - k * upe) * RX;
+                GuRegs<BITS, GCPL, RX> gb;
+                gu_load<BITS, GCPL, RX>(gb, slot_blob(A, Ly, sel, k), D, I, i0, lane);
+                float hv[RX];
+                gu_finish_c<BITS, GCPL, RX>(gb, v.dig, v.csum, v.xcinv, D, lane, hv);
+                if (lane == 0) {
+#pragma unroll
+                    for (int r = 0; r < RX; ++r)
+                        if (i0 + r < I) xstore(A->h + (size_t)k * I + i0 + r, hv[r]);
+                }
+            }
+        }
+        // barrier 2; in its shadow the down rows of every slot (first round)
+        grid_arrive_split(g, ++bar, true);
+        DnRegs<BITS, DCPL> dn[MAXS];
+        {
+            const int u = wv * NB + b;
+#pragma unroll
+            for (int k = 0; k < MAXS; ++k)
+                dn_load<BITS, LPR, DCPL>(dn[k], (k < S && u < nd) ? slot_blob(A, Ly, sel, k) : nullptr, D, I, u * RPU,
+                                         lane);
+        }
+        grid_wait_split(g, bar);
+
+        // ---- phase C: down rows of all slots, combined in slot order
+        lds_barrier();  // (7)
+        for (int u = wv * NB + b, j = 0; u < nd; u += NB * NWW, ++j) {
+            const int o0 = u * RPU, o = o0 + lane / LPR;
+            if (j > 0) {
+#pragma unroll
+                for (int k = 0; k < MAXS; ++k)
+                    dn_load<BITS, LPR, DCPL>(dn[k], k < S ? slot_blob(A, Ly, sel, k) : nullptr, D, I, o0, lane);
+            }
+            // slot partials weighted per lane, in slot order, then one
+            // reduction over the row's lanes
+            float c = 0.f;
+#pragma unroll
+            for (int k = 0; k < MAXS; ++k) {
+                if (k >= S) continue;
+                const float y = dn_part_c<BITS, LPR, DCPL>(dn[k], v.hdig + k * cpk * C::DW, v.hcsum + k * cpk,
+                                                           v.hcinv + k * cpk, I, lane);
+                c = fmaf(k < K ? selw[k] : 1.f, y, c);
+            }
+            c = group_sum<LPR>(c);
+            if (lane % LPR == 0 && o < D) v.u[o] = c;
+        }
+        lds_barrier();  // (8)
+        // barrier 3; in its shadow the next layer's router and shared rows
+        grid_arrive_split(g, ++bar, false);
+        if (l + 1 < n_layers) prefetch(A, l + 1);
+        grid_wait_split(g, bar);
+    }
+}
+
+template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
+__global__ void __launch_bounds__(NT) k_stack(StackArgs args)
+{
     extern __shared__ __align__(16) unsigned char smem[];
 
     // The barrier slots of a workspace belong to one grid size.
@@ -120,254 +473,16 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
     g.flags = args.flags;
     uint32_t bar = 0;
 
-    RtRegs<RN> ra;
-    GuRegs<BITS, GCPL, 1> ga;
-    // Router loads of a layer: this wave's slice of row b + NB*rs (the first
-    // round of the layer's router rows).
-    auto prefetch_router = [&](KArgs A, int l) {
-        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int NB = gridDim.x, b = blockIdx.x;
-        const int D = A->D, E = A->E;
-        const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rs = wave / RSL, sw = wave % RSL;
-        const StackLayer Ly = layer_of(A, l);
-        const int e = b + NB * rs;
-        rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
-    };
-    prefetch_router(kargs(), 0);
-
-    for (int l = 0; l < args.n_layers; ++l) {
-        KArgs A = kargs();
-        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int NB = gridDim.x, b = blockIdx.x;
-        const int gw = wave * NB + b, GW = NB * NWB;
-        const int D = A->D, E = A->E, K = A->K, I = A->I, S = A->n_slots;
-        const uint64_t bb = A->blob_bytes;
-        const StackLayer Ly = layer_of(A, l);
-
-        const StackLds lo = stack_lds(D, E, I, S, BITS);
-        float *xs = reinterpret_cast<float *>(smem + lo.xs);
-        int *dig = reinterpret_cast<int *>(smem + lo.dig);
-        float *csum = reinterpret_cast<float *>(smem + lo.csum);
-        float *lg = reinterpret_cast<float *>(smem + lo.u);  // logits in phase B ...
-        float *hs = reinterpret_cast<float *>(smem + lo.u);  // ... h in phase C
-        int *hdig = reinterpret_cast<int *>(smem + lo.hdig);
-        float *hcsum = reinterpret_cast<float *>(smem + lo.hcsum);
-        float *misc = reinterpret_cast<float *>(smem + lo.misc);
-        float *red = misc;                                              // [16]
-        float *rpart = misc + 16;                                       // [8]
-        int *ncand = reinterpret_cast<int *>(misc + 24);                // [1]
-        int *sel = reinterpret_cast<int *>(misc + 32);                  // [8]
-        float *selw = misc + 40;                                        // [8]
-        float *hmul = misc + 48;                                        // [16]
-        float *hinv = misc + 64;                                        // [16]
-        float *sspart = misc + 80;                                      // [16]
-        uint64_t *wmax = reinterpret_cast<uint64_t *>(misc + 96);       // [8]
-        uint64_t *sk = reinterpret_cast<uint64_t *>(misc + 112);        // [8]
-        uint64_t *cand = reinterpret_cast<uint64_t *>(misc + 128);      // [64]
-
-        // Slot k's blob of this layer (sel[] holds the layer's selection).
-        auto blob_k = [&](int k) -> const uint8_t * {
-            if (Ly.slab) return Ly.slab + (uint64_t)k * bb;
-            if (k >= K) return Ly.shared;
-            const int e = __builtin_amdgcn_readfirstlane(sel[k]);
-            if (e < 0 || e >= E) {
-                atomicOr(A->flags, MOE_DEVERR_EXPERT_RANGE);
-                return nullptr;
-            }
-            return Ly.experts + (uint64_t)e * bb;
-        };
-
-        // ---- phase A: the layer's input activation
-        if (l == 0) {
-            for (int d4 = tid; d4 < D / 4; d4 += NT) {
-                const float4 xv = reinterpret_cast<const float4 *>(A->x)[d4];
-                reinterpret_cast<float4 *>(xs)[d4] = xv;
-                if (A->record && b == 0) {
-                    reinterpret_cast<float4 *>(A->record)[d4] = reinterpret_cast<const float4 *>(A->resid)[d4];
-                    reinterpret_cast<float4 *>(A->record + D)[d4] = xv;
-                }
-            }
-        } else {
-            // the previous layer's residual rows and partial sums of squares
-            // in one round trip
-            float t = 0.f;
-            for (int q = tid; q < NB; q += NT) t += xload(A->ss + q);
-            float4 rv[RV];
-#pragma unroll
-            for (int j = 0; j < RV; ++j) {
-                const int d4 = tid + j * NT;
-                rv[j] = d4 < D / 4 ? xload4(A->rbuf, 4 * d4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-            const float inv = rms_inv(t, D, A->eps, red);
-            const float4 *gm = reinterpret_cast<const float4 *>(A->layer[l - 1].gamma);
-#pragma unroll
-            for (int j = 0; j < RV; ++j) {
-                const int d4 = tid + j * NT;
-                if (d4 >= D / 4) continue;
-                const float4 r = rv[j];
-                const float4 gv = gm[d4];
-                const float4 xv = make_float4(r.x * inv * gv.x, r.y * inv * gv.y, r.z * inv * gv.z, r.w * inv * gv.w);
-                reinterpret_cast<float4 *>(xs)[d4] = xv;
-                if (A->record && b == 0) {
-                    reinterpret_cast<float4 *>(A->record + (size_t)l * 2 * D)[d4] = r;
-                    reinterpret_cast<float4 *>(A->record + (size_t)l * 2 * D + D)[d4] = xv;
-                }
-            }
-        }
-        __syncthreads();
-        const float xinv = block_digit_table<BITS>(xs, D, dig, csum, red);
-
-        // router rows: RSL waves per row, RPB rows per block and round
-        {
-            const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rs = wave / RSL, sw = wave % RSL;
-            for (int j = 0; b + NB * RPB * j < E; ++j) {
-                const int e = b + NB * (RPB * j + rs);
-                float acc = 0.f;
-                for (int c0 = 0; c0 < Q; c0 += 64 * RN) {
-                    const int c_lo = sw * Q + c0, c_hi = min(nc4, sw * Q + Q);
-                    if (j > 0 || c0 > 0) rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, c_lo, c_hi, lane);
-                    acc += rt_finish<RN>(ra, xs, c_lo, c_hi, lane);
-                }
-                acc = group_sum<64>(acc);
-                if (lane == 0) rpart[wave] = acc;
-                __syncthreads();
-                if (tid < RPB) {
-                    const int ee = b + NB * (RPB * j + tid);
-                    if (ee < E) {
-                        float v = rpart[tid * RSL];
-#pragma unroll
-                        for (int q = 1; q < RSL; ++q) v += rpart[tid * RSL + q];
-                        xstore(A->logits + ee, v);
-                    }
-                }
-                __syncthreads();
-            }
-        }
-
-        // barrier 1; the shared expert's gate/up rows (needed in phase B, by
-        // waves 1..NWB-1) are requested between arrival and wait
-        grid_arrive(g, ++bar);
-        const uint8_t *sh = S > K ? (Ly.slab ? Ly.slab + (uint64_t)K * bb : Ly.shared) : nullptr;
-        const int su0 = b + NB * (wave - 1);  // first shared unit of waves >= 1
-        gu_load<BITS, GCPL, 1>(ga, wave > 0 && su0 < I ? sh : nullptr, D, I, su0, lane);
-        grid_wait(g, bar);
-
-        // ---- phase B: top-K, then the routed gate/up rows
-        for (int e = tid; e < E; e += NT) lg[e] = xload(A->logits + e);
-        __syncthreads();
-        block_topk_fast<NWB>(lg, E, K, cand, wmax, sk, ncand, sel, selw);
-        if (b == 0 && tid < K) {
-            A->topk_idx[l * K + tid] = sel[tid];
-            A->topk_w[l * K + tid] = selw[tid];
-        }
-        const int upe = (I + 1) / 2;  // routed gate/up units per expert (2 rows)
-        const int nd = (D + RPU - 1) / RPU;
-        GuRegs<BITS, GCPL, 2> gb;
-        {
-            const int k = gw / upe;
-            gu_load<BITS, GCPL, 2>(gb, gw < K * upe ? blob_k(k) : nullptr, D, I, (gw - k * upe) * 2, lane);
-        }
-        // the shared expert's gate/up rows (loaded at barrier 1) while the
-        // routed rows are in flight
-        if (S > K && wave > 0) {
-            float *hsh = A->h + (size_t)K * I;
-            for (int u = su0, j = 0; u < I; u += NB * (NWB - 1), ++j) {
-                if (j > 0) gu_load<BITS, GCPL, 1>(ga, sh, D, I, u, lane);
-                gu_finish<BITS, GCPL, 1>(ga, dig, csum, xinv, D, I, u, lane, hsh);
-            }
-        }
-        for (int u = gw, j = 0; u < K * upe; u += GW, ++j) {
-            const int k = u / upe, i0 = (u - k * upe) * 2;
-            if (j > 0) gu_load<BITS, GCPL, 2>(gb, blob_k(k), D, I, i0, lane);
-            gu_finish<BITS, GCPL, 2>(gb, dig, csum, xinv, D, I, i0, lane, A->h + (size_t)k * I);
-        }
-        // barrier 2; the down rows of every slot (needed right after it)
-        // stream in while the block waits
-        grid_arrive(g, ++bar);
-        DnRegs<BITS, DCPL> dn[MAXS];
-#pragma unroll
-        for (int k = 0; k < MAXS; ++k)
-            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? blob_k(k) : nullptr, D, I, gw * RPU, lane);
-        grid_wait(g, bar);
-
-        // ---- phase C: h of every slot into LDS and its digit tables
-        const int cpk = I / C::CODES;  // h chunks per slot
-        for (int q = tid; q < S * I / 4; q += NT) reinterpret_cast<float4 *>(hs)[q] = xload4(A->h, 4 * q);
-        __syncthreads();
-        for (int k = wave; k < S; k += NWB) {
-            float m = 0.f;
-            for (int i = lane; i < I; i += 64) m = fmaxf(m, fabsf(hs[k * I + i]));
-            m = group_max<64>(m);
-            if (lane == 0) {
-                float mul, inv;
-                fixed_scale(m, mul, inv);
-                hmul[k] = mul;
-                hinv[k] = inv;
-            }
-        }
-        __syncthreads();
-        for (int t = tid; t < S * cpk * 4 * C::SUBS; t += NT) {
-            const int kc = t / (4 * C::SUBS), r = t - kc * 4 * C::SUBS;
-            const int kw = r / C::SUBS, s = r - kw * C::SUBS;
-            const float mul = hmul[kc / cpk];
-            const float *v = hs + kc * C::CODES + kw * C::PER_WORD + s;
-            int *o = hdig + kc * C::DW + kw * C::SUBS + s;
-            digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
-        }
-        chunk_sums<BITS>(hs, S * cpk, hcsum);
-        __syncthreads();
-
-        // down rows of all slots, combined in slot order, plus the residual
-        float ssacc = 0.f;
-        for (int u = gw, j = 0; u < nd; u += GW, ++j) {
-            const int o0 = u * RPU, o = o0 + lane / LPR;
-            const bool owner = lane % LPR == 0 && o < D;
-            float r = 0.f;
-            if (owner) r = l == 0 ? A->resid[o] : xload(A->rbuf + o);
-            if (j > 0) {
-#pragma unroll
-                for (int k = 0; k < MAXS; ++k) dn_load<BITS, LPR, DCPL>(dn[k], k < S ? blob_k(k) : nullptr, D, I, o0, lane);
-            }
-            // slot partials weighted per lane, in slot order, then one
-            // reduction over the row's lanes
-            float c = 0.f;
-#pragma unroll
-            for (int k = 0; k < MAXS; ++k) {
-                if (k >= S) continue;
-                const float y = dn_part<BITS, LPR, DCPL>(dn[k], hdig + k * cpk * C::DW, hcsum + k * cpk, hinv[k], I, lane);
-                c = fmaf(k < K ? selw[k] : 1.f, y, c);
-            }
-            c = group_sum<LPR>(c);
-            if (owner) {
-                const float rn = r + c;
-                xstore(A->rbuf + o, rn);
-                ssacc = fmaf(rn, rn, ssacc);
-            }
-        }
-        ssacc = group_sum<64>(ssacc);
-        if (lane == 0) sspart[wave] = ssacc;
-        __syncthreads();
-        if (tid == 0) {
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < NWB; ++w) t += sspart[w];
-            xstore(A->ss + b, t);
-        }
-        grid_arrive(g, ++bar);
-        if (l + 1 < A->n_layers) prefetch_router(A, l + 1);
-        grid_wait(g, bar);
-    }
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < NX)
+        x_role<BITS, GCPL, RX, LPR>(smem, g, bar);
+    else
+        w_role<BITS, GCPL, RX, LPR, DCPL, MAXS>(smem, g, bar);
 
     // ---- the stack's output: residual stream and its normalisation
     {
         KArgs A = kargs();
-        const int tid = threadIdx.x, NB = gridDim.x, b = blockIdx.x, D = A->D, L = A->n_layers;
-        float *red = reinterpret_cast<float *>(smem + stack_lds(D, A->E, A->I, A->n_slots, BITS).misc);
-        float t = 0.f;
-        for (int q = tid; q < NB; q += NT) t += xload(A->ss + q);
-        const float inv = rms_inv(t, D, A->eps, red);
+        const int tid = threadIdx.x, lane = tid & 63, NB = gridDim.x, b = blockIdx.x, D = A->D, L = A->n_layers;
+        const float inv = rms_factor(rms_issue(A->ss, lane), A->ss, NB, D, A->eps, lane);
         const float4 *gm = reinterpret_cast<const float4 *>(A->layer[L - 1].gamma);
         for (int d4 = b * NT + tid; d4 < D / 4; d4 += NB * NT) {
             const float4 r = xload4(A->rbuf, 4 * d4);
@@ -390,10 +505,10 @@ struct StackPlanCache {
     int ready = 0, vgprs = 0, scratch = 0, n_cu = 0;
 };
 
-template <int GCPL, int LPR, int DCPL, int MAXS>
+template <int GCPL, int RX, int LPR, int DCPL, int MAXS>
 hipError_t stack_launch(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
 {
-    auto kern = k_stack<MOE_STACK_BITS, GCPL, LPR, DCPL, MAXS>;
+    auto kern = k_stack<MOE_STACK_BITS, GCPL, RX, LPR, DCPL, MAXS>;
     static StackPlanCache cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -424,27 +539,30 @@ hipError_t stack_launch(const StackArgs *a, int D, int E, int I, int S, hipStrea
     p->n_cu = c.n_cu;
     p->vgprs = c.vgprs;
     p->scratch = c.scratch;
-    p->grid = (c.scratch == 0 && per_cu >= 1 && lo.total <= 160u * 1024u) ? (c.n_cu < kMaxLayerBlocks ? c.n_cu : kMaxLayerBlocks) : 0;
+    p->grid = (c.scratch == 0 && per_cu >= 1 && lo.total <= 160u * 1024u && E <= 64 * KPL)
+                  ? (c.n_cu < kMaxLayerBlocks ? c.n_cu : kMaxLayerBlocks)
+                  : 0;
     if (!a) return hipSuccess;
     if (p->grid == 0) return hipErrorNotSupported;
     hipLaunchKernelGGL(kern, dim3(p->grid), dim3(NT), lo.total, s, *a);
     return hipGetLastError();
 }
 
-// Shape -> instantiation.  Gate/up: GCPL chunks per lane and row.  Down: the
-// smallest power-of-two LPR >= the row's chunks (8..64), DCPL chunks per lane.
+// Shape -> instantiation.  Gate/up: GCPL chunks per lane and row, RX rows
+// per activation-wave unit.  Down: LPR lanes per row (64/LPR rows per
+// weight-wave unit), DCPL chunks per lane.
 template <int GCPL>
 hipError_t stack_g(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
 {
+    constexpr int RX = GCPL <= 2 ? 2 : 1;
     const int nch = I * MOE_STACK_BITS / 128;
     const bool wide = S > 5;
 #define MOE_S(LPR_, DCPL_)                                                                                              \
-    return wide ? stack_launch<GCPL, LPR_, DCPL_, kMaxSlots>(a, D, E, I, S, s, p)                                       \
-                : stack_launch<GCPL, LPR_, DCPL_, 5>(a, D, E, I, S, s, p);
-    if (nch <= 8) MOE_S(8, 1)
+    return wide ? stack_launch<GCPL, RX, LPR_, DCPL_, kMaxSlots>(a, D, E, I, S, s, p)                                   \
+                : stack_launch<GCPL, RX, LPR_, DCPL_, 5>(a, D, E, I, S, s, p);
     if (nch <= 16) MOE_S(16, 1)
-    if (nch <= 32) MOE_S(32, 1)
-    if (nch <= 64) MOE_S(64, 1)
+    if (nch <= 32) MOE_S(16, 2)
+    if (nch <= 64) MOE_S(32, 2)
     MOE_S(64, 2)
 #undef MOE_S
 }

@@ -194,7 +194,7 @@ __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bi
     take(l.dig, xc * dw * 4);
     take(l.csum, xc * 4);
     take(l.xcinv, xc * 4);
-    const uint32_t un = (uint32_t)D > 2u * (uint32_t)E + 8u ? (uint32_t)D : 2u * (uint32_t)E + 8u;
+    const uint32_t un = (uint32_t)D > 4u * (uint32_t)E + 16u ? (uint32_t)D : 4u * (uint32_t)E + 16u;
     take(l.u, un * 4);
     take(l.hdig, hc * dw * 4);
     take(l.hcsum, hc * 4);

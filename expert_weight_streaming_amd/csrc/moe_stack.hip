@@ -56,13 +56,11 @@ using namespace dev;
 
 constexpr int NT = kStackThreads;  // threads per block
 constexpr int NWB = NT / 64;       // waves per block
-constexpr int NX = 4;              // activation waves
-constexpr int NWW = NWB - NX;      // weight waves
-constexpr int NXT = NX * 64;       // activation threads
-constexpr int RN = 8;              // router float4 per lane and load round
-constexpr int RSLW = 2;            // weight waves per router row
-constexpr int RPBW = NWW / RSLW;   // router rows per block and round
-constexpr int XV = 4;              // float4 per activation lane and round
+constexpr int RN = 4;              // router float4 per lane and load round
+constexpr int RSL = 4;             // waves per router row
+constexpr int RPB = NWB / RSL;     // router rows per block and round
+constexpr int XV = 2;              // x float4 per thread and round
+constexpr int HV = 3;              // h float4 per thread and round
 constexpr int KPL = 8;             // top-K keys per lane: E <= 512
 
 // Values that the compiler must not keep live across the layer loop: a
@@ -160,37 +158,74 @@ __device__ __forceinline__ const uint8_t *shared_blob(KArgs A, const StackLayer 
     return Ly.slab ? Ly.slab + (uint64_t)A->K * A->blob_bytes : Ly.shared;
 }
 
-// Activation waves (0..NX-1).  Every block barrier below has a partner in
-// w_role, in the same order.
-template <int BITS, int GCPL, int RX, int LPR>
-__device__ __forceinline__ void x_role(unsigned char *smem, GridBar &g, uint32_t &bar)
+template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
+__global__ void __launch_bounds__(NT) k_stack(StackArgs args)
 {
-    constexpr int RPU = 64 / LPR;
+    using C = Codes<BITS>;
+    constexpr int RPU = 64 / LPR;  // down rows per wave unit
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    // The barrier slots of a workspace belong to one grid size.
+    const uint32_t hdr = __hip_atomic_load(args.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (hdr != 0u && hdr != gridDim.x) {
+        if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(args.flags, MOE_DEVERR_WORKSPACE);
+        return;
+    }
+    GridBar g;
+    g.slots = args.slots;
+    g.base = __hip_atomic_load(args.slots + blockIdx.x * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g.nb = gridDim.x;
+    g.flags = args.flags;
+    uint32_t bar = 0;
+
+    // One layer ahead: this wave's slice of the layer's first round of
+    // router rows (row b + NB*rs, slice sw) and its shared gate/up row (unit
+    // wave*NB + b, if the expert has that many rows).
+    RtRegs<RN> ra;
+    GuRegs<BITS, GCPL, 1> ga;
+    auto prefetch = [&](KArgs A, int l) {
+        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int NB = gridDim.x, b = blockIdx.x;
+        const int D = A->D, E = A->E, I = A->I;
+        const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rs = wave / RSL, sw = wave % RSL;
+        const StackLayer Ly = layer_of(A, l);
+        const int e = b + NB * rs;
+        rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
+        const int su = wave * NB + b;
+        gu_load<BITS, GCPL, 1>(ga, su < I ? shared_blob(A, Ly) : nullptr, D, I, su, lane);
+    };
+    prefetch(kargs(), 0);
+
     const int n_layers = kargs()->n_layers;
     for (int l = 0; l < n_layers; ++l) {
         KArgs A = kargs();
         const int tid = opaque_v(threadIdx.x), lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int NB = gridDim.x, b = blockIdx.x;
+        const int gw = wave * NB + b, GW = NWB * NB;
         const int D = A->D, E = A->E, K = A->K, I = A->I, S = A->n_slots;
         const StackLayer Ly = layer_of(A, l);
         const Views v = views<BITS>(smem, D, E, I, S);
         int *sel = reinterpret_cast<int *>(v.misc);  // the block's selection [8]
         float *selw = v.misc + 8;                     // and its weights [8]
+        const int cpk = I / C::CODES;                 // h chunks per slot
+        const int nd = (D + RPU - 1) / RPU;           // down units
 
-        // ---- phase A: x_l, r_l and x_l's digit table
+        // ---- phase A: x_l, r_l and x_l's digit table; the router rows'
+        // loads (issued a layer ahead) land ahead of these
         {
             float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
             if (l > 0) s4 = rms_issue(A->ss, lane);
             const float4 *gm = l > 0 ? reinterpret_cast<const float4 *>(A->layer[l - 1].gamma) : nullptr;
-            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
             const float4 *r_src = reinterpret_cast<const float4 *>(A->resid);
             const float4 *x_src = reinterpret_cast<const float4 *>(A->x);
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
             float4 rv[XV], gv[XV];
 #define MOE_ISSUE(Q0)                                                                                                   \
     _Pragma("unroll") for (int j = 0; j < XV; ++j)                                                                      \
     {                                                                                                                   \
-        const int q = (Q0) + tid + j * NXT;                                                                             \
+        const int q = (Q0) + tid + j * NT;                                                                              \
         const bool ok = q < D / 4;                                                                                      \
         rv[j] = z4;                                                                                                     \
         gv[j] = z4;                                                                                                     \
@@ -204,13 +239,13 @@ __device__ __forceinline__ void x_role(unsigned char *smem, GridBar &g, uint32_t
     }
             MOE_ISSUE(0)
             const float inv = l > 0 ? rms_factor(s4, A->ss, NB, D, A->eps, lane) : 1.f;
-            for (int q0 = 0; q0 < D / 4; q0 += NXT * XV) {
+            for (int q0 = 0; q0 < D / 4; q0 += NT * XV) {
                 if (q0 > 0) {
                     MOE_ISSUE(q0)
                 }
 #pragma unroll
                 for (int j = 0; j < XV; ++j) {
-                    const int q = q0 + tid + j * NXT;
+                    const int q = q0 + tid + j * NT;
                     const bool ok = q < D / 4;
                     const float4 r = rv[j], gq = gv[j];
                     const float4 xv = l == 0 ? gq
@@ -229,146 +264,15 @@ __device__ __forceinline__ void x_role(unsigned char *smem, GridBar &g, uint32_t
             }
 #undef MOE_ISSUE
         }
-        lds_barrier();  // (1) x ready for the router
-        lds_barrier();  // (2) router partials ready
+        lds_barrier();
+
+        // router rows: RSL waves per row, RPB rows per block and round, the
+        // slices added in a fixed order
+        const int nr = b < E ? (E - b + NB * RPB - 1) / (NB * RPB) : 0;
         {
-            const int nr = b < E ? (E - b + NB * RPBW - 1) / (NB * RPBW) : 0;
-            for (int t = tid; t < nr * RPBW; t += NXT) {
-                const int j = t / RPBW, rr = t - j * RPBW;
-                const int e = b + NB * (RPBW * j + rr);
-                if (e < E) {
-                    float s = v.u[j * NWW + rr * RSLW];
-#pragma unroll
-                    for (int q = 1; q < RSLW; ++q) s += v.u[j * NWW + rr * RSLW + q];
-                    xstore(A->logits + e, s);
-                }
-            }
-        }
-        grid_arrive_split(g, ++bar, true);
-        grid_wait_split(g, bar);
-
-        // ---- phase B: the shared expert's h (staged by the weight waves in
-        // the barrier's shadow), logits, top-K, routed gate/up rows
-        if (wave == 0) {
-            wave_topk_global<KPL>(A->logits, E, K, sel, selw, lane);
-            if (b == 0 && lane < K) {
-                A->topk_idx[l * K + lane] = sel[lane];
-                A->topk_w[l * K + lane] = selw[lane];
-            }
-        }
-        lds_barrier();  // (4) the selection
-        // routed gate/up rows, RX rows per unit: unit wave*NB + b for every
-        // wave of the block, then further units on the activation waves
-        const int upe = (I + RX - 1) / RX;
-        for (int u = wave * NB + b, j = 0; u < K * upe; u += (j == 0 ? NWB : NX) * NB, ++j) {
-            const int k = u / upe, i0 = (u - k * upe) * RX;
-            GuRegs<BITS, GCPL, RX> gb;
-            gu_load<BITS, GCPL, RX>(gb, slot_blob(A, Ly, sel, k), D, I, i0, lane);
-            float hv[RX];
-            gu_finish_c<BITS, GCPL, RX>(gb, v.dig, v.csum, v.xcinv, D, lane, hv);
-            if (lane == 0) {
-#pragma unroll
-                for (int r = 0; r < RX; ++r)
-                    if (i0 + r < I) xstore(A->h + (size_t)k * I + i0 + r, hv[r]);
-            }
-        }
-        grid_arrive_split(g, ++bar, true);
-        grid_wait_split(g, bar);
-
-        // ---- phase C: h of every slot as digit tables
-        {
-            const int n4 = S * I / 4;
-            for (int q0 = 0; q0 < n4; q0 += NXT * XV) {
-                float4 hv[XV];
-#pragma unroll
-                for (int j = 0; j < XV; ++j) {
-                    const int q = q0 + tid + j * NXT;
-                    hv[j] = q < n4 ? xload4(A->h, 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int j = 0; j < XV; ++j) {
-                    const int q = q0 + tid + j * NXT;
-                    chunk_digits_lane<BITS>(hv[j], q, q < n4, v.hdig, v.hcsum, v.hcinv);
-                }
-            }
-        }
-        lds_barrier();  // (7) h tables ready for the down rows
-        lds_barrier();  // (8) combined rows ready
-        // the block's rows (units b + NB*m): r' = r + c, published with the
-        // block's sum of squares
-        if (wave == 0) {
-            const int nd = (D + RPU - 1) / RPU;
-            float ssacc = 0.f;
-            for (int t = lane;; t += 64) {
-                const int m = t / RPU, rr = t - m * RPU;
-                const int u = b + NB * m;
-                if (u >= nd) break;
-                const int o = u * RPU + rr;
-                if (o < D) {
-                    const float rn = v.rs[o] + v.u[o];
-                    xstore(A->rbuf + o, rn);
-                    ssacc = fmaf(rn, rn, ssacc);
-                }
-            }
-            ssacc = group_sum<64>(ssacc);
-            if (lane == 0) xstore(A->ss + b, ssacc);
-        }
-        grid_arrive_split(g, ++bar, true);
-        grid_wait_split(g, bar);
-    }
-}
-
-// Weight waves (NX..NWB-1): weight loads, the router and down arithmetic
-// and the shared expert's gate/up rows; results go to LDS only, so these
-// waves never wait for a store and their weight loads stay in flight
-// across barriers.
-template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
-__device__ __forceinline__ void w_role(unsigned char *smem, GridBar &g, uint32_t &bar)
-{
-    using C = Codes<BITS>;
-    constexpr int RPU = 64 / LPR;
-
-    // one layer ahead: this wave's slice of the layer's first round of
-    // router rows (row b + NB*rs, slice sw) and its first shared gate/up row
-    RtRegs<RN> ra;
-    GuRegs<BITS, GCPL, 1> ga;
-    auto prefetch = [&](KArgs A, int l) {
-        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
-        const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) - NX;
-        const int NB = gridDim.x, b = blockIdx.x;
-        const int D = A->D, E = A->E, I = A->I;
-        const int nc4 = D / 4, Q = (nc4 + RSLW - 1) / RSLW, rs = wv / RSLW, sw = wv % RSLW;
-        const StackLayer Ly = layer_of(A, l);
-        const int e = b + NB * rs;
-        rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
-        const int su = wv * NB + b;
-        gu_load<BITS, GCPL, 1>(ga, su < I ? shared_blob(A, Ly) : nullptr, D, I, su, lane);
-    };
-    prefetch(kargs(), 0);
-
-    const int n_layers = kargs()->n_layers;
-    for (int l = 0; l < n_layers; ++l) {
-        KArgs A = kargs();
-        const int tid = opaque_v(threadIdx.x), lane = tid & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wv = wave - NX;
-        const int NB = gridDim.x, b = blockIdx.x;
-        const int D = A->D, E = A->E, K = A->K, I = A->I, S = A->n_slots;
-        const StackLayer Ly = layer_of(A, l);
-        const Views v = views<BITS>(smem, D, E, I, S);
-        int *sel = reinterpret_cast<int *>(v.misc);  // the block's selection [8]
-        float *selw = v.misc + 8;                     // and its weights [8]
-        const int cpk = I / C::CODES;
-        const int nd = (D + RPU - 1) / RPU;
-
-        // ---- phase A: router rows, RSLW waves per row, RPBW rows per block
-        // and round
-        lds_barrier();  // (1)
-        {
-            const int nr = b < E ? (E - b + NB * RPBW - 1) / (NB * RPBW) : 0;
-            const int nc4 = D / 4, Q = (nc4 + RSLW - 1) / RSLW, rsr = wv / RSLW, sw = wv % RSLW;
+            const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rsr = wave / RSL, sw = wave % RSL;
             for (int j = 0; j < nr; ++j) {
-                const int e = b + NB * (RPBW * j + rsr);
+                const int e = b + NB * (RPB * j + rsr);
                 float acc = 0.f;
                 for (int c0 = 0; c0 < Q; c0 += 64 * RN) {
                     const int c_lo = sw * Q + c0, c_hi = min(nc4, sw * Q + Q);
@@ -376,16 +280,27 @@ __device__ __forceinline__ void w_role(unsigned char *smem, GridBar &g, uint32_t
                     acc += rt_finish<RN>(ra, v.xs, c_lo, c_hi, lane);
                 }
                 acc = group_sum<64>(acc);
-                if (lane == 0) v.u[j * NWW + wv] = acc;
+                if (lane == 0) v.u[j * NWB + wave] = acc;
             }
         }
-        lds_barrier();  // (2)
-        grid_arrive_split(g, ++bar, false);
-        // in barrier 1's shadow: the shared expert's gate/up rows (units
-        // b + NB*m, m = wv + NWW*j); their loads are the last in flight, and
-        // the stores are waited for at barrier 2
+        lds_barrier();
+        for (int t = tid; t < nr * RPB; t += NT) {
+            const int j = t / RPB, rr = t - j * RPB;
+            const int e = b + NB * (RPB * j + rr);
+            if (e < E) {
+                float s = v.u[j * NWB + rr * RSL];
+#pragma unroll
+                for (int q = 1; q < RSL; ++q) s += v.u[j * NWB + rr * RSL + q];
+                xstore(A->logits + e, s);
+            }
+        }
+
+        // barrier 1; in its shadow the shared expert's gate/up rows (their
+        // loads were issued a layer ahead; the stores are waited for at
+        // barrier 2)
+        grid_arrive_split(g, ++bar, true);
         if (const uint8_t *sh = shared_blob(A, Ly)) {
-            for (int u = wv * NB + b, j = 0; u < I; u += NB * NWW, ++j) {
+            for (int u = gw, j = 0; u < I; u += GW, ++j) {
                 if (j > 0) gu_load<BITS, GCPL, 1>(ga, sh, D, I, u, lane);
                 float hv[1];
                 gu_finish_c<BITS, GCPL, 1>(ga, v.dig, v.csum, v.xcinv, D, lane, hv);
@@ -394,13 +309,19 @@ __device__ __forceinline__ void w_role(unsigned char *smem, GridBar &g, uint32_t
         }
         grid_wait_split(g, bar);
 
-        // ---- phase B: one unit of routed gate/up rows (the layer's gate/up
-        // rows have the memory system to themselves)
-        lds_barrier();  // (4) the selection
+        // ---- phase B: top-K (one wave, from the logits), then the routed
+        // experts' gate/up rows, RX rows per wave unit
+        if (wave == 0) {
+            wave_topk_global<KPL>(A->logits, E, K, sel, selw, lane);
+            if (b == 0 && lane < K) {
+                A->topk_idx[l * K + lane] = sel[lane];
+                A->topk_w[l * K + lane] = selw[lane];
+            }
+        }
+        lds_barrier();
         {
             const int upe = (I + RX - 1) / RX;
-            const int u = wave * NB + b;
-            if (u < K * upe) {
+            for (int u = gw; u < K * upe; u += GW) {
                 const int k = u / upe, i0 = (u - k * upe) * RX;
                 GuRegs<BITS, GCPL, RX> gb;
                 gu_load<BITS, GCPL, RX>(gb, slot_blob(A, Ly, sel, k), D, I, i0, lane);
@@ -413,21 +334,35 @@ __device__ __forceinline__ void w_role(unsigned char *smem, GridBar &g, uint32_t
                 }
             }
         }
+
         // barrier 2; in its shadow the down rows of every slot (first round)
         grid_arrive_split(g, ++bar, true);
         DnRegs<BITS, DCPL> dn[MAXS];
-        {
-            const int u = wv * NB + b;
 #pragma unroll
-            for (int k = 0; k < MAXS; ++k)
-                dn_load<BITS, LPR, DCPL>(dn[k], (k < S && u < nd) ? slot_blob(A, Ly, sel, k) : nullptr, D, I, u * RPU,
-                                         lane);
-        }
+        for (int k = 0; k < MAXS; ++k)
+            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? slot_blob(A, Ly, sel, k) : nullptr, D, I, gw * RPU, lane);
         grid_wait_split(g, bar);
 
-        // ---- phase C: down rows of all slots, combined in slot order
-        lds_barrier();  // (7)
-        for (int u = wv * NB + b, j = 0; u < nd; u += NB * NWW, ++j) {
+        // ---- phase C: h of every slot as digit tables
+        {
+            const int n4 = S * I / 4;
+            for (int q0 = 0; q0 < n4; q0 += NT * HV) {
+                float4 hv[HV];
+#pragma unroll
+                for (int j = 0; j < HV; ++j) {
+                    const int q = q0 + tid + j * NT;
+                    hv[j] = q < n4 ? xload4(A->h, 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < HV; ++j) {
+                    const int q = q0 + tid + j * NT;
+                    chunk_digits_lane<BITS>(hv[j], q, q < n4, v.hdig, v.hcsum, v.hcinv);
+                }
+            }
+        }
+        lds_barrier();
+        // down rows of all slots, combined in slot order into LDS
+        for (int u = gw, j = 0; u < nd; u += GW, ++j) {
             const int o0 = u * RPU, o = o0 + lane / LPR;
             if (j > 0) {
 #pragma unroll
@@ -447,36 +382,31 @@ __device__ __forceinline__ void w_role(unsigned char *smem, GridBar &g, uint32_t
             c = group_sum<LPR>(c);
             if (lane % LPR == 0 && o < D) v.u[o] = c;
         }
-        lds_barrier();  // (8)
+        lds_barrier();
+        // the block's rows (units b + NB*m): r' = r + c, published with the
+        // block's sum of squares
+        if (wave == 0) {
+            float ssacc = 0.f;
+            for (int t = lane;; t += 64) {
+                const int m = t / RPU, rr = t - m * RPU;
+                const int u = b + NB * m;
+                if (u >= nd) break;
+                const int o = u * RPU + rr;
+                if (o < D) {
+                    const float rn = v.rs[o] + v.u[o];
+                    xstore(A->rbuf + o, rn);
+                    ssacc = fmaf(rn, rn, ssacc);
+                }
+            }
+            ssacc = group_sum<64>(ssacc);
+            if (lane == 0) xstore(A->ss + b, ssacc);
+        }
+
         // barrier 3; in its shadow the next layer's router and shared rows
-        grid_arrive_split(g, ++bar, false);
+        grid_arrive_split(g, ++bar, true);
         if (l + 1 < n_layers) prefetch(A, l + 1);
         grid_wait_split(g, bar);
     }
-}
-
-template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
-__global__ void __launch_bounds__(NT) k_stack(StackArgs args)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-
-    // The barrier slots of a workspace belong to one grid size.
-    const uint32_t hdr = __hip_atomic_load(args.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (hdr != 0u && hdr != gridDim.x) {
-        if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(args.flags, MOE_DEVERR_WORKSPACE);
-        return;
-    }
-    GridBar g;
-    g.slots = args.slots;
-    g.base = __hip_atomic_load(args.slots + blockIdx.x * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    g.nb = gridDim.x;
-    g.flags = args.flags;
-    uint32_t bar = 0;
-
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < NX)
-        x_role<BITS, GCPL, RX, LPR>(smem, g, bar);
-    else
-        w_role<BITS, GCPL, RX, LPR, DCPL, MAXS>(smem, g, bar);
 
     // ---- the stack's output: residual stream and its normalisation
     {
@@ -549,8 +479,8 @@ hipError_t stack_launch(const StackArgs *a, int D, int E, int I, int S, hipStrea
 }
 
 // Shape -> instantiation.  Gate/up: GCPL chunks per lane and row, RX rows
-// per activation-wave unit.  Down: LPR lanes per row (64/LPR rows per
-// weight-wave unit), DCPL chunks per lane.
+// per wave unit.  Down: the smallest power-of-two LPR >= the row's chunks
+// (8..64), DCPL chunks per lane.
 template <int GCPL>
 hipError_t stack_g(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
 {
@@ -560,9 +490,10 @@ hipError_t stack_g(const StackArgs *a, int D, int E, int I, int S, hipStream_t s
 #define MOE_S(LPR_, DCPL_)                                                                                              \
     return wide ? stack_launch<GCPL, RX, LPR_, DCPL_, kMaxSlots>(a, D, E, I, S, s, p)                                   \
                 : stack_launch<GCPL, RX, LPR_, DCPL_, 5>(a, D, E, I, S, s, p);
+    if (nch <= 8) MOE_S(8, 1)
     if (nch <= 16) MOE_S(16, 1)
-    if (nch <= 32) MOE_S(16, 2)
-    if (nch <= 64) MOE_S(32, 2)
+    if (nch <= 32) MOE_S(32, 1)
+    if (nch <= 64) MOE_S(64, 1)
     MOE_S(64, 2)
 #undef MOE_S
 }

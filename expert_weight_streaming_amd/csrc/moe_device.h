@@ -32,9 +32,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // the result in every lane of the group.  Inside a row of 16 lanes the
 // steps are DPP moves (two quad permutations, the half-row and the row
 // mirror: each pairs a lane with one of the other half of its group), 32
-// lanes swap halves through ds_swizzle, and the full wave reads lanes 0 and
-// 32 as scalars.  Every lane of a group adds the same operands, so the
-// result is bit-identical across the group.  All 64 lanes must be active.
+// lanes swap halves through ds_swizzle, and the full wave reads the four
+// row results (lanes 0, 16, 32, 48) as scalars, with no LDS round trip.
+// Every lane of a group adds the same operands, so the result is
+// bit-identical across the group.  All 64 lanes must be active.
 template <int CTRL>
 __device__ __forceinline__ float fdpp(float v, float identity)
 {
@@ -48,10 +49,12 @@ __device__ __forceinline__ float group_sum(float v)
     if constexpr (W >= 4) v += fdpp<0x4E>(v, 0.f);   // quad_perm [2,3,0,1]
     if constexpr (W >= 8) v += fdpp<0x141>(v, 0.f);  // row_half_mirror
     if constexpr (W >= 16) v += fdpp<0x140>(v, 0.f); // row_mirror
-    if constexpr (W >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16
+    if constexpr (W == 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // lane ^ 16
     if constexpr (W == 64)
-        v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+        v = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+            (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
     return v;
 }
 template <int W>
@@ -62,10 +65,12 @@ __device__ __forceinline__ float group_max(float v)
     if constexpr (W >= 4) v = fmaxf(v, fdpp<0x4E>(v, -INFINITY));
     if constexpr (W >= 8) v = fmaxf(v, fdpp<0x141>(v, -INFINITY));
     if constexpr (W >= 16) v = fmaxf(v, fdpp<0x140>(v, -INFINITY));
-    if constexpr (W >= 32) v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+    if constexpr (W == 32) v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
     if constexpr (W == 64)
-        v = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
+        v = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
     return v;
 }
 
@@ -1003,16 +1008,16 @@ __device__ __forceinline__ void topk_merge(const uint64_t *ck, int K, int *sel, 
     }
 }
 
-// Wave-wide maximum / minimum of an unsigned value (DPP inside rows, the
-// row halves via swizzle, then lanes 0 and 32), returned in every lane.
+// Wave-wide maximum / minimum of an unsigned value (DPP inside rows of 16,
+// then the four row results as scalars), returned in every lane.
 __device__ __forceinline__ uint32_t udpp_max(uint32_t v)
 {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
-    return max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 __device__ __forceinline__ uint32_t udpp_min(uint32_t v)
 {
@@ -1020,8 +1025,8 @@ __device__ __forceinline__ uint32_t udpp_min(uint32_t v)
     v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x4E, 0xF, 0xF, false));
     v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x141, 0xF, 0xF, false));
     v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x140, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
-    return min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+    return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+               min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
 // Top K of logits[0..E) (E <= 64 * KPL) by one wave, from the logits
@@ -1055,7 +1060,7 @@ __device__ __forceinline__ void wave_topk_global(const float *logits, int E, int
             bj = j;
         }
     int idx[kMaxTopK];
-    float vals[kMaxTopK], w[kMaxTopK];
+    float vals[kMaxTopK];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
         idx[k] = 0;
@@ -1087,67 +1092,24 @@ __device__ __forceinline__ void wave_topk_global(const float *logits, int E, int
                 }
         }
     }
-    topk_weights(vals, K, w);
+    // routing weights: softmax over the selected logits, lane k < K taking
+    // selection k (one exp per lane), the sum in rank order
     int mi = 0;
-    float mw = 0.f;
+    float mv = vals[0];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
         if (lane == k) {
             mi = idx[k];
-            mw = w[k];
+            mv = vals[k];
         }
-    if (lane < K) {
-        sel[lane] = mi;
-        selw[lane] = mw;
-    }
-}
-
-// Top K of lg[0..E) (LDS, E <= 64 * KPL) by one wave on its own, so every
-// wave of a block derives the same selection without a block barrier.
-// Lane l holds the keys of elements l + 64 j; each of the K rounds takes
-// the wave's largest key, and the one lane that held it moves to its next
-// largest.  sel[k] / selw[k] (LDS, written by lanes k < K) receive the
-// indices in rank order and the routing weights.
-template <int KPL>
-__device__ __forceinline__ void wave_topk_lds(const float *lg, int E, int K, int *sel, float *selw, int lane)
-{
-    uint64_t key[KPL];
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-        const int e = lane + 64 * j;
-        key[j] = e < E ? route_key(lg[e], e) : 0ull;
-        best = key[j] > best ? key[j] : best;
-    }
-    int idx[kMaxTopK];
-    float vals[kMaxTopK], w[kMaxTopK];
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-        idx[k] = 0;
-        vals[k] = -INFINITY;
-        if (k >= K) continue;
-        const uint64_t m = wave_max_key(best);
-        idx[k] = key_index(m);
-        vals[k] = key_value(m);
-        if (best == m) {
-            uint64_t nb = 0ull;
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) nb = (key[j] < m && key[j] > nb) ? key[j] : nb;
-            best = nb;
-        }
-    }
-    topk_weights(vals, K, w);
-    int mi = 0;
-    float mw = 0.f;
+    const float ex = lane < K ? expf(mv - vals[0]) : 0.f;
+    float z = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
-        if (lane == k) {
-            mi = idx[k];
-            mw = w[k];
-        }
+        if (k < K) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), k));
     if (lane < K) {
         sel[lane] = mi;
-        selw[lane] = mw;
+        selw[lane] = ex / z;
     }
 }
 

@@ -1029,6 +1029,20 @@ __device__ __forceinline__ uint32_t udpp_min(uint32_t v)
                min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
+// Wait until wave_topk_global has published index k of the selection
+// (rdy[k] == tag, LDS); bounded like the grid barrier.
+__device__ __forceinline__ void wait_selected(const int *rdy, int k, int tag, uint32_t *flags)
+{
+    uint32_t spins = 0;
+    while (__hip_atomic_load(rdy + k, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kSpinLimit) {
+            atomicOr(flags, MOE_DEVERR_BARRIER_TIMEOUT);
+            break;
+        }
+    }
+}
+
 // Top K of logits[0..E) (E <= 64 * KPL) by one wave, from the logits
 // themselves (agent-coherent loads, lane l holding elements l + 64 j).
 // Order: the larger logit (the float's bits mapped to an unsigned order,
@@ -1036,9 +1050,12 @@ __device__ __forceinline__ uint32_t udpp_min(uint32_t v)
 // element (the lowest j on equal bits); a round takes the wave's largest
 // order value, the lowest index among the lanes holding it, and that lane
 // moves to its next best.  sel/selw (LDS) receive the indices in rank order
-// and the routing weights (lanes k < K write).
+// and the routing weights (lanes k < K write).  Each index is published as
+// soon as its round ends: sel[k] is written, then rdy[k] = tag (LDS), so
+// that other waves can start on slot k before the later rounds finish.
 template <int KPL>
-__device__ __forceinline__ void wave_topk_global(const float *logits, int E, int K, int *sel, float *selw, int lane)
+__device__ __forceinline__ void wave_topk_global(const float *logits, int E, int K, int *sel, float *selw, int *rdy,
+                                                 int tag, int lane)
 {
     // every load in flight before the first use (clamped indices, masked
     // afterwards)
@@ -1077,6 +1094,10 @@ __device__ __forceinline__ void wave_topk_global(const float *logits, int E, int
         }
         idx[k] = e;
         vals[k] = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+        if (lane == 0) {
+            __hip_atomic_store(sel + k, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_store(rdy + k, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         if (lane == (e & 63)) {
             const int jw = e >> 6;
 #pragma unroll
@@ -1107,10 +1128,8 @@ __device__ __forceinline__ void wave_topk_global(const float *logits, int E, int
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
         if (k < K) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), k));
-    if (lane < K) {
-        sel[lane] = mi;
-        selw[lane] = ex / z;
-    }
+    (void)mi;
+    if (lane < K) selw[lane] = ex / z;
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)

@@ -177,6 +177,12 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
     g.nb = gridDim.x;
     g.flags = args.flags;
     uint32_t bar = 0;
+    {
+        KArgs A = kargs();
+        const Views v = views<BITS>(smem, A->D, A->E, A->I, A->n_slots);
+        if (threadIdx.x < 8) reinterpret_cast<int *>(v.misc)[16 + threadIdx.x] = 0;
+        __syncthreads();
+    }
 
     // One layer ahead: this wave's slice of the layer's first round of
     // router rows (row b + NB*rs, slice sw) and its shared gate/up row (unit
@@ -209,6 +215,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         const Views v = views<BITS>(smem, D, E, I, S);
         int *sel = reinterpret_cast<int *>(v.misc);  // the block's selection [8]
         float *selw = v.misc + 8;                     // and its weights [8]
+        int *rdy = reinterpret_cast<int *>(v.misc) + 16;  // selection k published: rdy[k] == l + 1
         const int cpk = I / C::CODES;                 // h chunks per slot
         const int nd = (D + RPU - 1) / RPU;           // down units
 
@@ -309,20 +316,21 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         }
         grid_wait_split(g, bar);
 
-        // ---- phase B: top-K (one wave, from the logits), then the routed
-        // experts' gate/up rows, RX rows per wave unit
+        // ---- phase B: top-K (one wave, from the logits), each selected
+        // index published as soon as it is known; the routed experts' gate/up
+        // rows (RX rows per wave unit) start as soon as their slot's expert is
         if (wave == 0) {
-            wave_topk_global<KPL>(A->logits, E, K, sel, selw, lane);
+            wave_topk_global<KPL>(A->logits, E, K, sel, selw, rdy, l + 1, lane);
             if (b == 0 && lane < K) {
                 A->topk_idx[l * K + lane] = sel[lane];
                 A->topk_w[l * K + lane] = selw[lane];
             }
         }
-        lds_barrier();
         {
             const int upe = (I + RX - 1) / RX;
             for (int u = gw; u < K * upe; u += GW) {
                 const int k = u / upe, i0 = (u - k * upe) * RX;
+                if (Ly.experts) wait_selected(rdy, k, l + 1, A->flags);
                 GuRegs<BITS, GCPL, RX> gb;
                 gu_load<BITS, GCPL, RX>(gb, slot_blob(A, Ly, sel, k), D, I, i0, lane);
                 float hv[RX];

@@ -99,6 +99,14 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
     off = round_up(off + (size_t)moe::kMaxLayerBlocks * moe::kSlotWords * 4, 256);
     L.rbuf = off;
     off = round_up(off + (size_t)d->hidden * 4, 256);
+    L.tlog = off;
+    off = round_up(off + (size_t)d->n_experts * 8, 256);
+    L.th = off;
+    off = round_up(off + (size_t)(d->top_k + d->n_shared) * d->inter * 8, 256);
+    L.tres = off;
+    off = round_up(off + (size_t)d->hidden * 8, 256);
+    L.tss = off;
+    off = round_up(off + (size_t)moe::kMaxLayerBlocks * 8, 256);
     if (T > 1) {
         const size_t E = d->n_experts, K = d->top_k, D = d->hidden, I = d->inter;
         const size_t P = (size_t)T * (K + d->n_shared);
@@ -239,10 +247,10 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
         a.topk_idx = idx + (size_t)l0 * K;
         a.topk_w = w + (size_t)l0 * K;
         a.record = record ? record + (size_t)l0 * 2 * D : nullptr;
-        a.logits = reinterpret_cast<float *>(ws + L.logits);
-        a.h = reinterpret_cast<float *>(ws + L.h);
-        a.rbuf = reinterpret_cast<float *>(ws + L.rbuf);
-        a.ss = reinterpret_cast<float *>(ws + L.ss);
+        a.tlog = reinterpret_cast<uint64_t *>(ws + L.tlog);
+        a.th = reinterpret_cast<uint64_t *>(ws + L.th);
+        a.tres = reinterpret_cast<uint64_t *>(ws + L.tres);
+        a.tss = reinterpret_cast<uint64_t *>(ws + L.tss);
         a.hdr = reinterpret_cast<uint32_t *>(ws + L.hdr);
         a.slots = reinterpret_cast<uint32_t *>(ws + L.slots);
         a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);

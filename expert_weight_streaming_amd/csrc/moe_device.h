@@ -345,6 +345,25 @@ __device__ __forceinline__ float4 xload4(const float *base, int i)
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 
+// Values handed between the blocks of one persistent launch travel with the
+// epoch that produced them, as one 64-bit word (value low, epoch high),
+// stored single-copy atomically at agent scope.  A reader polls the words it
+// needs until every epoch is the expected one, so no grid barrier and no wait
+// for store acknowledgements separate producer and consumer.
+__device__ __forceinline__ void tag_store(uint64_t *p, float v, uint32_t tag)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Pairs i and i+1 (16 coherent bytes): x = value i, y = epoch i, z = value
+// i+1, w = epoch i+1.  Each 8-byte half is one stored word.
+__device__ __forceinline__ uint4 tag_load2(const uint64_t *base, int i)
+{
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(base), (short)0, 0x7FFFFFFF,
+                                                                 0x00020000);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, i * 8, 0, 16 /* sc1: agent scope */);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // One wave: dot of router row `row` (D fp32) with x; x may live in LDS.
 // Returns the full sum in every lane.  Rows of up to 4096 are fetched with
 // every load in flight before the first FMA.
@@ -1043,8 +1062,9 @@ __device__ __forceinline__ void wait_selected(const int *rdy, int k, int tag, ui
     }
 }
 
-// Top K of logits[0..E) (E <= 64 * KPL) by one wave, from the logits
-// themselves (agent-coherent loads, lane l holding elements l + 64 j).
+// Top K of logits[0..E) (E <= 64 * KPL) by one wave, from the tagged logits
+// themselves (agent-coherent loads, lane l holding elements l + 64 j; the
+// wave polls until every logit carries epoch `ltag`).
 // Order: the larger logit (the float's bits mapped to an unsigned order,
 // as route_key does), then the lower index.  Each lane keeps its best
 // element (the lowest j on equal bits); a round takes the wave's largest
@@ -1054,14 +1074,27 @@ __device__ __forceinline__ void wait_selected(const int *rdy, int k, int tag, ui
 // soon as its round ends: sel[k] is written, then rdy[k] = tag (LDS), so
 // that other waves can start on slot k before the later rounds finish.
 template <int KPL>
-__device__ __forceinline__ void wave_topk_global(const float *logits, int E, int K, int *sel, float *selw, int *rdy,
-                                                 int tag, int lane)
+__device__ __forceinline__ void wave_topk_global(const uint64_t *tlog, uint32_t ltag, int E, int K, int *sel,
+                                                 float *selw, int *rdy, int tag, int lane, uint32_t *flags)
 {
     // every load in flight before the first use (clamped indices, masked
     // afterwards)
     uint32_t ord[KPL];
+    for (uint32_t spins = 0;;) {
+        bool ok = true;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) ord[j] = __float_as_uint(xload(logits + min(lane + 64 * j, E - 1)));
+        for (int j = 0; j < KPL; ++j) {
+            const uint64_t w = __hip_atomic_load(tlog + min(lane + 64 * j, E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ord[j] = (uint32_t)w;
+            ok &= (uint32_t)(w >> 32) == ltag;
+        }
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == (1u << 16)) {
+            atomicOr(flags, MOE_DEVERR_BARRIER_TIMEOUT);
+            break;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
         const uint32_t u = ord[j];

@@ -28,6 +28,11 @@ struct WsLayout {
     size_t ss = 0;           // float [kMaxLayerBlocks]
     size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the stack kernel
     size_t rbuf = 0;         // float [D] residual stream handed between layers of one stack launch
+    // the stack kernel's exchanges: (value, epoch) pairs, uint64
+    size_t tlog = 0;         // [E] logits
+    size_t th = 0;           // [slots][I] h
+    size_t tres = 0;         // [D] residual rows
+    size_t tss = 0;          // [kMaxLayerBlocks] per-block sums of squares
     // batches (T > 1)
     size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0, big = 0, n_big = 0;
     size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
@@ -158,12 +163,12 @@ struct StackArgs {
     int32_t *topk_idx;       // [n_layers][K] out
     float *topk_w;           // [n_layers][K] out
     float *record;           // [n_layers+1][2][D] (r, x) entering each layer and the output, or NULL
-    float *logits;           // workspace [E]
-    float *h;                // workspace [slots][I]
-    float *rbuf;             // workspace [D]
-    float *ss;               // workspace [grid]
+    uint64_t *tlog;          // workspace [E]: (logit, epoch)
+    uint64_t *th;            // workspace [slots][I]: (h, epoch)
+    uint64_t *tres;          // workspace [D]: (residual, epoch)
+    uint64_t *tss;           // workspace [kMaxLayerBlocks]: (partial sum of squares, epoch)
     uint32_t *hdr;           // workspace: grid of the last persistent launch (0: none yet)
-    uint32_t *slots;         // workspace: per-block barrier epochs
+    uint32_t *slots;         // workspace: per-block epoch reached by the last launch
     uint32_t *flags;
     uint64_t blob_bytes;
     int32_t n_layers, D, E, K, I, n_slots;

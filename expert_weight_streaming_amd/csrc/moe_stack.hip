@@ -62,6 +62,7 @@ constexpr int RPB = NWB / RSL;     // router rows per block and round
 constexpr int XV = 2;              // x float4 per thread and round
 constexpr int HV = 3;              // h float4 per thread and round
 constexpr int KPL = 8;             // top-K keys per lane: E <= 512
+constexpr uint32_t kTagSpins = 1u << 16;  // polls of an exchange before it is given up (error flag)
 
 // Values that the compiler must not keep live across the layer loop: a
 // persistent kernel's loop body would otherwise have every lane-dependent
@@ -158,6 +159,52 @@ __device__ __forceinline__ const uint8_t *shared_blob(KArgs A, const StackLayer 
     return Ly.slab ? Ly.slab + (uint64_t)A->K * A->blob_bytes : Ly.shared;
 }
 
+// Residual rows and per-block sums of squares of the previous layer, from
+// their tagged words: polls until every word this thread reads carries
+// epoch `tag`.  rv[j] receives float4 q0 + tid + j*NT of the residual; the
+// return value is this lane's share of the NB partial sums (blocks
+// 4*lane + 256*i .. +3, added in that order).  Every wave polls and adds the
+// same way.
+template <int NV>
+__device__ __forceinline__ float poll_residual(KArgs A, int q0, int D, int NB, uint32_t tag, bool with_ss, float4 (&rv)[NV])
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    float t = 0.f;
+    for (uint32_t spins = 0;;) {
+        bool ok = true;
+        t = 0.f;
+        if (with_ss) {
+            for (int i = 0; 256 * i < NB; ++i) {
+                const int p = 256 * i + 4 * lane;
+                const uint4 a = tag_load2(A->tss, p), c = tag_load2(A->tss, p + 2);
+                ok &= (p >= NB || a.y == tag) && (p + 1 >= NB || a.w == tag) && (p + 2 >= NB || c.y == tag) &&
+                      (p + 3 >= NB || c.w == tag);
+                t += p < NB ? __uint_as_float(a.x) : 0.f;
+                t += p + 1 < NB ? __uint_as_float(a.z) : 0.f;
+                t += p + 2 < NB ? __uint_as_float(c.x) : 0.f;
+                t += p + 3 < NB ? __uint_as_float(c.z) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int q = q0 + tid + j * NT;
+            rv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (q < D / 4) {
+                const uint4 a = tag_load2(A->tres, 4 * q), c = tag_load2(A->tres, 4 * q + 2);
+                ok &= a.y == tag && a.w == tag && c.y == tag && c.w == tag;
+                rv[j] = make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(c.x), __uint_as_float(c.z));
+            }
+        }
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kTagSpins) {
+            atomicOr(A->flags, MOE_DEVERR_BARRIER_TIMEOUT);
+            break;
+        }
+    }
+    return t;
+}
+
 template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
 __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
 {
@@ -165,18 +212,16 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
     constexpr int RPU = 64 / LPR;  // down rows per wave unit
     extern __shared__ __align__(16) unsigned char smem[];
 
-    // The barrier slots of a workspace belong to one grid size.
+    // The epochs of a workspace belong to one grid size.
     const uint32_t hdr = __hip_atomic_load(args.hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (hdr != 0u && hdr != gridDim.x) {
         if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(args.flags, MOE_DEVERR_WORKSPACE);
         return;
     }
-    GridBar g;
-    g.slots = args.slots;
-    g.base = __hip_atomic_load(args.slots + blockIdx.x * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    g.nb = gridDim.x;
-    g.flags = args.flags;
-    uint32_t bar = 0;
+    // Epochs: the exchanges of layer l carry base + 3l + 1 (logits), + 2 (h)
+    // and + 3 (residual rows and sums of squares); every block starts from
+    // the epoch the previous launch on this workspace ended with.
+    const uint32_t base = __hip_atomic_load(args.slots + blockIdx.x * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
         KArgs A = kargs();
         const Views v = views<BITS>(smem, A->D, A->E, A->I, A->n_slots);
@@ -185,8 +230,9 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
     }
 
     // One layer ahead: this wave's slice of the layer's first round of
-    // router rows (row b + NB*rs, slice sw) and its shared gate/up row (unit
-    // wave*NB + b, if the expert has that many rows).
+    // router rows (row b + NB*rs, slice sw) and, for waves 1.., its shared
+    // gate/up row (unit (wave-1)*NB + b, if the expert has that many rows;
+    // wave 0 takes the top-K instead).
     RtRegs<RN> ra;
     GuRegs<BITS, GCPL, 1> ga;
     auto prefetch = [&](KArgs A, int l) {
@@ -198,8 +244,8 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         const StackLayer Ly = layer_of(A, l);
         const int e = b + NB * rs;
         rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
-        const int su = wave * NB + b;
-        gu_load<BITS, GCPL, 1>(ga, su < I ? shared_blob(A, Ly) : nullptr, D, I, su, lane);
+        const int su = (wave - 1) * NB + b;
+        gu_load<BITS, GCPL, 1>(ga, wave > 0 && su < I ? shared_blob(A, Ly) : nullptr, D, I, su, lane);
     };
     prefetch(kargs(), 0);
 
@@ -218,37 +264,30 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         int *rdy = reinterpret_cast<int *>(v.misc) + 16;  // selection k published: rdy[k] == l + 1
         const int cpk = I / C::CODES;                 // h chunks per slot
         const int nd = (D + RPU - 1) / RPU;           // down units
+        const uint32_t t_log = base + 3u * l + 1u, t_h = t_log + 1u, t_res = t_log + 2u;
 
-        // ---- phase A: x_l, r_l and x_l's digit table; the router rows'
-        // loads (issued a layer ahead) land ahead of these
+        // ---- phase A: x_l, r_l and x_l's digit table
         {
-            float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (l > 0) s4 = rms_issue(A->ss, lane);
             const float4 *gm = l > 0 ? reinterpret_cast<const float4 *>(A->layer[l - 1].gamma) : nullptr;
             const float4 *r_src = reinterpret_cast<const float4 *>(A->resid);
             const float4 *x_src = reinterpret_cast<const float4 *>(A->x);
-            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            float4 rv[XV], gv[XV];
-#define MOE_ISSUE(Q0)                                                                                                   \
-    _Pragma("unroll") for (int j = 0; j < XV; ++j)                                                                      \
-    {                                                                                                                   \
-        const int q = (Q0) + tid + j * NT;                                                                              \
-        const bool ok = q < D / 4;                                                                                      \
-        rv[j] = z4;                                                                                                     \
-        gv[j] = z4;                                                                                                     \
-        if (ok && l == 0) {                                                                                             \
-            rv[j] = r_src[q];                                                                                           \
-            gv[j] = x_src[q];                                                                                           \
-        } else if (ok) {                                                                                                \
-            rv[j] = xload4(A->rbuf, 4 * q);                                                                             \
-            gv[j] = gm[q];                                                                                              \
-        }                                                                                                               \
-    }
-            MOE_ISSUE(0)
-            const float inv = l > 0 ? rms_factor(s4, A->ss, NB, D, A->eps, lane) : 1.f;
+            float inv = 1.f;
             for (int q0 = 0; q0 < D / 4; q0 += NT * XV) {
-                if (q0 > 0) {
-                    MOE_ISSUE(q0)
+                float4 rv[XV], gv[XV];
+#pragma unroll
+                for (int j = 0; j < XV; ++j) {
+                    const int q = q0 + tid + j * NT;
+                    gv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    rv[j] = gv[j];
+                    if (q < D / 4) {
+                        gv[j] = l == 0 ? x_src[q] : gm[q];
+                        if (l == 0) rv[j] = r_src[q];
+                    }
+                }
+                if (l > 0) {
+                    // the residual rows and sums of squares of layer l-1
+                    const float t = poll_residual<XV>(A, q0, D, NB, t_res - 3u, q0 == 0, rv);
+                    if (q0 == 0) inv = 1.f / sqrtf(group_sum<64>(t) / (float)D + A->eps);
                 }
 #pragma unroll
                 for (int j = 0; j < XV; ++j) {
@@ -269,12 +308,11 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                     chunk_digits_lane<BITS>(xv, q, ok, v.dig, v.csum, v.xcinv);
                 }
             }
-#undef MOE_ISSUE
         }
         lds_barrier();
 
         // router rows: RSL waves per row, RPB rows per block and round, the
-        // slices added in a fixed order
+        // slices added in a fixed order; the logits go out tagged
         const int nr = b < E ? (E - b + NB * RPB - 1) / (NB * RPB) : 0;
         {
             const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rsr = wave / RSL, sw = wave % RSL;
@@ -298,32 +336,27 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 float s = v.u[j * NWB + rr * RSL];
 #pragma unroll
                 for (int q = 1; q < RSL; ++q) s += v.u[j * NWB + rr * RSL + q];
-                xstore(A->logits + e, s);
+                tag_store(A->tlog + e, s, t_log);
             }
         }
 
-        // barrier 1; in its shadow the shared expert's gate/up rows (their
-        // loads were issued a layer ahead; the stores are waited for at
-        // barrier 2)
-        grid_arrive_split(g, ++bar, true);
-        if (const uint8_t *sh = shared_blob(A, Ly)) {
-            for (int u = gw, j = 0; u < I; u += GW, ++j) {
-                if (j > 0) gu_load<BITS, GCPL, 1>(ga, sh, D, I, u, lane);
-                float hv[1];
-                gu_finish_c<BITS, GCPL, 1>(ga, v.dig, v.csum, v.xcinv, D, lane, hv);
-                if (lane == 0) xstore(A->h + (size_t)K * I + u, hv[0]);
-            }
-        }
-        grid_wait_split(g, bar);
-
-        // ---- phase B: top-K (one wave, from the logits), each selected
-        // index published as soon as it is known; the routed experts' gate/up
-        // rows (RX rows per wave unit) start as soon as their slot's expert is
+        // ---- phase B: wave 0 polls the logits and takes the top-K, each
+        // selected index published as soon as it is known; waves 1.. run the
+        // shared expert's gate/up rows (loaded a layer ahead) meanwhile, then
+        // every wave its unit of routed gate/up rows (RX rows) as soon as its
+        // slot's expert is known
         if (wave == 0) {
-            wave_topk_global<KPL>(A->logits, E, K, sel, selw, rdy, l + 1, lane);
+            wave_topk_global<KPL>(A->tlog, t_log, E, K, sel, selw, rdy, l + 1, lane, A->flags);
             if (b == 0 && lane < K) {
                 A->topk_idx[l * K + lane] = sel[lane];
                 A->topk_w[l * K + lane] = selw[lane];
+            }
+        } else if (const uint8_t *sh = shared_blob(A, Ly)) {
+            for (int u = (wave - 1) * NB + b, j = 0; u < I; u += (NWB - 1) * NB, ++j) {
+                if (j > 0) gu_load<BITS, GCPL, 1>(ga, sh, D, I, u, lane);
+                float hv[1];
+                gu_finish_c<BITS, GCPL, 1>(ga, v.dig, v.csum, v.xcinv, D, lane, hv);
+                if (lane == 0) tag_store(A->th + (size_t)K * I + u, hv[0], t_h);
             }
         }
         {
@@ -338,29 +371,46 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 if (lane == 0) {
 #pragma unroll
                     for (int r = 0; r < RX; ++r)
-                        if (i0 + r < I) xstore(A->h + (size_t)k * I + i0 + r, hv[r]);
+                        if (i0 + r < I) tag_store(A->th + (size_t)k * I + i0 + r, hv[r], t_h);
                 }
             }
         }
-
-        // barrier 2; in its shadow the down rows of every slot (first round)
-        grid_arrive_split(g, ++bar, true);
+        // the down rows of every slot (first round): they stream while the
+        // other blocks finish their gate/up rows
         DnRegs<BITS, DCPL> dn[MAXS];
+        if (Ly.experts) wait_selected(rdy, K - 1, l + 1, A->flags);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k)
             dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? slot_blob(A, Ly, sel, k) : nullptr, D, I, gw * RPU, lane);
-        grid_wait_split(g, bar);
 
-        // ---- phase C: h of every slot as digit tables
+        // ---- phase C: h of every slot (polled until all of it carries this
+        // layer's epoch) as digit tables; then the next layer's router and
+        // shared rows are requested
         {
             const int n4 = S * I / 4;
             for (int q0 = 0; q0 < n4; q0 += NT * HV) {
                 float4 hv[HV];
+                for (uint32_t spins = 0;;) {
+                    bool ok = true;
 #pragma unroll
-                for (int j = 0; j < HV; ++j) {
-                    const int q = q0 + tid + j * NT;
-                    hv[j] = q < n4 ? xload4(A->h, 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int j = 0; j < HV; ++j) {
+                        const int q = q0 + tid + j * NT;
+                        hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (q < n4) {
+                            const uint4 a = tag_load2(A->th, 4 * q), c = tag_load2(A->th, 4 * q + 2);
+                            ok &= a.y == t_h && a.w == t_h && c.y == t_h && c.w == t_h;
+                            hv[j] = make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(c.x),
+                                                __uint_as_float(c.z));
+                        }
+                    }
+                    if (__all(ok)) break;
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins == kTagSpins) {
+                        atomicOr(A->flags, MOE_DEVERR_BARRIER_TIMEOUT);
+                        break;
+                    }
                 }
+                if (q0 + NT * HV >= n4 && l + 1 < n_layers) prefetch(A, l + 1);
 #pragma unroll
                 for (int j = 0; j < HV; ++j) {
                     const int q = q0 + tid + j * NT;
@@ -391,8 +441,8 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             if (lane % LPR == 0 && o < D) v.u[o] = c;
         }
         lds_barrier();
-        // the block's rows (units b + NB*m): r' = r + c, published with the
-        // block's sum of squares
+        // the block's rows (units b + NB*m): r' = r + c, published tagged with
+        // the block's sum of squares
         if (wave == 0) {
             float ssacc = 0.f;
             for (int t = lane;; t += 64) {
@@ -402,28 +452,38 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 const int o = u * RPU + rr;
                 if (o < D) {
                     const float rn = v.rs[o] + v.u[o];
-                    xstore(A->rbuf + o, rn);
+                    tag_store(A->tres + o, rn, t_res);
                     ssacc = fmaf(rn, rn, ssacc);
                 }
             }
             ssacc = group_sum<64>(ssacc);
-            if (lane == 0) xstore(A->ss + b, ssacc);
+            if (lane == 0) tag_store(A->tss + b, ssacc, t_res);
         }
-
-        // barrier 3; in its shadow the next layer's router and shared rows
-        grid_arrive_split(g, ++bar, true);
-        if (l + 1 < n_layers) prefetch(A, l + 1);
-        grid_wait_split(g, bar);
+        // the block's LDS is rewritten by the next layer
+        lds_barrier();
     }
 
     // ---- the stack's output: residual stream and its normalisation
     {
         KArgs A = kargs();
         const int tid = threadIdx.x, lane = tid & 63, NB = gridDim.x, b = blockIdx.x, D = A->D, L = A->n_layers;
-        const float inv = rms_factor(rms_issue(A->ss, lane), A->ss, NB, D, A->eps, lane);
+        const uint32_t t_res = base + 3u * L;
+        float4 rv[1];
+        const float t = poll_residual<1>(A, 0, 0, NB, t_res, true, rv);
+        const float inv = 1.f / sqrtf(group_sum<64>(t) / (float)D + A->eps);
         const float4 *gm = reinterpret_cast<const float4 *>(A->layer[L - 1].gamma);
         for (int d4 = b * NT + tid; d4 < D / 4; d4 += NB * NT) {
-            const float4 r = xload4(A->rbuf, 4 * d4);
+            float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (uint32_t spins = 0;;) {
+                const uint4 a = tag_load2(A->tres, 4 * d4), c = tag_load2(A->tres, 4 * d4 + 2);
+                r = make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(c.x), __uint_as_float(c.z));
+                if (a.y == t_res && a.w == t_res && c.y == t_res && c.w == t_res) break;
+                __builtin_amdgcn_s_sleep(1);
+                if (++spins == kTagSpins) {
+                    atomicOr(A->flags, MOE_DEVERR_BARRIER_TIMEOUT);
+                    break;
+                }
+            }
             const float4 gv = gm[d4];
             const float4 xv = make_float4(r.x * inv * gv.x, r.y * inv * gv.y, r.z * inv * gv.z, r.w * inv * gv.w);
             reinterpret_cast<float4 *>(A->resid)[d4] = r;
@@ -433,6 +493,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 reinterpret_cast<float4 *>(A->record + (size_t)L * 2 * D + D)[d4] = xv;
             }
         }
+        if (tid == 0) __hip_atomic_store(A->slots + b * kSlotWords, t_res, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tid == 0 && b == 0) __hip_atomic_store(A->hdr, (uint32_t)NB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }

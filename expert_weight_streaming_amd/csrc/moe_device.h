@@ -610,39 +610,8 @@ __device__ __forceinline__ void dn_load(DnRegs<BITS, CPL> &d, const uint8_t *blo
 }
 
 // A lane's share of the row sums of a dn_load unit against a digit table
-// of h (LDS: hdig/hcsum of this expert's slot, fixed-point step hinv); the
-// row's sum is the sum over its LPR lanes.
-template <int BITS, int LPR, int CPL>
-__device__ __forceinline__ float dn_part(const DnRegs<BITS, CPL> &d, const int *hdig, const float *hcsum, float hinv,
-                                         int I, int lane)
-{
-    using C = Codes<BITS>;
-    const int nchunks = I * BITS / 128;
-    const int lc = lane % LPR;
-    float t = 0.f;
-#pragma unroll
-    for (int m = 0; m < CPL; ++m) {
-        const int c = lc + LPR * m;
-        if (c < nchunks) {
-            int dg[C::DW];
-            const int4 *src = reinterpret_cast<const int4 *>(hdig + c * C::DW);
-#pragma unroll
-            for (int t4 = 0; t4 < C::DW / 4; ++t4) {
-                const int4 v = src[t4];
-                dg[4 * t4] = v.x;
-                dg[4 * t4 + 1] = v.y;
-                dg[4 * t4 + 2] = v.z;
-                dg[4 * t4 + 3] = v.w;
-            }
-            const float qh = qdot<BITS>(d.q[m], dg);
-            t = fmaf(bf16_lo(d.sb[m]) * hinv, qh, t);
-            t = fmaf(bf16_hi(d.sb[m]), hcsum[c], t);
-        }
-    }
-    return t;
-}
-
-// As dn_part against a digit table of h with one fixed-point step per chunk.
+// of h (LDS: hdig/hcsum/hcinv of this expert's slot, one fixed-point step
+// per chunk); the row's sum is the sum over its LPR lanes.
 template <int BITS, int LPR, int CPL>
 __device__ __forceinline__ float dn_part_c(const DnRegs<BITS, CPL> &d, const int *hdig, const float *hcsum,
                                            const float *hcinv, int I, int lane)
@@ -784,98 +753,6 @@ __device__ __forceinline__ void wave_down(const uint8_t *blob, const float *h, i
 
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-// Grid barrier of one launch.  Every block owns a 64-byte slot holding an
-// epoch count; at barrier i a block publishes base + i in its slot and
-// waits until every slot of the grid has reached it.  The epochs carry over
-// from launch to launch (each launch adds 3), so no counter is ever reset
-// and no atomic read-modify-write is contended.  Before publishing, the
-// block waits for its own stores to complete; all data crossing a barrier
-// is stored and loaded agent-coherently (xstore / xload / xload4).
-struct GridBar {
-    uint32_t *slots;
-    uint32_t base;
-    uint32_t nb;
-    uint32_t *flags;
-};
-
-// Arrival at barrier i: the block's stores complete, then one store of the
-// epoch.  Loads issued after the arrival (a prefetch) do not delay it.
-__device__ __forceinline__ void grid_arrive(const GridBar &g, uint32_t i)
-{
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0)
-        __hip_atomic_store(g.slots + blockIdx.x * kSlotWords, g.base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until every block has arrived at barrier i (epochs newer than the
-// target count too: a fast block may already have passed it).
-__device__ __forceinline__ void grid_wait(const GridBar &g, uint32_t i)
-{
-    const uint32_t target = g.base + i;
-    if (threadIdx.x < 64) {
-        uint32_t spins = 0;
-        for (;;) {
-            bool ok = true;
-            for (uint32_t j = threadIdx.x; j < g.nb; j += 64)
-                ok &= (int32_t)(__hip_atomic_load(g.slots + j * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                                target) >= 0;
-            if (__all(ok)) break;
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins == kSpinLimit) {
-                atomicOr(g.flags, MOE_DEVERR_BARRIER_TIMEOUT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ void grid_sync(const GridBar &g, uint32_t i)
-{
-    grid_arrive(g, i);
-    grid_wait(g, i);
-}
-
-// Split arrival for blocks whose waves have different jobs: only the
-// waves that store (`stores`, wave-uniform) wait for their stores; every
-// wave then meets at an LDS-only block barrier, so waves holding weight
-// loads in flight keep them in flight; thread 0 publishes the epoch.
-__device__ __forceinline__ void grid_arrive_split(const GridBar &g, uint32_t i, bool stores)
-{
-    if (stores) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    lds_barrier();
-    if (threadIdx.x == 0)
-        __hip_atomic_store(g.slots + blockIdx.x * kSlotWords, g.base + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait for barrier i: wave 0 (which must hold no loads, or its polls would
-// queue behind them) polls, then an LDS-only block barrier releases the
-// block.
-__device__ __forceinline__ void grid_wait_split(const GridBar &g, uint32_t i)
-{
-    const uint32_t target = g.base + i;
-    if (threadIdx.x < 64) {
-        uint32_t spins = 0;
-        for (;;) {
-            bool ok = true;
-            for (uint32_t j = threadIdx.x; j < g.nb; j += 64)
-                ok &= (int32_t)(__hip_atomic_load(g.slots + j * kSlotWords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                                target) >= 0;
-            if (__all(ok)) break;
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins == kSpinLimit) {
-                atomicOr(g.flags, MOE_DEVERR_BARRIER_TIMEOUT);
-                break;
-            }
-        }
-    }
-    lds_barrier();
-}
-
 // One wave: the K largest of lg[0..E) (LDS), descending, the lower index
 // first on an exact tie; idx/vals identical in every lane.  Loops run over
 // the compile-time bound so the arrays stay in registers.
@@ -970,61 +847,6 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
     return ((uint64_t)hi << 32) | lo;
-}
-
-// Stage one of the block top-K: every wave takes the K largest keys of its
-// elements (e = 64 w + lane + 64 NW j, j < 8) and parks them in ck[w*K + k]
-// (LDS).  E <= 512 NW.  Whole waves only.
-template <int NW>
-__device__ __forceinline__ void topk_local(const float *lg, int E, int K, uint64_t *ck)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t key[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int e = 64 * wave + lane + 64 * NW * j;
-        key[j] = e < E ? route_key(lg[e], e) : 0ull;
-    }
-    for (int k = 0; k < K; ++k) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) best = key[j] > best ? key[j] : best;
-        const uint64_t w = wave_max_key(best);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (key[j] == w) key[j] = 0ull;
-        if (lane == 0) ck[wave * K + k] = w;
-    }
-}
-
-// Stage two, one wave: the K largest of the NW*K parked keys, in order;
-// sel/selw (LDS) receive the indices and the routing weights.
-template <int NW>
-__device__ __forceinline__ void topk_merge(const uint64_t *ck, int K, int *sel, float *selw)
-{
-    const int lane = threadIdx.x & 63;
-    uint64_t key = lane < NW * K ? ck[lane] : 0ull;
-    int idx[kMaxTopK];
-    float vals[kMaxTopK], w[kMaxTopK];
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-        idx[k] = -1;
-        vals[k] = -INFINITY;
-        if (k >= K) continue;
-        const uint64_t m = wave_max_key(key);
-        idx[k] = key_index(m);
-        vals[k] = key_value(m);
-        if (key == m) key = 0ull;
-    }
-    topk_weights(vals, K, w);
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            if (k >= K) continue;
-            sel[k] = idx[k];
-            selw[k] = w[k];
-        }
-    }
 }
 
 // Wave-wide maximum / minimum of an unsigned value (DPP inside rows of 16,
@@ -1164,215 +986,6 @@ __device__ __forceinline__ void wave_topk_global(const uint64_t *tlog, uint32_t 
     (void)mi;
     if (lane < K) selw[lane] = ex / z;
 }
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
-{
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Top K of lg[0..E) (LDS) for a block of NW waves, K <= NW (E <= 512 NW).
-// The K-th largest of the NW wave maxima is a lower bound T of the K-th
-// largest element, so every selected element has a key >= T.  Those
-// candidates (usually a handful) are compacted into LDS and ranked against
-// each other in one pass.  Degenerate inputs with more than 64 candidates
-// (many equal logits) take K rounds of wave maxima instead.  sel/selw (LDS)
-// receive the indices in rank order and the routing weights (softmax over
-// the selected logits, summed in rank order).  LDS scratch: cand[64],
-// wmax[NW], sk[kMaxTopK] (64-bit) and one int.  All threads of the block
-// call it; it ends with __syncthreads.
-template <int NW, bool LDS_SYNC = false>
-__device__ __forceinline__ void block_topk_fast(const float *lg, int E, int K, uint64_t *cand, uint64_t *wmax,
-                                                uint64_t *sk, int *ncand, int *sel, float *selw)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint64_t key[8];
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) key[j] = 0ull;
-    if (E <= 64 * NW) {
-        const int e = 64 * wave + lane;
-        key[0] = e < E ? route_key(lg[e], e) : 0ull;
-        best = key[0];
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int e = 64 * wave + lane + 64 * NW * j;
-            key[j] = e < E ? route_key(lg[e], e) : 0ull;
-            best = key[j] > best ? key[j] : best;
-        }
-    }
-    const uint64_t wm = wave_max_key(best);
-    if (lane == 0) wmax[wave] = wm;
-    if (tid == 0) *ncand = 0;
-    bsync<LDS_SYNC>();
-    // T = the K-th largest wave maximum: lane i < NW ranks maximum i
-    const uint64_t mi = lane < NW ? wmax[lane] : 0ull;
-    int r = 0;
-#pragma unroll
-    for (int q = 0; q < NW; ++q) r += readlane_u64(mi, q) > mi;
-    const uint64_t hit = __ballot(lane < NW && r == K - 1);
-    const uint64_t T = hit ? readlane_u64(mi, __builtin_ctzll(hit)) : 0ull;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (key[j] != 0ull && key[j] >= T) {
-            const int p = atomicAdd(ncand, 1);
-            if (p < 64) cand[p] = key[j];
-        }
-    bsync<LDS_SYNC>();
-    const int n = *ncand;
-    if (n > 64) {
-        // every wave's K largest, then the K largest of those
-        for (int k = 0; k < K; ++k) {
-            uint64_t b = key[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) b = key[j] > b ? key[j] : b;
-            const uint64_t w = wave_max_key(b);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (key[j] == w) key[j] = 0ull;
-            if (lane == 0) sk[wave * K + k] = w;
-        }
-        bsync<LDS_SYNC>();
-    }
-    if (wave == 0) {
-        // one candidate per lane, ranked against the others
-        const int nc = n <= 64 ? n : NW * K;
-        const uint64_t mine = lane < nc ? (n <= 64 ? cand[lane] : sk[lane]) : 0ull;
-        int rank = 0;
-        for (int q = 0; q < nc; ++q) rank += readlane_u64(mine, q) > mine;
-        const bool chosen = lane < nc && rank < K;
-        // softmax over the selected logits, summed in rank order
-        const uint64_t top = readlane_u64(mine, __builtin_ctzll(__ballot(lane < nc && rank == 0)));
-        const float v0 = key_value(top);
-        const float ex = chosen ? expf(key_value(mine) - v0) : 0.f;
-        float z = 0.f;
-        for (int k = 0; k < K; ++k)
-            z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), __builtin_ctzll(__ballot(chosen && rank == k))));
-        if (chosen) {
-            sel[rank] = key_index(mine);
-            selw[rank] = ex / z;
-        }
-    }
-    bsync<LDS_SYNC>();
-}
-
-// (v, i) pairs ordered by value, then by the lower index: true when (ov, oi)
-// comes first.
-__device__ __forceinline__ bool key_before(float ov, int oi, float v, int i)
-{
-    return ov > v || (ov == v && oi < i);
-}
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v)
-{
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
-}
-
-// First (v, i) of a full wave by key_before, returned in every lane.  Within
-// each row of 16 lanes: two quad permutations, the half-row mirror and the
-// row mirror (DPP, no LDS round trip); the four row winners are then read
-// as scalars.  Must be called by all 64 lanes.
-__device__ __forceinline__ void wave_argmax(float &v, int &i)
-{
-#define MOE_ARGMAX_STEP(CTRL)                                                                                           \
-    {                                                                                                                   \
-        const float ov = __int_as_float(dpp_i<CTRL>(__float_as_int(v)));                                                \
-        const int oi = dpp_i<CTRL>(i);                                                                                  \
-        if (key_before(ov, oi, v, i)) {                                                                                 \
-            v = ov;                                                                                                     \
-            i = oi;                                                                                                     \
-        }                                                                                                               \
-    }
-    MOE_ARGMAX_STEP(0xB1)   // quad_perm [1,0,3,2]
-    MOE_ARGMAX_STEP(0x4E)   // quad_perm [2,3,0,1]
-    MOE_ARGMAX_STEP(0x141)  // row_half_mirror
-    MOE_ARGMAX_STEP(0x140)  // row_mirror
-#undef MOE_ARGMAX_STEP
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (key_before(rv, ri, bv, bi)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    v = bv;
-    i = bi;
-}
-
-// Top K of lg[0..E) (LDS) for a whole block of NW waves: every wave takes
-// the K first of its elements (e = 64 w + lane + 64 NW j) by K wave argmax
-// rounds, parks them in cv/ci (LDS, NW*K entries), and wave 0 merges them in
-// K more rounds.  Order: larger value first, the lower index on an exact
-// tie.  sel/selw (LDS) receive the indices and the routing weights.  Ends
-// with __syncthreads.  E <= 64*NW*8.
-template <int NW>
-__device__ __forceinline__ void block_topk(const float *lg, int E, int K, float *cv, int *ci, int *sel, float *selw)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t taken = 0;
-    for (int k = 0; k < K; ++k) {
-        float v = -INFINITY;
-        int i = 0x7FFFFFFF;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int e = 64 * wave + lane + 64 * NW * j;
-            if (e < E && !((taken >> j) & 1u) && key_before(lg[e], e, v, i)) {
-                v = lg[e];
-                i = e;
-            }
-        }
-        wave_argmax(v, i);
-        if (i != 0x7FFFFFFF && (i & 63) == lane && ((i >> 6) % NW) == wave) taken |= 1u << ((i >> 6) / NW);
-        if (lane == 0) {
-            cv[wave * K + k] = v;
-            ci[wave * K + k] = i;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        float v = -INFINITY;
-        int i = 0x7FFFFFFF;
-        if (lane < NW * K) {
-            v = cv[lane];
-            i = ci[lane];
-        }
-        int idx[kMaxTopK];
-        float vals[kMaxTopK], w[kMaxTopK];
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            idx[k] = -1;
-            vals[k] = -INFINITY;
-            if (k >= K) continue;
-            float bv = v;
-            int bi = i;
-            wave_argmax(bv, bi);
-            idx[k] = bi;
-            vals[k] = bv;
-            if (i == bi) {
-                v = -INFINITY;
-                i = 0x7FFFFFFF;
-            }
-        }
-        topk_weights(vals, K, w);
-        if (lane == 0) {
-#pragma unroll
-            for (int k = 0; k < kMaxTopK; ++k) {
-                if (k >= K) continue;
-                sel[k] = idx[k];
-                selw[k] = w[k];
-            }
-        }
-    }
-    __syncthreads();
-}
-
 
 }  // namespace dev
 }  // namespace moe

@@ -177,13 +177,14 @@ struct StackArgs {
 
 // Dynamic LDS of the stack kernel (byte offsets, 16-byte aligned).
 struct StackLds {
-    uint32_t xs, rs, dig, csum, xcinv, u, hdig, hcsum, hcinv, shst, misc, total;
+    uint32_t xs, rs, dig, csum, xcinv, u, hdig, hcsum, hcinv, misc, total;
 };
 constexpr int kStackMiscWords = 256;
 // LDS of the stack kernel: x (fp32) and r of the layer, x's digit table
 // with per-chunk sums and steps, a region shared by the router partials
-// (phase A), the logits (B) and the combined rows (C), h's digit tables,
-// the shared expert's staged h rows, and small scalars.
+// (phase A: one per wave and round of router rows) and the combined rows
+// (phase C), h's digit tables with their per-chunk
+// sums and steps, and small scalars (selection, weights, ready flags).
 __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bits)
 {
     const uint32_t codes = 128 / bits, dw = 4 * (8 / bits) * 3;
@@ -204,7 +205,6 @@ __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bi
     take(l.hdig, hc * dw * 4);
     take(l.hcsum, hc * 4);
     take(l.hcinv, hc * 4);
-    take(l.shst, ((uint32_t)I + 8u) * 4);
     take(l.misc, kStackMiscWords * 4);
     l.total = o;
     return l;

@@ -4,35 +4,33 @@
 // experts, runs them, and hands the combined, normalised result to the
 // next layer (hakusoku.com, "パイプライン概要" and "主要技術"; toolarium.ru,
 // "Оптимизации, которые сработали").  Here every layer of a token runs in
-// one launch of one 512-thread block per CU, and a layer is three phases
-// separated by grid barriers:
+// one launch of one 512-thread block per CU, and every wave of a block
+// takes part in every phase:
 //
 //   A  x_l = RMSNorm(r_l) * gamma_{l-1} in every block, from the residual
-//      rows the previous layer published, with its digit table; the
-//      router rows                                           -> barrier 1
-//   B  top-K in every wave (no broadcast round trip); the routed experts'
-//      gate/up rows                                          -> barrier 2
-//   C  h of every slot as digit tables; down rows of all slots, combined in
-//      slot order, plus the residual; per-block sum of squares -> barrier 3
+//      rows and sums of squares the previous layer published, and x_l's
+//      digit table; the block's router rows (four waves per row); the
+//      logits go out tagged
+//   B  wave 0 polls the logits and takes the top-K, publishing each
+//      selected index (LDS) as soon as its round ends; waves 1.. run the
+//      shared expert's gate/up rows (loaded a layer ahead) meanwhile; then
+//      every wave its unit of routed gate/up rows as soon as its slot's
+//      expert is known; h goes out tagged and the down rows of every slot
+//      are requested
+//   C  h of every slot, polled, as digit tables; the next layer's router
+//      and shared rows are requested; down rows of all slots, combined in
+//      slot order; r' = r + c for the block's rows and the block's sum of
+//      squares go out tagged
 //
-// The waves of a block have two jobs.  A wave's loads complete in the
-// order they were issued, so a wave holding megabytes of weight loads in
-// flight cannot also make the small, latency-critical reads (the residual,
-// the logits, h) or wait for its own stores without waiting for those
-// weights first.  So:
-//   - activation waves (0..3) make every such read and every global store:
-//     the residual and x's digit table, the logits and the top-K, the
-//     routed gate/up rows (loaded right after the top-K, nothing else in
-//     flight) and h, h's digit tables, r' = r + c and the block's sum of
-//     squares, and they poll the barriers;
-//   - weight waves (4..7) only load weights and hand results over in LDS:
-//     the router rows, the shared expert's gate/up rows (computed in the
-//     shadow of barrier 1, so off the critical path), and the down rows of
-//     every slot, issued right after the top-K together with the next
-//     layer's router and shared gate/up rows, so that the memory system
-//     streams the layer's weights back to back while the block computes.
-// Arrival at a grid barrier waits only for the activation waves' stores;
-// every block barrier inside a layer is LDS-only.
+// Blocks never meet at a grid barrier.  Every value handed from block to
+// block (logits, h, residual rows, sums of squares) is a 64-bit word that
+// carries the epoch of the exchange that produced it (tag_store); a reader
+// polls the words it needs until each carries the expected epoch.  A
+// producer therefore never waits for its own stores to be acknowledged,
+// and a consumer waits only for the values it reads.  Epochs grow by three
+// per layer and carry over from launch to launch through per-block slots
+// in the workspace, so nothing is ever reset.  Inside a block every
+// barrier is LDS-only.
 //
 // Digit tables are built in registers with one fixed-point step per
 // 16-byte code chunk (chunk_digits_lane): no block-wide maximum, no LDS
@@ -40,9 +38,9 @@
 //
 // Arithmetic per layer is that of moe_layer_step's definition: every sum
 // runs in a fixed order (no float atomics), every block and every wave
-// derives the same RMS factor from the same partial sums in the same order
-// and the same top-K from the same logits, so results are deterministic and
-// a stack launch equals the same layers launched one by one, bit for bit.
+// derives the same RMS factor from the same partial sums in the same order,
+// and one top-K per block from the same logits, so results are
+// deterministic and equal, bit for bit, from launch to launch.
 #include "moe_device.h"
 
 #ifndef MOE_STACK_BITS
@@ -92,33 +90,9 @@ __device__ __forceinline__ StackLayer layer_of(KArgs A, int l)
     return y;
 }
 
-// The total of the NB per-block partial sums of squares, by one wave:
-// lane l adds blocks 4l..4l+3 (+256 i for larger grids) in order, then the
-// lanes; every wave of every block adds the same values in the same order,
-// so all of them derive the same RMS factor.  rms_issue starts the first
-// load (so that other loads can follow it into flight), rms_factor waits.
-__device__ __forceinline__ float4 rms_issue(const float *ss, int lane)
-{
-    return xload4(ss, 4 * lane);
-}
-__device__ __forceinline__ float rms_factor(float4 v, const float *ss, int NB, int D, float eps, int lane)
-{
-    float t = 0.f;
-    for (int i = 0; 256 * i < NB; ++i) {
-        if (i > 0) v = xload4(ss, 256 * i + 4 * lane);
-        const int q = 256 * i + 4 * lane;
-        t += q < NB ? v.x : 0.f;
-        t += q + 1 < NB ? v.y : 0.f;
-        t += q + 2 < NB ? v.z : 0.f;
-        t += q + 3 < NB ? v.w : 0.f;
-    }
-    t = group_sum<64>(t);
-    return 1.f / sqrtf(t / (float)D + eps);
-}
-
 // Per-layer LDS views.
 struct Views {
-    float *xs, *rs, *csum, *xcinv, *u, *hcsum, *hcinv, *shst, *misc;
+    float *xs, *rs, *csum, *xcinv, *u, *hcsum, *hcinv, *misc;
     int *dig, *hdig;
 };
 template <int BITS>
@@ -131,11 +105,10 @@ __device__ __forceinline__ Views views(unsigned char *smem, int D, int E, int I,
     v.dig = reinterpret_cast<int *>(smem + lo.dig);
     v.csum = reinterpret_cast<float *>(smem + lo.csum);
     v.xcinv = reinterpret_cast<float *>(smem + lo.xcinv);
-    v.u = reinterpret_cast<float *>(smem + lo.u);  // router partials (A), logits (B), combined rows (C)
+    v.u = reinterpret_cast<float *>(smem + lo.u);  // router partials (A), combined rows (C)
     v.hdig = reinterpret_cast<int *>(smem + lo.hdig);
     v.hcsum = reinterpret_cast<float *>(smem + lo.hcsum);
     v.hcinv = reinterpret_cast<float *>(smem + lo.hcinv);
-    v.shst = reinterpret_cast<float *>(smem + lo.shst);
     v.misc = reinterpret_cast<float *>(smem + lo.misc);
     return v;
 }
@@ -466,7 +439,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
     // ---- the stack's output: residual stream and its normalisation
     {
         KArgs A = kargs();
-        const int tid = threadIdx.x, lane = tid & 63, NB = gridDim.x, b = blockIdx.x, D = A->D, L = A->n_layers;
+        const int tid = threadIdx.x, NB = gridDim.x, b = blockIdx.x, D = A->D, L = A->n_layers;
         const uint32_t t_res = base + 3u * L;
         float4 rv[1];
         const float t = poll_residual<1>(A, 0, 0, NB, t_res, true, rv);

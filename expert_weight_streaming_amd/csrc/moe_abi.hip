@@ -115,6 +115,7 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
             field = off;
             off = round_up(off + bytes, 256);
         };
+        take(L.lpart, (size_t)moe::kRouteSplit * T * E * 4);
         take(L.count, E * 4);
         take(L.offset, (E + 1) * 4);
         take(L.perm, T * K * 4);
@@ -305,6 +306,7 @@ moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, in
     b.topk_idx = idx;
     b.topk_w = w;
     b.logits = logits ? logits : reinterpret_cast<float *>(ws + L.logits);
+    b.lpart = reinterpret_cast<float *>(ws + L.lpart);
     b.count = reinterpret_cast<int32_t *>(ws + L.count);
     b.offset = reinterpret_cast<int32_t *>(ws + L.offset);
     b.perm = reinterpret_cast<int32_t *>(ws + L.perm);

@@ -6,8 +6,10 @@
 // every selected expert's rows are fetched once per step and applied to all
 // of that expert's tokens:
 //
-//   k_route_m      logits[t][e] for all tokens (fp32 matrix cores)
-//   k_topk_b       per-token top-K and softmax weights (one wave per token)
+//   k_route_m      partial logits of every token over kRouteSplit slices of
+//                  the hidden dimension (fp32 matrix cores)
+//   k_topk_b       the logits (slices added in order), per-token top-K and
+//                  softmax weights (one wave per token)
 //   k_group        the grouping: count[e], offset[e] (exclusive prefix
 //                  sum), the pair permutation perm[pos] = t*K + k sorted by
 //                  (expert, pair index), its inverse, and the list of active
@@ -33,26 +35,28 @@ using namespace dev;
 
 // ---------------------------------------------------------------------------
 // Router for T tokens on the matrix cores (fp32): a block owns a tile of 16
-// router rows x 16 tokens, its four waves take every fourth 64-column block
-// of the hidden dimension, and their partial logits are added in order in
-// LDS.
+// router rows x 16 tokens over one slice of the hidden dimension (slices
+// spread the router's bytes over enough CUs); its four waves take every
+// fourth 64-column block of the slice, and their partial logits are added
+// in order in LDS.  lpart[s][t][e] receives slice s's partial logit.
 // v_mfma_f32_16x16x4f32: lane l supplies row (A) / token (B) l % 16 at
 // k = l / 16; each lane loads 4 consecutive columns, so 4 instructions
 // cover 16 columns (A and B use the same column-to-instruction map).
 typedef float v4f __attribute__((ext_vector_type(4)));
-__global__ void __launch_bounds__(256) k_route_m(BatchArgs a)
+__global__ void __launch_bounds__(256) k_route_m(BatchArgs a, int splits)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, h = lane >> 4;
     const int D = a.D, E = a.E, T = a.T;
-    const int ttiles = (T + 15) / 16;
-    const int e0 = (blockIdx.x / ttiles) * 16, t0 = (blockIdx.x % ttiles) * 16;
+    const int ttiles = (T + 15) / 16, rtiles = (E + 15) / 16;
+    const int sl = blockIdx.x / (rtiles * ttiles), rem = blockIdx.x - sl * rtiles * ttiles;
+    const int e0 = (rem / ttiles) * 16, t0 = (rem % ttiles) * 16;
     const int row = min(e0 + r16, E - 1), tok = min(t0 + r16, T - 1);
     const float *w = a.router + (size_t)row * D;
     const float *x = a.x + (size_t)tok * D;
-    // wave w: the 64-column blocks w, w + 4, ... (D is a multiple of 64)
+    const int lo = sl * (D / splits), hi = lo + D / splits;  // D / splits is a multiple of 64
     v4f c = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 64 * wave; k0 < D; k0 += 256) {
+    for (int k0 = lo + 64 * wave; k0 < hi; k0 += 256) {
         float4 wv[4], xv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -74,27 +78,59 @@ __global__ void __launch_bounds__(256) k_route_m(BatchArgs a)
     __syncthreads();
     if (wave == 0) {
         const int t = t0 + r16;
+        float *out = a.lpart + (size_t)sl * T * E;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = e0 + 4 * h + r;
             const float v = ((part[0][lane][r] + part[1][lane][r]) + part[2][lane][r]) + part[3][lane][r];
-            if (e < E && t < T) a.logits[(size_t)t * E + e] = v;
+            if (e < E && t < T) out[(size_t)t * E + e] = v;
         }
     }
 }
 
+// Hidden-dimension slices of the batched router: kRouteSplit when the
+// slices stay multiples of 64 columns.
+__host__ __device__ inline int route_splits(int D)
+{
+    for (int s = kRouteSplit; s > 1; s >>= 1)
+        if (D % (64 * s) == 0) return s;
+    return 1;
+}
+
 // ---------------------------------------------------------------------------
-// Top-K of every token: one wave per token, its logits in LDS; K rounds of
+// Top-K of every token: one wave per token, its logits (the slices' partial
+// logits added in slice order, also stored to logits[t]) in LDS; K rounds of
 // the wave's largest remaining key (larger logit first, the lower index on a
 // tie), then the softmax over the selected logits.
-__global__ void __launch_bounds__(256) k_topk_b(BatchArgs a)
+__global__ void __launch_bounds__(256) k_topk_b(BatchArgs a, int splits)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
-    const int E = a.E, K = a.K;
+    const int E = a.E, K = a.K, T = a.T;
     __shared__ float lg[4][4096];
-    if (t >= a.T) return;  // whole waves leave; no block barrier follows
-    for (int e = lane; e < E; e += 64) lg[wave][e] = a.logits[(size_t)t * E + e];
+    if (t >= T) return;  // whole waves leave; no block barrier follows
+    for (int e0 = 0; e0 < E; e0 += 64 * 8) {
+        float v[8][kRouteSplit];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + lane + 64 * u;
+#pragma unroll
+            for (int sl = 0; sl < kRouteSplit; ++sl)
+                v[u][sl] = e < E && sl < splits ? a.lpart[((size_t)sl * T + t) * E + e] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + lane + 64 * u;
+            float sum = v[u][0];
+#pragma unroll
+            for (int sl = 1; sl < kRouteSplit; ++sl)
+                if (sl < splits) sum += v[u][sl];
+            if (e < E) {
+                lg[wave][e] = sum;
+                a.logits[(size_t)t * E + e] = sum;
+            }
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     uint64_t taken = 0;  // bit j: element lane + 64 j selected
@@ -128,36 +164,55 @@ __global__ void __launch_bounds__(256) k_topk_b(BatchArgs a)
     }
 }
 
-// Exclusive prefix sums of v[0..n) in place (n <= 4 * blockDim.x), plus the
-// total; one block.  Each thread sums 4 consecutive entries, then a
-// Hillis-Steele scan over the threads' sums in LDS.
-__device__ __forceinline__ int block_exscan(int *v, int n, int *part)
+// Exclusive prefix sums of three arrays v0, v1, v2 [0..n) in place
+// (n <= 4 * blockDim.x), their totals in tot[]; one block.  Each thread sums
+// 4 consecutive entries, a wave scan (shuffles) runs over the threads' sums,
+// then every thread adds the totals of the waves before its own (one
+// barrier).  wsum: LDS [blockDim.x / 64][3].
+__device__ __forceinline__ void block_exscan3(int *v0, int *v1, int *v2, int n, int (*wsum)[3], int (&tot)[3])
 {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    int loc[4], run = 0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    int *const v[3] = {v0, v1, v2};
+    int loc[3][4], run[3], inc[3];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = 4 * tid + q;
-        loc[q] = run;
-        run += i < n ? v[i] : 0;
-    }
-    part[tid] = run;
-    __syncthreads();
-    for (int off = 1; off < nt; off <<= 1) {
-        const int add = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += add;
-        __syncthreads();
-    }
-    const int before = tid > 0 ? part[tid - 1] : 0;
-    const int total = part[nt - 1];
+    for (int c = 0; c < 3; ++c) {
+        run[c] = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = 4 * tid + q;
-        if (i < n) v[i] = before + loc[q];
+        for (int q = 0; q < 4; ++q) {
+            const int i = 4 * tid + q;
+            loc[c][q] = run[c];
+            run[c] += i < n ? v[c][i] : 0;
+        }
+        inc[c] = run[c];
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const int y = __shfl_up(inc[c], off, 64);
+            if (lane >= off) inc[c] += y;
+        }
+    if (lane == 63)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) wsum[wave][c] = inc[c];
     __syncthreads();
-    return total;
+    int before[3] = {0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < 3; ++c) tot[c] = 0;
+    for (int w = 0; w < nw; ++w)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            if (w < wave) before[c] += wsum[w][c];
+            tot[c] += wsum[w][c];
+        }
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = 4 * tid + q;
+            if (i < n) v[c][i] = before[c] + (inc[c] - run[c]) + loc[c][q];
+        }
+    __syncthreads();
 }
 
 // One block of 1024 threads: the token -> expert grouping of the
@@ -174,7 +229,7 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     __shared__ int s_off[4096];
     __shared__ int s_flag[4096];
     __shared__ int s_big[4096];
-    __shared__ int part[1024];
+    __shared__ int wsum[16][3];
     for (int p = tid; p < P; p += 1024) s_idx[p] = a.topk_idx[p];
     for (int e = tid; e < E; e += 1024) s_count[e] = 0;
     __syncthreads();
@@ -191,18 +246,17 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
         a.count[e] = s_count[e];
     }
     __syncthreads();
-    const int total = block_exscan(s_off, E, part);
-    const int nact = block_exscan(s_flag, E, part);
-    const int nbig = block_exscan(s_big, E, part);
+    int tot[3];
+    block_exscan3(s_off, s_flag, s_big, E, wsum, tot);
     for (int e = tid; e < E; e += 1024) {
         a.offset[e] = s_off[e];
         if (s_count[e]) a.act[s_flag[e]] = e;
         if (s_count[e] >= kMfmaMin) a.big[s_big[e]] = e;
     }
     if (tid == 0) {
-        a.offset[E] = total;
-        *a.n_act = nact;
-        *a.n_big = nbig;
+        a.offset[E] = tot[0];
+        *a.n_act = tot[1];
+        *a.n_big = tot[2];
     }
     for (int p = tid; p < P; p += 1024) {
         const int e = s_idx[p];
@@ -470,17 +524,27 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
     float rv[PER];
     float ss = 0.f;
     // the combine of the token's rows first (the outputs never alias y),
-    // summed in slot order, then residual and norm
+    // summed in slot order, then residual and norm; each slot's rows are
+    // loaded together
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int o = tid + 1024 * j;
-        float c = 0.f;
-        if (o < D) {
-            for (int k = 0; k < K; ++k)
-                if (pos[k] >= 0) c += wts[k] * a.y[(size_t)pos[k] * D + o];
-            if (has_shared) c += a.y[(size_t)(a.T * K + t) * D + o];
+    for (int j = 0; j < PER; ++j) rv[j] = 0.f;
+    for (int k = 0; k <= K; ++k) {
+        const int pk = k < K ? pos[k] : (has_shared ? a.T * K + t : -1);
+        if (pk < 0) continue;
+        float yv[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int o = tid + 1024 * j;
+            yv[j] = o < D ? a.y[(size_t)pk * D + o] : 0.f;
         }
-        rv[j] = c;
+        if (k < K) {
+            const float wk = wts[k];
+#pragma unroll
+            for (int j = 0; j < PER; ++j) rv[j] += wk * yv[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) rv[j] += yv[j];
+        }
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -696,7 +760,7 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gate_up_m(BatchArgs a)
         const uint8_t *const sbr[2] = {it.blob + sb0 + (uint64_t)(i0 + 4 * h) * ng * 4,
                                        it.blob + sb0 + mat_sb + (uint64_t)(i0 + 4 * h) * ng * 4};
         float acc[2][4];
-        mf_tile<BITS, 2, 4>(rowq, sbr, ng * 4, a.xdig + (size_t)tok * xdw, a.xcsum + (size_t)tok * nchunks, a.xinv[tok], wave,
+        mf_tile<BITS, 2, 2>(rowq, sbr, ng * 4, a.xdig + (size_t)tok * xdw, a.xcsum + (size_t)tok * nchunks, a.xinv[tok], wave,
                             kMfWaves, ng, h, acc);
         mf_reduce<2, kMfWaves>(acc, part);
         if (wave == 0 && tok_ok) {
@@ -762,7 +826,7 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
                            nchunks_d * C::DW, nchunks_d);
         break;
     case 1: {  // gate/up
-        constexpr int R = BITS == 4 ? 4 : 8;
+        constexpr int R = 4;
         if (cpl <= 1) hipLaunchKernelGGL((k_gate_up_b<BITS, 1, R>), dim3(1024), dim3(256), 0, s, a);
         else if constexpr (BITS == 4) {
             if (cpl <= 2) hipLaunchKernelGGL((k_gate_up_b<BITS, 2, 2>), dim3(1024), dim3(256), 0, s, a);
@@ -809,10 +873,11 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s)
 {
     if (do_topk) {
-        hipLaunchKernelGGL(k_route_m, dim3(((a.E + 15) / 16) * ((a.T + 15) / 16)), dim3(256), 0, s, a);
+        const int splits = route_splits(a.D);
+        hipLaunchKernelGGL(k_route_m, dim3(splits * ((a.E + 15) / 16) * ((a.T + 15) / 16)), dim3(256), 0, s, a, splits);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_topk_b, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_topk_b, dim3((a.T + 3) / 4), dim3(256), 0, s, a, splits);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, a);

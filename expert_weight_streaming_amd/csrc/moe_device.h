@@ -288,7 +288,13 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
     using C = Codes<BITS>;
     const int tid = threadIdx.x, nt = blockDim.x;
     float m = 0.f;
-    for (int i = tid; i < n; i += nt) m = fmaxf(m, fabsf(x[i]));
+    for (int i0 = tid; i0 < n; i0 += 4 * nt) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = i0 + u * nt < n ? fabsf(x[i0 + u * nt]) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m = fmaxf(m, v[u]);
+    }
     m = group_max<64>(m);
     if ((tid & 63) == 0) red[tid >> 6] = m;
     bsync<LDS_SYNC>();

@@ -16,6 +16,7 @@ constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
 // In a batch, experts with at least this many tokens take the matrix-core
 // grouped kernels, the others the dot-product ones.
 constexpr int kMfmaMin = 8;
+constexpr int kRouteSplit = 4;  // hidden-dimension slices of the batched router (partial logits)
 
 // Workspace layout (byte offsets), all 64-byte aligned.
 struct WsLayout {
@@ -34,6 +35,7 @@ struct WsLayout {
     size_t tres = 0;         // [D] residual rows
     size_t tss = 0;          // [kMaxLayerBlocks] per-block sums of squares
     // batches (T > 1)
+    size_t lpart = 0;        // float [kRouteSplit][T][E] partial logits
     size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0, big = 0, n_big = 0;
     size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
     size_t total = 0;
@@ -103,6 +105,7 @@ struct BatchArgs {
     int32_t *topk_idx;       // [T][K]
     float *topk_w;           // [T][K]
     float *logits;           // [T][E]
+    float *lpart;            // [splits][T][E] partial logits over slices of the hidden dimension
     int32_t *count;          // [E]
     int32_t *offset;         // [E+1]
     int32_t *perm;           // [T*K] position -> pair index t*K + k

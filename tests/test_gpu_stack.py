@@ -6,6 +6,7 @@ valid alternative).  Also: HIP-graph replay equals eager execution bitwise.
 import numpy as np
 import pytest
 
+import oracle
 import seedgen
 import workloads as W
 
@@ -108,6 +109,33 @@ def test_stack_launch_equals_layer_by_layer(name, bits, layers):
         assert torch.equal(r1, r2) and torch.equal(x1, x2)
         assert torch.equal(rec_a, rec_b)
         v = x1.clone()
+
+
+def test_stack_topk_exact_ties_pick_lower_index():
+    """Logits that tie exactly, within one lane's elements (indices 64 apart)
+    and across lanes, go to the lower expert index in the stack kernel's
+    top-K, as in the oracle; the weights follow the oracle's softmax."""
+    cfg = seedgen.CONFIGS["tiny"].replace(E=512, K=4, layers=2, seed=0x5EED00F0)
+    print("[gpu case] stack top-K exact ties", flush=True)
+    st = W.build_stack(cfg, layers=2)
+    Wr = np.zeros((cfg.E, cfg.D), np.float32)
+    Wr[:, 0] = np.random.default_rng(7).uniform(-1.0, 1.0, cfg.E).astype(np.float32)
+    for e in (400, 17):
+        Wr[e, 0] = 5.0
+    for e in (134, 6, 300, 70):
+        Wr[e, 0] = 2.0
+    st.router[0].copy_(torch.from_numpy(Wr))
+    x = np.zeros(cfg.D, np.float32)
+    x[0] = 1.0
+    r, xx = torch.from_numpy(x).cuda().view(1, -1), torch.from_numpy(x).cuda().view(1, -1)
+    st.step(r, xx)
+    torch.cuda.synchronize()
+    assert int(st.workspace[:4].view(torch.int32).item()) == 0, "device error flags"
+    lo = Wr.astype(np.float64) @ x.astype(np.float64)
+    osel, _ = oracle.topk(lo, cfg.K)
+    sel = st.topk_idx.cpu().numpy()[0, 0]
+    assert list(sel) == list(osel) == [17, 400, 6, 70]
+    W.assert_close(st.topk_w.cpu().numpy()[0, 0], oracle.route_weights(lo, osel), "routing weights", rel=1e-5)
 
 
 def test_layer_plan_is_fused_at_the_pages_shape():

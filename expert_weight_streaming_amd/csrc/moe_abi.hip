@@ -124,6 +124,8 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
         take(L.n_act, 4);
         take(L.big, E * 4);
         take(L.n_big, 4);
+        take(L.mwork, (E + 1) * 4 * 4);
+        take(L.n_mwork, 4);
         take(L.xdig, (size_t)T * (D * 3 / 4) * 4);
         take(L.xcsum, (size_t)T * (D / cw) * 4);
         take(L.xinv, (size_t)T * 4);
@@ -315,6 +317,8 @@ moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, in
     b.n_act = reinterpret_cast<int32_t *>(ws + L.n_act);
     b.big = reinterpret_cast<int32_t *>(ws + L.big);
     b.n_big = reinterpret_cast<int32_t *>(ws + L.n_big);
+    b.mwork = reinterpret_cast<int32_t *>(ws + L.mwork);
+    b.n_mwork = reinterpret_cast<int32_t *>(ws + L.n_mwork);
     b.xdig = reinterpret_cast<int *>(ws + L.xdig);
     b.xcsum = reinterpret_cast<float *>(ws + L.xcsum);
     b.xinv = reinterpret_cast<float *>(ws + L.xinv);

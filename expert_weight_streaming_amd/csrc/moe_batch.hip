@@ -219,7 +219,9 @@ __device__ __forceinline__ void block_exscan3(int *v0, int *v1, int *v2, int n, 
 // selections: count[e], offset[e] (exclusive prefix sums), the pair
 // permutation perm[pos] = t*K + k sorted by (expert, pair index), its
 // inverse, the active experts in ascending order and, among them, those
-// with at least kMfmaMin tokens (the matrix-core kernels' work list).
+// with at least kMfmaMin tokens; and the matrix-core kernels' dense work
+// list: every (such expert, or the shared expert when T >= kMfmaMin; tile of
+// 16 of its tokens).
 __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
 {
     const int tid = threadIdx.x;
@@ -230,6 +232,7 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     __shared__ int s_flag[4096];
     __shared__ int s_big[4096];
     __shared__ int wsum[16][3];
+    __shared__ int s_bigl[4096];
     for (int p = tid; p < P; p += 1024) s_idx[p] = a.topk_idx[p];
     for (int e = tid; e < E; e += 1024) s_count[e] = 0;
     __syncthreads();
@@ -251,12 +254,24 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     for (int e = tid; e < E; e += 1024) {
         a.offset[e] = s_off[e];
         if (s_count[e]) a.act[s_flag[e]] = e;
-        if (s_count[e] >= kMfmaMin) a.big[s_big[e]] = e;
+        if (s_count[e] >= kMfmaMin) {
+            a.big[s_big[e]] = e;
+            s_bigl[s_big[e]] = e;
+        }
     }
     if (tid == 0) {
         a.offset[E] = tot[0];
         *a.n_act = tot[1];
         *a.n_big = tot[2];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int w = 0;
+        for (int ii = 0; ii < tot[2]; ++ii)
+            for (int tt = 0; 16 * tt < s_count[s_bigl[ii]]; ++tt) a.mwork[w++] = ii << 2 | tt;
+        if (a.src.n_slots > K && T >= kMfmaMin)
+            for (int tt = 0; 16 * tt < T; ++tt) a.mwork[w++] = tot[2] << 2 | tt;
+        *a.n_mwork = w;
     }
     for (int p = tid; p < P; p += 1024) {
         const int e = s_idx[p];
@@ -739,20 +754,18 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_gate_up_m(BatchArgs a)
     using C = Codes<BITS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, h = lane >> 4;
-    const int D = a.D, I = a.I, T = a.T;
-    const int nbig = *a.n_big;
-    const int items = nbig + (a.src.n_slots > a.src.top_k && T >= kMfmaMin ? 1 : 0);
-    const int rtiles = I / 16, ttiles = (T + 15) / 16;  // I is a multiple of 64
+    const int D = a.D, I = a.I;
+    const int nbig = *a.n_big, nwork = *a.n_mwork;
+    const int rtiles = I / 16;  // I is a multiple of 64
     const int ng = D / kGroup, nchunks = D * BITS / 128;
     const int xdw = nchunks * C::DW;
     const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)D * BITS / 8;
     const uint64_t sb0 = 3 * mat_q, mat_sb = (uint64_t)I * ng * 4;
     __shared__ float part[kMfWaves - 1][2][64][4];
-    for (int u = blockIdx.x; u < items * rtiles * ttiles; u += gridDim.x) {
-        const int ii = u / (rtiles * ttiles), rem = u - ii * rtiles * ttiles;
-        const int i0 = (rem / ttiles) * 16, j0 = (rem % ttiles) * 16;
+    for (int u = blockIdx.x; u < nwork * rtiles; u += gridDim.x) {
+        const int wk = a.mwork[u / rtiles], ii = wk >> 2;
+        const int i0 = (u % rtiles) * 16, j0 = (wk & 3) * 16;
         const Item it = big_item_of(a, ii, nbig);
-        if (j0 >= it.n) continue;  // uniform over the block
         const int jt = j0 + r16;
         const bool tok_ok = jt < it.n;
         const int tok = token_of(a, it, tok_ok ? jt : j0);
@@ -782,20 +795,18 @@ __global__ void __launch_bounds__(64 * kMfWaves) k_down_m(BatchArgs a)
     using C = Codes<BITS>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, h = lane >> 4;
-    const int D = a.D, I = a.I, T = a.T;
-    const int nbig = *a.n_big;
-    const int items = nbig + (a.src.n_slots > a.src.top_k && T >= kMfmaMin ? 1 : 0);
-    const int rtiles = D / 16, ttiles = (T + 15) / 16;  // D is a multiple of 64
+    const int D = a.D, I = a.I;
+    const int nbig = *a.n_big, nwork = *a.n_mwork;
+    const int rtiles = D / 16;  // D is a multiple of 64
     const int ng = I / kGroup, nchunks = I * BITS / 128;
     const int hdw = nchunks * C::DW;
     const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)I * BITS / 8;
     const uint64_t sbd = 3 * mat_q + 2 * ((uint64_t)D * ng * 4);
     __shared__ float part[kMfWaves - 1][1][64][4];
-    for (int u = blockIdx.x; u < items * rtiles * ttiles; u += gridDim.x) {
-        const int ii = u / (rtiles * ttiles), rem = u - ii * rtiles * ttiles;
-        const int o0 = (rem / ttiles) * 16, j0 = (rem % ttiles) * 16;
+    for (int u = blockIdx.x; u < nwork * rtiles; u += gridDim.x) {
+        const int wk = a.mwork[u / rtiles], ii = wk >> 2;
+        const int o0 = (u % rtiles) * 16, j0 = (wk & 3) * 16;
         const Item it = big_item_of(a, ii, nbig);
-        if (j0 >= it.n) continue;  // uniform over the block
         const int jt = j0 + r16;
         const bool ok = jt < it.n;
         const int pos = it.pos0 + (ok ? jt : j0);

@@ -37,6 +37,7 @@ struct WsLayout {
     // batches (T > 1)
     size_t lpart = 0;        // float [kRouteSplit][T][E] partial logits
     size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0, big = 0, n_big = 0;
+    size_t mwork = 0, n_mwork = 0;  // matrix-core work list: (item << 2 | 16-token tile), its length
     size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
     size_t total = 0;
 };
@@ -114,6 +115,9 @@ struct BatchArgs {
     int32_t *n_act;          // [1]
     int32_t *big;            // [E] experts with at least kMfmaMin tokens, ascending
     int32_t *n_big;          // [1]
+    int32_t *mwork;          // [(E+1)*4] matrix-core work: item ii (big[ii], or the shared expert for
+                             // ii == n_big) << 2 | tile of 16 of its tokens
+    int32_t *n_mwork;        // [1]
     int *xdig;               // [T][D/chunk][DW] digit tables of x
     float *xcsum;            // [T][D/chunk]
     float *xinv;             // [T]

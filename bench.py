@@ -316,7 +316,7 @@ def resident_extra(cfg, steps, warmup):
     if T > 1:
         out["distinct_experts_per_layer"] = round(float(np.mean(distinct)), 2)
         out["experts_with_8plus_tokens_per_layer"] = round(float(np.mean(heavy)), 2)
-        out["note"] = "experts with 8+ tokens and the shared expert run on the int8 matrix-core grouped kernels"
+        out["note"] = "every active expert and the shared expert run on the int8 matrix-core grouped kernels (16-token tiles)"
     log(f"{cfg.name}: {out['tokens_per_s']} tok/s, {ms:.3f} ms per step, {gbs:.0f} GB/s, flags {flags}")
     del st, graph
     torch.cuda.empty_cache()

@@ -122,8 +122,6 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
         take(L.pos_of_pair, T * K * 4);
         take(L.act, E * 4);
         take(L.n_act, 4);
-        take(L.big, E * 4);
-        take(L.n_big, 4);
         take(L.mwork, (E + 1) * 4 * 4);
         take(L.n_mwork, 4);
         take(L.xdig, (size_t)T * (D * 3 / 4) * 4);
@@ -315,8 +313,6 @@ moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, in
     b.pos_of_pair = reinterpret_cast<int32_t *>(ws + L.pos_of_pair);
     b.act = reinterpret_cast<int32_t *>(ws + L.act);
     b.n_act = reinterpret_cast<int32_t *>(ws + L.n_act);
-    b.big = reinterpret_cast<int32_t *>(ws + L.big);
-    b.n_big = reinterpret_cast<int32_t *>(ws + L.n_big);
     b.mwork = reinterpret_cast<int32_t *>(ws + L.mwork);
     b.n_mwork = reinterpret_cast<int32_t *>(ws + L.n_mwork);
     b.xdig = reinterpret_cast<int *>(ws + L.xdig);

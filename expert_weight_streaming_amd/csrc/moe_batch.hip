@@ -12,16 +12,15 @@
 //                  softmax weights (one wave per token)
 //   k_group        the grouping: count[e], offset[e] (exclusive prefix
 //                  sum), the pair permutation perm[pos] = t*K + k sorted by
-//                  (expert, pair index), its inverse, and the list of active
-//                  experts
+//                  (expert, pair index), its inverse, the list of active
+//                  experts and the expert kernels' work list (expert, tile
+//                  of 16 of its tokens)
 //   k_digits       fixed-point digit tables of the tokens' activations
-//   k_gate_up_b    per active expert (and the shared expert, all tokens):
-//                  gate/up rows x that expert's tokens, SwiGLU -> h[pos]
-//                  (k_gate_up_m on the matrix cores for experts with 8+
-//                  tokens)
+//   k_expert_mm<0> per active expert (and the shared expert, all tokens):
+//                  gate/up rows x that expert's tokens on the matrix cores,
+//                  SwiGLU -> h[pos]
 //   k_digits       digit tables of h
-//   k_down_b       per active expert: down rows x its tokens' h -> y[pos]
-//                  (k_down_m for experts with 8+ tokens)
+//   k_expert_mm<1> per active expert: down rows x its positions' h -> y[pos]
 //   k_combine_b    per token, in slot order: sum_k w_k y[pos(t,k)] + the
 //                  shared expert's y, then (layer mode) residual + RMSNorm
 //
@@ -218,10 +217,9 @@ __device__ __forceinline__ void block_exscan3(int *v0, int *v1, int *v2, int n, 
 // One block of 1024 threads: the token -> expert grouping of the
 // selections: count[e], offset[e] (exclusive prefix sums), the pair
 // permutation perm[pos] = t*K + k sorted by (expert, pair index), its
-// inverse, the active experts in ascending order and, among them, those
-// with at least kMfmaMin tokens; and the matrix-core kernels' dense work
-// list: every (such expert, or the shared expert when T >= kMfmaMin; tile of
-// 16 of its tokens).
+// inverse, the active experts in ascending order; and the expert kernels'
+// dense work list: (item, tile of 16 of its tokens) for every active expert
+// in that order (item = its rank) and then the shared expert (item n_act).
 __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
 {
     const int tid = threadIdx.x;
@@ -230,9 +228,8 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     __shared__ int s_count[4096];
     __shared__ int s_off[4096];
     __shared__ int s_flag[4096];
-    __shared__ int s_big[4096];
+    __shared__ int s_nt[4096];
     __shared__ int wsum[16][3];
-    __shared__ int s_bigl[4096];
     for (int p = tid; p < P; p += 1024) s_idx[p] = a.topk_idx[p];
     for (int e = tid; e < E; e += 1024) s_count[e] = 0;
     __syncthreads();
@@ -245,33 +242,25 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     for (int e = tid; e < E; e += 1024) {
         s_off[e] = s_count[e];
         s_flag[e] = s_count[e] > 0;
-        s_big[e] = s_count[e] >= kMfmaMin;
+        s_nt[e] = (s_count[e] + 15) / 16;
         a.count[e] = s_count[e];
     }
     __syncthreads();
     int tot[3];
-    block_exscan3(s_off, s_flag, s_big, E, wsum, tot);
+    block_exscan3(s_off, s_flag, s_nt, E, wsum, tot);
     for (int e = tid; e < E; e += 1024) {
         a.offset[e] = s_off[e];
-        if (s_count[e]) a.act[s_flag[e]] = e;
-        if (s_count[e] >= kMfmaMin) {
-            a.big[s_big[e]] = e;
-            s_bigl[s_big[e]] = e;
+        if (s_count[e]) {
+            a.act[s_flag[e]] = e;
+            for (int tt = 0; 16 * tt < s_count[e]; ++tt) a.mwork[s_nt[e] + tt] = s_flag[e] << 2 | tt;
         }
     }
+    const bool shared = a.src.n_slots > K;
+    if (shared && tid < (T + 15) / 16) a.mwork[tot[2] + tid] = tot[1] << 2 | tid;
     if (tid == 0) {
         a.offset[E] = tot[0];
         *a.n_act = tot[1];
-        *a.n_big = tot[2];
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int w = 0;
-        for (int ii = 0; ii < tot[2]; ++ii)
-            for (int tt = 0; 16 * tt < s_count[s_bigl[ii]]; ++tt) a.mwork[w++] = ii << 2 | tt;
-        if (a.src.n_slots > K && T >= kMfmaMin)
-            for (int tt = 0; 16 * tt < T; ++tt) a.mwork[w++] = tot[2] << 2 | tt;
-        *a.n_mwork = w;
+        *a.n_mwork = tot[2] + (shared ? (T + 15) / 16 : 0);
     }
     for (int p = tid; p < P; p += 1024) {
         const int e = s_idx[p];
@@ -326,197 +315,9 @@ __device__ __forceinline__ Item item_of(const BatchArgs &a, int it, int nact)
     return r;
 }
 
-// Item ii of the matrix-core work list: expert big[ii], or the shared
-// expert for ii == n_big.
-__device__ __forceinline__ Item big_item_of(const BatchArgs &a, int ii, int nbig)
-{
-    Item r;
-    if (ii < nbig) {
-        const int e = a.big[ii];
-        r.blob = a.src.experts + (uint64_t)e * a.src.blob_bytes;
-        r.pos0 = a.offset[e];
-        r.n = a.count[e];
-        r.slot = 0;
-    } else {
-        r.blob = a.src.shared;
-        r.pos0 = a.T * a.K;
-        r.n = a.T;
-        r.slot = 1;
-    }
-    return r;
-}
-
 __device__ __forceinline__ int token_of(const BatchArgs &a, const Item &it, int j)
 {
     return it.slot ? j : a.perm[it.pos0 + j] / a.K;
-}
-
-// ---------------------------------------------------------------------------
-// Grouped gate/up: wave units of R intermediate rows of one item, applied to
-// every token of the item.
-template <int BITS, int CPL, int R>
-__global__ void __launch_bounds__(256) k_gate_up_b(BatchArgs a)
-{
-    using C = Codes<BITS>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int D = a.D, I = a.I;
-    const int nact = *a.n_act;
-    const int items = nact + (a.src.n_slots > a.src.top_k ? 1 : 0);
-    const int upi = (I + R - 1) / R;
-    const int nchunks = D * BITS / 128;
-    const int xdw = nchunks * C::DW, xcs = nchunks;
-    const uint64_t mat_q = (uint64_t)I * D * BITS / 8;
-    const uint64_t row_q = (uint64_t)D * BITS / 8;
-    const uint64_t sb0 = 3 * mat_q;
-    const uint64_t mat_sb = (uint64_t)I * (D / kGroup) * 4;
-    const int gpr = D / kGroup;
-    for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
-        const int ii = u / upi, i0 = (u - ii * upi) * R;
-        const Item it = item_of(a, ii, nact);
-        if (it.n >= kMfmaMin) continue;  // taken by the matrix-core kernel
-        uint4 q[CPL][R][2];
-        uint32_t sb[CPL][R][2];
-#pragma unroll
-        for (int m = 0; m < CPL; ++m)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int mat = 0; mat < 2; ++mat) {
-                    const int i = i0 + r, c = lane + 64 * m;
-                    const bool ok = i < I && c < nchunks;
-                    q[m][r][mat] = ok ? *reinterpret_cast<const uint4 *>(it.blob + mat * mat_q + (uint64_t)i * row_q +
-                                                                         (uint64_t)c * 16)
-                                      : make_uint4(0, 0, 0, 0);
-                    sb[m][r][mat] = ok ? *reinterpret_cast<const uint32_t *>(it.blob + sb0 + mat * mat_sb +
-                                                                             ((uint64_t)i * gpr + (uint64_t)c * C::CODES / kGroup) * 4)
-                                       : 0u;
-                }
-        for (int j = 0; j < it.n; ++j) {
-            const int t = token_of(a, it, j);
-            const float inv = a.xinv[t];
-            float acc[R][2];
-#pragma unroll
-            for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m) {
-                const int c = lane + 64 * m;
-                int dg[C::DW];
-                float cs = 0.f;
-                if (c < nchunks) {
-                    const int4 *src = reinterpret_cast<const int4 *>(a.xdig + (size_t)t * xdw + c * C::DW);
-#pragma unroll
-                    for (int v = 0; v < C::DW / 4; ++v) {
-                        const int4 w = src[v];
-                        dg[4 * v] = w.x;
-                        dg[4 * v + 1] = w.y;
-                        dg[4 * v + 2] = w.z;
-                        dg[4 * v + 3] = w.w;
-                    }
-                    cs = a.xcsum[(size_t)t * xcs + c];
-                } else {
-#pragma unroll
-                    for (int v = 0; v < C::DW; ++v) dg[v] = 0;
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int mat = 0; mat < 2; ++mat) {
-                        const float qx = qdot<BITS>(q[m][r][mat], dg);
-                        acc[r][mat] = fmaf(bf16_lo(sb[m][r][mat]) * inv, qx, acc[r][mat]);
-                        acc[r][mat] = fmaf(bf16_hi(sb[m][r][mat]), cs, acc[r][mat]);
-                    }
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float g = group_sum<64>(acc[r][0]);
-                const float uu = group_sum<64>(acc[r][1]);
-                const int i = i0 + r;
-                if (lane == 0 && i < I) a.h[(size_t)(it.pos0 + j) * I + i] = g / (1.f + expf(-g)) * uu;
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Grouped down: wave units of STEPS x (64/LPR) output rows of one item,
-// applied to every token of the item (digits of that token's h).
-template <int BITS, int LPR, int CPL, int STEPS>
-__global__ void __launch_bounds__(256) k_down_b(BatchArgs a)
-{
-    using C = Codes<BITS>;
-    constexpr int RPS = 64 / LPR;
-    constexpr int RW = RPS * STEPS;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int D = a.D, I = a.I;
-    const int nact = *a.n_act;
-    const int items = nact + (a.src.n_slots > a.src.top_k ? 1 : 0);
-    const int upi = (D + RW - 1) / RW;
-    const int nchunks = I * BITS / 128;
-    const int hdw = nchunks * C::DW;
-    const int sub = lane / LPR, lc = lane % LPR;
-    const uint64_t mat_q = (uint64_t)I * D * BITS / 8;
-    const uint64_t row_q = (uint64_t)I * BITS / 8;
-    const uint64_t sbd = 3 * mat_q + 2 * ((uint64_t)D * (I / kGroup) * 4);
-    const int gpr = I / kGroup;
-    for (int u = blockIdx.x * 4 + wave; u < items * upi; u += gridDim.x * 4) {
-        const int ii = u / upi, o0 = (u - ii * upi) * RW;
-        const Item it = item_of(a, ii, nact);
-        if (it.n >= kMfmaMin) continue;  // taken by the matrix-core kernel
-        uint4 q[CPL][STEPS];
-        uint32_t sb[CPL][STEPS];
-#pragma unroll
-        for (int m = 0; m < CPL; ++m)
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                const int o = o0 + s * RPS + sub, c = lc + LPR * m;
-                const bool ok = o < D && c < nchunks;
-                q[m][s] = ok ? *reinterpret_cast<const uint4 *>(it.blob + 2 * mat_q + (uint64_t)o * row_q + (uint64_t)c * 16)
-                             : make_uint4(0, 0, 0, 0);
-                sb[m][s] = ok ? *reinterpret_cast<const uint32_t *>(it.blob + sbd +
-                                                                    ((uint64_t)o * gpr + (uint64_t)c * C::CODES / kGroup) * 4)
-                              : 0u;
-            }
-        for (int j = 0; j < it.n; ++j) {
-            const int pos = it.pos0 + j;
-            const float inv = a.hinv[pos];
-            float t[STEPS];
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) t[s] = 0.f;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m) {
-                const int c = lc + LPR * m;
-                int dg[C::DW];
-                float cs = 0.f;
-                if (c < nchunks) {
-                    const int4 *src = reinterpret_cast<const int4 *>(a.hdig + (size_t)pos * hdw + c * C::DW);
-#pragma unroll
-                    for (int v = 0; v < C::DW / 4; ++v) {
-                        const int4 w = src[v];
-                        dg[4 * v] = w.x;
-                        dg[4 * v + 1] = w.y;
-                        dg[4 * v + 2] = w.z;
-                        dg[4 * v + 3] = w.w;
-                    }
-                    cs = a.hcsum[(size_t)pos * nchunks + c];
-                } else {
-#pragma unroll
-                    for (int v = 0; v < C::DW; ++v) dg[v] = 0;
-                }
-#pragma unroll
-                for (int s = 0; s < STEPS; ++s) {
-                    const float qh = qdot<BITS>(q[m][s], dg);
-                    t[s] = fmaf(bf16_lo(sb[m][s]) * inv, qh, t[s]);
-                    t[s] = fmaf(bf16_hi(sb[m][s]), cs, t[s]);
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                const float v = group_sum<LPR>(t[s]);
-                const int o = o0 + s * RPS + sub;
-                if (lc == 0 && o < D) a.y[(size_t)pos * D + o] = v;
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -594,32 +395,49 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core variants for experts with at least kMfmaMin tokens: the
-// expert's weights meet its tokens as a dense contraction.  One
-// v_mfma_i32_16x16x64_i8 multiplies a 16-row x 64-code tile of masked codes
-// (A, one code per byte) by the tokens' 64 x 16 digits of one plane (B):
-// exact int32 sums over one scale group, so the bf16 scale and bias of the
-// group apply to its three plane sums exactly as in the dot-product path.
-// Lane l supplies row (A) / token (B) l % 16 and the 16 codes of K-slice
-// l / 16; A and B list a slice's codes in the same order (the masked-word
-// order of the digit table), and the C tile arrives as rows 4 (l / 16) + r,
-// token l % 16.
+// Grouped expert contractions of a batch on the matrix cores, for every
+// item (each active routed expert, then the shared expert):
+//   MODE 0: the item's gate and up rows (I each) x the digit tables of its
+//           tokens' activations -> h[pos][i] = silu(g) * u
+//   MODE 1: its down rows (D) x the digit tables of its positions' h
+//           -> y[pos][o]
+// A block unit is one entry of the work list (item, tile of 16 of its
+// vectors) and one group of 64 WT rows; wave w takes WT tiles of 16 rows.
+// The contraction runs in stages of SG scale groups: the block loads a
+// stage's codes, scale words, digit words and group sums with coalesced
+// 16-byte loads into registers while it computes the previous stage from
+// LDS.  One v_mfma_i32_16x16x64_i8 per (plane, matrix, scale group) takes
+// the vectors' digit words of the plane as A (vector l % 16, K-slice l / 16)
+// and the group's masked codes as B (row l % 16), so C arrives as vectors
+// 4 (l / 16) + r, row l % 16 and a lane needs only its own row's scale and
+// bias word.  The three plane sums are exact int32; the group's bf16 scale
+// multiplies their fp32 combination, its bias the vectors' group sums, and
+// each vector's fixed-point step 2^-k applies once at the end.
 typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr int kGroupWords = 48;  // digit words per scale group (any bit width)
 
-// Masked codes of row `q` (the row's packed codes), scale group g, slice h.
+template <int BITS, int SG>
+struct MmShape {
+    static constexpr int GB = 16 * BITS / 2;                       // code bytes per row and scale group
+    static constexpr int ROWB = SG * GB + (BITS == 4 ? 32 : 16);   // LDS bytes per code row (padded)
+    static constexpr int DIGROW = SG * kGroupWords + 16;           // LDS words per vector (+16: 16 banks apart)
+};
+
+// A lane's 16 codes (K-slice h of scale group g) of an LDS code row, one per
+// byte, in the order of the digit table's words.
 template <int BITS>
-__device__ __forceinline__ v4i mfma_a(const uint8_t *q, int g, int h)
+__device__ __forceinline__ v4i codes_of(const uint8_t *row, int g, int h)
 {
     using C = Codes<BITS>;
     v4i r;
     if constexpr (BITS == 4) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(q + 32 * g + 8 * h);
+        const uint2 w = *reinterpret_cast<const uint2 *>(row + 32 * g + 8 * h);
         r[0] = (int)(w.x & C::MASK);
         r[1] = (int)((w.x >> 4) & C::MASK);
         r[2] = (int)(w.y & C::MASK);
         r[3] = (int)((w.y >> 4) & C::MASK);
     } else {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(q + 16 * g + 4 * h);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 16 * g + 4 * h);
         r[0] = (int)(w & C::MASK);
         r[1] = (int)((w >> 2) & C::MASK);
         r[2] = (int)((w >> 4) & C::MASK);
@@ -627,19 +445,18 @@ __device__ __forceinline__ v4i mfma_a(const uint8_t *q, int g, int h)
     }
     return r;
 }
-
-// Digit words of plane p matching mfma_a's slice h of group g, from a
-// vector's digit table.
+// Digit words of plane p matching codes_of's slice h of group g, from a
+// vector's digit words whose groups are kGroupWords apart.
 template <int BITS>
-__device__ __forceinline__ v4i mfma_b(const int *dig, int g, int h, int p)
+__device__ __forceinline__ v4i digits_of(const int *dig, int g, int h, int p)
 {
     using C = Codes<BITS>;
-    const int4 *src;
+    const int *src;
     if constexpr (BITS == 4)
-        src = reinterpret_cast<const int4 *>(dig + (2 * g + (h >> 1)) * C::DW + p * C::PW + 4 * (h & 1));
+        src = dig + g * kGroupWords + (h >> 1) * C::DW + p * C::PW + 4 * (h & 1);
     else
-        src = reinterpret_cast<const int4 *>(dig + g * C::DW + p * C::PW + 4 * h);
-    const int4 v = *src;
+        src = dig + g * kGroupWords + p * C::PW + 4 * h;
+    const int4 v = *reinterpret_cast<const int4 *>(src);
     v4i r;
     r[0] = v.x;
     r[1] = v.y;
@@ -648,177 +465,187 @@ __device__ __forceinline__ v4i mfma_b(const int *dig, int g, int h, int p)
     return r;
 }
 
-__device__ __forceinline__ float plane_sum(const v4i &c0, const v4i &c1, const v4i &c2, int r)
+template <int BITS, int MODE, int WT, int SG>
+__global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
 {
-    return fmaf((float)c2[r], 65536.f, fmaf((float)c1[r], 256.f, (float)c0[r]));
-}
-
-// One scale group's operands for a wave: the masked codes of M matrices'
-// rows (A), the digit words of the three planes (B), the lane's four output
-// rows' scale/bias words and the chunk sums of the group.
-template <int M>
-struct MfStage {
-    v4i a[M];
-    v4i b0, b1, b2;
-    uint32_t sb[M][4];
-    float gs;
-};
-
-template <int BITS, int M>
-__device__ __forceinline__ void mf_load(MfStage<M> &st, const uint8_t *const (&rowq)[M], const uint8_t *const (&sbr)[M],
-                                        uint32_t sb_stride, const int *dig, const float *cs, int g, int h)
-{
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        st.a[m] = mfma_a<BITS>(rowq[m], g, h);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.sb[m][r] = *reinterpret_cast<const uint32_t *>(sbr[m] + (size_t)r * sb_stride + 4 * g);
-    }
-    st.b0 = mfma_b<BITS>(dig, g, h, 0);
-    st.b1 = mfma_b<BITS>(dig, g, h, 1);
-    st.b2 = mfma_b<BITS>(dig, g, h, 2);
-    st.gs = BITS == 4 ? cs[2 * g] + cs[2 * g + 1] : cs[g];
-}
-
-template <int M>
-__device__ __forceinline__ void mf_step(const MfStage<M> &st, float inv, float (&acc)[M][4])
-{
-    const v4i z = {0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[m], st.b0, z, 0, 0, 0);
-        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[m], st.b1, z, 0, 0, 0);
-        const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[m], st.b2, z, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            acc[m][r] = fmaf(bf16_lo(st.sb[m][r]) * inv, plane_sum(c0, c1, c2, r), acc[m][r]);
-            acc[m][r] = fmaf(bf16_hi(st.sb[m][r]), st.gs, acc[m][r]);
+    using C = Codes<BITS>;
+    using S = MmShape<BITS, SG>;
+    static_assert(C::DW * (kGroup / C::CODES) == kGroupWords, "a scale group's digit words");
+    constexpr int M = MODE == 0 ? 2 : 1;
+    constexpr int UR = 64 * WT;                               // rows per unit
+    constexpr int CQ = UR * SG * S::GB / 16 / 256;            // code int4 per thread, matrix and stage
+    constexpr int SQ = UR * SG / 256;                         // scale words per thread, matrix and stage
+    constexpr int DQ = 16 * SG * kGroupWords / 4 / 256;       // digit int4 per thread and stage
+    static_assert(CQ >= 1 && SQ >= 1 && DQ >= 1 && 16 * SG <= 256, "stage split over 256 threads");
+    static_assert(UR * SG * S::GB % (16 * 256) == 0 && UR * SG % 256 == 0 && 16 * SG * kGroupWords % 1024 == 0,
+                  "whole stage loads per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, h = lane >> 4;
+    const int D = a.D, I = a.I;
+    const int rows = MODE == 0 ? I : D, klen = MODE == 0 ? D : I;
+    const int ng = klen / kGroup, nch = klen / C::CODES;
+    const int rgroups = (rows + UR - 1) / UR, nst = (ng + SG - 1) / SG;
+    const int nact = *a.n_act, nunits = *a.n_mwork * rgroups;
+    const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)klen * BITS / 8;
+    const uint64_t sb0 = 3 * mat_q + (MODE == 0 ? 0 : 2 * (uint64_t)I * (D / kGroup) * 4);
+    const uint64_t mat_sb = (uint64_t)rows * ng * 4;
+    const int *dsrc = MODE == 0 ? a.xdig : a.hdig;
+    const float *csrc = MODE == 0 ? a.xcsum : a.hcsum;
+    const float *isrc = MODE == 0 ? a.xinv : a.hinv;
+    __shared__ __align__(16) uint8_t s_code[M][UR][S::ROWB];
+    __shared__ uint32_t s_sw[M][SG][UR];               // scale words [group][row]
+    __shared__ __align__(16) int s_dig[16][S::DIGROW];
+    __shared__ __align__(16) float s_gs[SG][16];       // group sums [group][vector]
+    __shared__ int s_vec[16];                          // the tile's vectors (token or position), -1 past n
+    for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+        const int wk = a.mwork[u / rgroups];
+        const Item it = item_of(a, wk >> 2, nact);
+        const int j0 = (wk & 3) * 16, row0 = (u % rgroups) * UR;
+        __syncthreads();  // the previous unit's readers of LDS are done
+        if (tid < 16) {
+            const int j = j0 + tid;
+            s_vec[tid] = j < it.n ? (MODE == 0 ? token_of(a, it, j) : it.pos0 + j) : -1;
         }
-    }
-}
-
-// A wave's share of the contraction of one 16-row tile (M matrices) with
-// one 16-vector tile: scale groups g0, g0 + gs, ... below ng, in batches of
-// NB groups whose loads are all issued before the batch's arithmetic.
-template <int BITS, int M, int NB>
-__device__ __forceinline__ void mf_tile(const uint8_t *const (&rowq)[M], const uint8_t *const (&sbr)[M], uint32_t sb_stride,
-                                        const int *dig, const float *cs, float inv, int g0, int gs, int ng, int h,
-                                        float (&acc)[M][4])
-{
+        __syncthreads();
+        // one stage's loads into registers (clamped rows, groups and
+        // vectors: every load is in bounds); what lies past ng or past the
+        // tile's vectors is zeroed when the stage is stored, after the data
+        // has arrived (a select on a load's registers would wait for it)
+        uint4 rq[M][CQ];
+        uint32_t rw[M][SQ];
+        int4 rd[DQ];
+        float rg = 0.f;
+        auto load = [&](int g0) {
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+            for (int m = 0; m < M; ++m) {
+                const uint8_t *mq = it.blob + (uint64_t)(MODE == 0 ? m : 2) * mat_q;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[m][r] = 0.f;
-    for (int gb = g0; gb < ng; gb += NB * gs) {
-        MfStage<M> st[NB];
+                for (int c = 0; c < CQ; ++c) {
+                    const int f = tid + 256 * c, row = f / (SG * S::GB / 16);
+                    const int b16 = f - row * (SG * S::GB / 16);
+                    const int g = g0 + b16 * 16 / S::GB;
+                    const uint64_t rr = row0 + row < rows ? row0 + row : rows - 1;
+                    const uint64_t off = (uint64_t)(g < ng ? g : ng - 1) * S::GB + (uint64_t)(b16 * 16) % S::GB;
+                    rq[m][c] = *reinterpret_cast<const uint4 *>(mq + rr * row_q + off);
+                }
+                const uint8_t *ms = it.blob + sb0 + (uint64_t)m * mat_sb;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (gb + b * gs < ng) mf_load<BITS, M>(st[b], rowq, sbr, sb_stride, dig, cs, gb + b * gs, h);
+                for (int c = 0; c < SQ; ++c) {
+                    const int f = tid + 256 * c, row = f / SG, g = g0 + (f - row * SG);
+                    const uint64_t rr = row0 + row < rows ? row0 + row : rows - 1;
+                    rw[m][c] = *reinterpret_cast<const uint32_t *>(ms + (rr * ng + (g < ng ? g : ng - 1)) * 4);
+                }
+            }
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (gb + b * gs < ng) mf_step<M>(st[b], inv, acc);
-    }
-}
-
-// The partial tiles of the block's KS waves, added in wave order into wave
-// 0's lanes.
-template <int M, int KS>
-__device__ __forceinline__ void mf_reduce(float (&acc)[M][4], float (*part)[M][64][4])
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (wave > 0) {
+            for (int c = 0; c < DQ; ++c) {
+                const int f = tid + 256 * c, t = f / (SG * kGroupWords / 4);
+                const int rem = f - t * (SG * kGroupWords / 4), gl = rem / (kGroupWords / 4);
+                const int w4 = rem - gl * (kGroupWords / 4), g = g0 + gl, vec = s_vec[t];
+                const int vc = vec >= 0 ? vec : 0, gc = g < ng ? g : ng - 1;
+                rd[c] = *reinterpret_cast<const int4 *>(dsrc + (size_t)vc * nch * C::DW + gc * kGroupWords + 4 * w4);
+            }
+            {
+                const int tt = tid & (16 * SG - 1);
+                const int t = tt / SG, gl = tt - t * SG, g = g0 + gl, vec = s_vec[t];
+                const int vc = vec >= 0 ? vec : 0, gc = g < ng ? g : ng - 1;
+                const float *cs = csrc + (size_t)vc * nch;
+                rg = BITS == 4 ? cs[2 * gc] + cs[2 * gc + 1] : cs[gc];
+            }
+        };
+        auto store = [&](int g0) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+#pragma unroll
+                for (int c = 0; c < CQ; ++c) {
+                    const int f = tid + 256 * c, row = f / (SG * S::GB / 16);
+                    const int b16 = f - row * (SG * S::GB / 16);
+                    const bool ok = g0 + b16 * 16 / S::GB < ng;
+                    *reinterpret_cast<uint4 *>(&s_code[m][row][16 * b16]) = ok ? rq[m][c] : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int c = 0; c < SQ; ++c) {
+                    const int f = tid + 256 * c, row = f / SG, gl = f - row * SG;
+                    s_sw[m][gl][row] = g0 + gl < ng ? rw[m][c] : 0u;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < DQ; ++c) {
+                const int f = tid + 256 * c, t = f / (SG * kGroupWords / 4);
+                const int rem = f - t * (SG * kGroupWords / 4), gl = rem / (kGroupWords / 4);
+                const bool ok = s_vec[t] >= 0 && g0 + gl < ng;
+                *reinterpret_cast<int4 *>(&s_dig[t][4 * rem]) = ok ? rd[c] : make_int4(0, 0, 0, 0);
+            }
+            if (tid < 16 * SG) {
+                const int t = tid / SG, gl = tid - t * SG;
+                s_gs[gl][t] = s_vec[t] >= 0 && g0 + gl < ng ? rg : 0.f;
+            }
+        };
+        float acs[M][WT][4], acb[M][WT][4];
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[wave - 1][m][lane][r] = acc[m][r];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        for (int w = 0; w < KS - 1; ++w)
+            for (int wt = 0; wt < WT; ++wt)
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+                for (int r = 0; r < 4; ++r) acs[m][wt][r] = acb[m][wt][r] = 0.f;
+        load(0);
+        store(0);
+        __syncthreads();
+        const int wrow0 = 16 * WT * wave + r16;  // the lane's row in the unit, tile 0
+        for (int st = 0; st < nst; ++st) {
+            const int g0 = st * SG;
+            if (st + 1 < nst) load(g0 + SG);  // in flight while this stage is computed
+            const int gn = ng - g0 < SG ? ng - g0 : SG;
+            for (int gl = 0; gl < gn; ++gl) {
+                v4i da[3];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[m][r] += part[w][m][lane][r];
-    }
-    __syncthreads();
-}
-
-constexpr int kMfWaves = 8;  // waves per matrix-core block (scale groups split over them)
-
-// Gate/up: a block unit is one 16-row tile of an item's gate and up
-// matrices x one tile of 16 of its tokens; the block's kMfWaves waves take
-// every kMfWaves-th scale group and their partial sums meet in LDS.
-template <int BITS>
-__global__ void __launch_bounds__(64 * kMfWaves) k_gate_up_m(BatchArgs a)
-{
-    using C = Codes<BITS>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, h = lane >> 4;
-    const int D = a.D, I = a.I;
-    const int nbig = *a.n_big, nwork = *a.n_mwork;
-    const int rtiles = I / 16;  // I is a multiple of 64
-    const int ng = D / kGroup, nchunks = D * BITS / 128;
-    const int xdw = nchunks * C::DW;
-    const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)D * BITS / 8;
-    const uint64_t sb0 = 3 * mat_q, mat_sb = (uint64_t)I * ng * 4;
-    __shared__ float part[kMfWaves - 1][2][64][4];
-    for (int u = blockIdx.x; u < nwork * rtiles; u += gridDim.x) {
-        const int wk = a.mwork[u / rtiles], ii = wk >> 2;
-        const int i0 = (u % rtiles) * 16, j0 = (wk & 3) * 16;
-        const Item it = big_item_of(a, ii, nbig);
-        const int jt = j0 + r16;
-        const bool tok_ok = jt < it.n;
-        const int tok = token_of(a, it, tok_ok ? jt : j0);
-        const uint8_t *const rowq[2] = {it.blob + (uint64_t)(i0 + r16) * row_q, it.blob + mat_q + (uint64_t)(i0 + r16) * row_q};
-        const uint8_t *const sbr[2] = {it.blob + sb0 + (uint64_t)(i0 + 4 * h) * ng * 4,
-                                       it.blob + sb0 + mat_sb + (uint64_t)(i0 + 4 * h) * ng * 4};
-        float acc[2][4];
-        mf_tile<BITS, 2, 2>(rowq, sbr, ng * 4, a.xdig + (size_t)tok * xdw, a.xcsum + (size_t)tok * nchunks, a.xinv[tok], wave,
-                            kMfWaves, ng, h, acc);
-        mf_reduce<2, kMfWaves>(acc, part);
-        if (wave == 0 && tok_ok) {
+                for (int p = 0; p < 3; ++p) da[p] = digits_of<BITS>(&s_dig[r16][0], gl, h, p);
+                const float4 gs = *reinterpret_cast<const float4 *>(&s_gs[gl][4 * h]);
+                const float gv[4] = {gs.x, gs.y, gs.z, gs.w};
+                const v4i z = {0, 0, 0, 0};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float gg = acc[0][r], uu = acc[1][r];
-                a.h[(size_t)(it.pos0 + jt) * I + i0 + 4 * h + r] = gg / (1.f + expf(-gg)) * uu;
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int wt = 0; wt < WT; ++wt) {
+                        const int wr = wrow0 + 16 * wt;
+                        const v4i bq = codes_of<BITS>(&s_code[m][wr][0], gl, h);
+                        const uint32_t w = s_sw[m][gl][wr];
+                        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[0], bq, z, 0, 0, 0);
+                        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[1], bq, z, 0, 0, 0);
+                        const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[2], bq, z, 0, 0, 0);
+                        const float sc = bf16_lo(w), bi = bf16_hi(w);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            // (c0 + 256 c1) is exact in int32 and rounds once to fp32, as the
+                            // one-token path's fma(c1, 256, c0) does
+                            const float ps = fmaf((float)c2[r], 65536.f, (float)(c0[r] + (c1[r] << 8)));
+                            acs[m][wt][r] = fmaf(sc, ps, acs[m][wt][r]);
+                            acb[m][wt][r] = fmaf(bi, gv[r], acb[m][wt][r]);
+                        }
+                    }
+            }
+            if (st + 1 < nst) {
+                __syncthreads();  // every wave is done with this stage
+                store(g0 + SG);
+                __syncthreads();
             }
         }
-    }
-}
-
-// Down: a block unit is one 16-row tile of an item's down matrix x one tile
-// of 16 of its positions (digit tables of h), scale groups split over the
-// waves as above.
-template <int BITS>
-__global__ void __launch_bounds__(64 * kMfWaves) k_down_m(BatchArgs a)
-{
-    using C = Codes<BITS>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, h = lane >> 4;
-    const int D = a.D, I = a.I;
-    const int nbig = *a.n_big, nwork = *a.n_mwork;
-    const int rtiles = D / 16;  // D is a multiple of 64
-    const int ng = I / kGroup, nchunks = I * BITS / 128;
-    const int hdw = nchunks * C::DW;
-    const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)I * BITS / 8;
-    const uint64_t sbd = 3 * mat_q + 2 * ((uint64_t)D * ng * 4);
-    __shared__ float part[kMfWaves - 1][1][64][4];
-    for (int u = blockIdx.x; u < nwork * rtiles; u += gridDim.x) {
-        const int wk = a.mwork[u / rtiles], ii = wk >> 2;
-        const int o0 = (u % rtiles) * 16, j0 = (wk & 3) * 16;
-        const Item it = big_item_of(a, ii, nbig);
-        const int jt = j0 + r16;
-        const bool ok = jt < it.n;
-        const int pos = it.pos0 + (ok ? jt : j0);
-        const uint8_t *const rowq[1] = {it.blob + 2 * mat_q + (uint64_t)(o0 + r16) * row_q};
-        const uint8_t *const sbr[1] = {it.blob + sbd + (uint64_t)(o0 + 4 * h) * ng * 4};
-        float acc[1][4];
-        mf_tile<BITS, 1, 8>(rowq, sbr, ng * 4, a.hdig + (size_t)pos * hdw, a.hcsum + (size_t)pos * nchunks, a.hinv[pos], wave,
-                            kMfWaves, ng, h, acc);
-        mf_reduce<1, kMfWaves>(acc, part);
-        if (wave == 0 && ok) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a.y[(size_t)(it.pos0 + jt) * D + o0 + 4 * h + r] = acc[0][r];
+        for (int wt = 0; wt < WT; ++wt) {
+            const int row = row0 + wrow0 + 16 * wt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * h + r, vec = s_vec[t];
+                if (vec < 0 || row >= rows) continue;
+                const float inv = isrc[vec];
+                const size_t pos = (size_t)it.pos0 + j0 + t;
+                if constexpr (MODE == 0) {
+                    const float g = fmaf(acs[0][wt][r], inv, acb[0][wt][r]);
+                    const float uu = fmaf(acs[1][wt][r], inv, acb[1][wt][r]);
+                    a.h[pos * I + row] = g / (1.f + expf(-g)) * uu;
+                } else {
+                    a.y[pos * D + row] = fmaf(acs[0][wt][r], inv, acb[0][wt][r]);
+                }
+            }
         }
     }
 }
@@ -829,52 +656,21 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 {
     using C = Codes<BITS>;
     const int nchunks_d = a.D * BITS / 128, nchunks_i = a.I * BITS / 128;
-    const int cpl = (nchunks_d + 63) / 64;
-    const DownShape d = down_shape(a.I, BITS);
     switch (stage) {
     case 0:  // x digits
         hipLaunchKernelGGL(k_digits<BITS>, dim3(a.T), dim3(256), 0, s, a.x, a.D, a.xdig, a.xcsum, a.xinv,
                            nchunks_d * C::DW, nchunks_d);
         break;
-    case 1: {  // gate/up
-        constexpr int R = 4;
-        if (cpl <= 1) hipLaunchKernelGGL((k_gate_up_b<BITS, 1, R>), dim3(1024), dim3(256), 0, s, a);
-        else if constexpr (BITS == 4) {
-            if (cpl <= 2) hipLaunchKernelGGL((k_gate_up_b<BITS, 2, 2>), dim3(1024), dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_gate_up_b<BITS, 4, 1>), dim3(1024), dim3(256), 0, s, a);
-        } else {
-            hipLaunchKernelGGL((k_gate_up_b<BITS, 2, 4>), dim3(1024), dim3(256), 0, s, a);
-        }
-        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_gate_up_m<BITS>), dim3(1024), dim3(64 * kMfWaves), 0, s, a);
+    case 1:  // gate/up: 64-row units, 8 scale groups per stage
+        hipLaunchKernelGGL((k_expert_mm<BITS, 0, 1, 8>), dim3(2048), dim3(256), 0, s, a);
         break;
-    }
     case 2:  // h digits (all positions)
         hipLaunchKernelGGL(k_digits<BITS>, dim3(a.T * a.src.n_slots), dim3(256), 0, s, a.h, a.I, a.hdig, a.hcsum,
                            a.hinv, nchunks_i * C::DW, nchunks_i);
         break;
-    case 3: {  // down
-#define MOE_DB(LPR_)                                                                                         \
-    case LPR_:                                                                                               \
-        if (d.cpl <= 1)                                                                                      \
-            hipLaunchKernelGGL((k_down_b<BITS, LPR_, 1, ((4 * LPR_ / 64) < 1 ? 1 : 4 * LPR_ / 64)>), dim3(1024), \
-                               dim3(256), 0, s, a);                                                          \
-        else                                                                                                 \
-            hipLaunchKernelGGL((k_down_b<BITS, LPR_, 2, ((4 * LPR_ / 64) < 1 ? 1 : 4 * LPR_ / 64)>), dim3(1024), \
-                               dim3(256), 0, s, a);                                                          \
+    case 3:  // down: 128-row units (the digit tables of h shared by more rows)
+        hipLaunchKernelGGL((k_expert_mm<BITS, 1, 2, (BITS == 4 ? 4 : 8)>), dim3(2048), dim3(256), 0, s, a);
         break;
-        switch (d.lpr) {
-            MOE_DB(1)
-            MOE_DB(2)
-            MOE_DB(4)
-            MOE_DB(8)
-            MOE_DB(16)
-            MOE_DB(32)
-            MOE_DB(64)
-        }
-#undef MOE_DB
-        if (a.T >= kMfmaMin) hipLaunchKernelGGL((k_down_m<BITS>), dim3(1024), dim3(64 * kMfWaves), 0, s, a);
-        break;
-    }
     }
     return hipGetLastError();
 }

@@ -15,7 +15,6 @@ constexpr int kMaxLayerBlocks = 1024;    // grid cap of the persistent stack ker
 constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
 // In a batch, experts with at least this many tokens take the matrix-core
 // grouped kernels, the others the dot-product ones.
-constexpr int kMfmaMin = 8;
 constexpr int kRouteSplit = 4;  // hidden-dimension slices of the batched router (partial logits)
 
 // Workspace layout (byte offsets), all 64-byte aligned.
@@ -36,8 +35,8 @@ struct WsLayout {
     size_t tss = 0;          // [kMaxLayerBlocks] per-block sums of squares
     // batches (T > 1)
     size_t lpart = 0;        // float [kRouteSplit][T][E] partial logits
-    size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0, big = 0, n_big = 0;
-    size_t mwork = 0, n_mwork = 0;  // matrix-core work list: (item << 2 | 16-token tile), its length
+    size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0;
+    size_t mwork = 0, n_mwork = 0;  // expert-kernel work list: (item << 2 | 16-token tile), its length
     size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
     size_t total = 0;
 };
@@ -113,10 +112,8 @@ struct BatchArgs {
     int32_t *pos_of_pair;    // [T*K] pair index -> position (-1: invalid id)
     int32_t *act;            // [E] active experts, ascending
     int32_t *n_act;          // [1]
-    int32_t *big;            // [E] experts with at least kMfmaMin tokens, ascending
-    int32_t *n_big;          // [1]
-    int32_t *mwork;          // [(E+1)*4] matrix-core work: item ii (big[ii], or the shared expert for
-                             // ii == n_big) << 2 | tile of 16 of its tokens
+    int32_t *mwork;          // [(E+1)*4] expert-kernel work: item ii (act[ii], or the shared expert for
+                             // ii == n_act) << 2 | tile of 16 of its tokens
     int32_t *n_mwork;        // [1]
     int *xdig;               // [T][D/chunk][DW] digit tables of x
     float *xcsum;            // [T][D/chunk]

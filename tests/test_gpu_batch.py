@@ -134,13 +134,13 @@ def test_batched_expert_forward_forced_and_batch_equals_singles():
 
 @pytest.mark.parametrize("bits", [4, 2])
 def test_batched_matrix_core_path_hidden4096(bits):
-    """Hidden 4096, inter 1024, 32 experts, 48 skewed tokens: most selected
-    experts receive 8+ tokens (the matrix-core grouped kernels), a few fewer
-    (the dot-product kernels); every token against the oracle and against
-    the same token run alone."""
+    """Hidden 4096, inter 1024, 32 experts, 48 skewed tokens: some selected
+    experts receive 8+ tokens (more than one 16-token tile of the grouped
+    matrix-core kernels when over 16), a few fewer (one partly filled tile);
+    every token against the oracle and against the same token run alone."""
     cfg = CFG["layer"].replace(E=32, bits=bits, seed=0x5EED00F0 + bits)
     T = 48
-    print(f"[gpu case] matrix-core batch bits={bits}", flush=True)
+    print(f"[gpu case] hidden-4096 batch bits={bits}", flush=True)
     base = seedgen.activation(cfg, 0)
     x = (base[None, :] + 0.35 * seedgen.activations(cfg, 1, T)).astype(np.float32)
     st = W.build_stack(cfg, layers=1, T=T)

@@ -46,6 +46,8 @@ def _run_batch(cfg, T, token0=0, r_scale=None):
     ("ragged_T5_k3", seedgen.Config("rg", D=320, E=24, K=3, I=192, bits=4, router_sigma=0.05, seed=0x5EED00E2), 5),
     ("k8_T64", CFG["tiny"].replace(E=64, K=8, seed=0x5EED00E3), 64),
     ("noshared_T4", CFG["tiny"].replace(n_shared=0, seed=0x5EED00E4), 4),
+    ("wide_T20", CFG["tiny"].replace(D=8192, I=64, E=8, K=2, seed=0x5EED00E5), 20),
+    ("deep_inter_T6", CFG["tiny"].replace(D=128, I=4096, E=8, K=2, bits=2, seed=0x5EED00E6), 6),
 ])
 def test_batched_layer_step(name, cfg, T):
     print(f"[gpu case] batched layer {name}", flush=True)

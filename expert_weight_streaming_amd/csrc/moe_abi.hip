@@ -110,7 +110,7 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
     if (T > 1) {
         const size_t E = d->n_experts, K = d->top_k, D = d->hidden, I = d->inter;
         const size_t P = (size_t)T * (K + d->n_shared);
-        const size_t cw = 128 / d->bits;  // activations per 16-byte chunk
+        const size_t G = moe::kGroup;  // activations per scale group
         auto take = [&](size_t &field, size_t bytes) {
             field = off;
             off = round_up(off + bytes, 256);
@@ -125,12 +125,11 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
         take(L.mwork, (E + 1) * 4 * 4);
         take(L.n_mwork, 4);
         take(L.xdig, (size_t)T * (D * 3 / 4) * 4);
-        take(L.xcsum, (size_t)T * (D / cw) * 4);
-        take(L.xinv, (size_t)T * 4);
-        take(L.hb, P * I * 4);
+        take(L.xcsum, (size_t)T * (D / G) * 4);
+        take(L.xinv, (size_t)T * (D / G) * 4);
         take(L.hdig, P * (I * 3 / 4) * 4);
-        take(L.hcsum, P * (I / cw) * 4);
-        take(L.hinv, P * 4);
+        take(L.hcsum, P * (I / G) * 4);
+        take(L.hinv, P * (I / G) * 4);
         take(L.y, P * D * 4);
     }
     L.total = off;
@@ -318,7 +317,6 @@ moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, in
     b.xdig = reinterpret_cast<int *>(ws + L.xdig);
     b.xcsum = reinterpret_cast<float *>(ws + L.xcsum);
     b.xinv = reinterpret_cast<float *>(ws + L.xinv);
-    b.h = reinterpret_cast<float *>(ws + L.hb);
     b.hdig = reinterpret_cast<int *>(ws + L.hdig);
     b.hcsum = reinterpret_cast<float *>(ws + L.hcsum);
     b.hinv = reinterpret_cast<float *>(ws + L.hinv);
@@ -375,7 +373,7 @@ int moe_route(const moe_layer_desc *desc, const float *x, int32_t n_tokens, int3
     const moe::WsLayout L = layout(desc, n_tokens);
     if (n_tokens > 1) {
         const moe::BatchArgs b = batch_args(desc, n_tokens, x, topk_idx, topk_w, logits, (uint8_t *)workspace, L);
-        hipError_t e = moe::launch_batch_route(b, 1, (hipStream_t)stream);
+        hipError_t e = moe::launch_batch_route(b, 1, desc->bits, (hipStream_t)stream);
         return e == hipSuccess ? MOE_OK : hip_fail(e, "batched route launch");
     }
     return enqueue_route(desc, x, topk_idx, topk_w, logits, (uint8_t *)workspace, L, (hipStream_t)stream);
@@ -396,7 +394,7 @@ int moe_expert_forward(const moe_layer_desc *desc, const float *x, int32_t n_tok
                                       nullptr, (uint8_t *)workspace, L);
         b.yout = y;
         b.mode = 0;
-        hipError_t e = moe::launch_batch_route(b, 0, (hipStream_t)stream);
+        hipError_t e = moe::launch_batch_route(b, 0, desc->bits, (hipStream_t)stream);
         if (e == hipSuccess) e = moe::launch_batch_experts(b, desc->bits, (hipStream_t)stream);
         return e == hipSuccess ? MOE_OK : hip_fail(e, "batched expert launch");
     }
@@ -422,7 +420,7 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
         b.resid = resid;
         b.xout = x;
         b.mode = 1;
-        hipError_t e = moe::launch_batch_route(b, 1, (hipStream_t)stream);
+        hipError_t e = moe::launch_batch_route(b, 1, desc->bits, (hipStream_t)stream);
         if (e == hipSuccess) e = moe::launch_batch_experts(b, desc->bits, (hipStream_t)stream);
         return e == hipSuccess ? MOE_OK : hip_fail(e, "batched layer launch");
     }

@@ -7,7 +7,9 @@
 // of that expert's tokens:
 //
 //   k_route_m      partial logits of every token over kRouteSplit slices of
-//                  the hidden dimension (fp32 matrix cores)
+//                  the hidden dimension (fp32 matrix cores), and the
+//                  tokens' activations as digit words, one fixed-point step
+//                  per scale group (k_xdigits alone when routing is given)
 //   k_topk_b       the logits (slices added in order), per-token top-K and
 //                  softmax weights (one wave per token)
 //   k_group        the grouping: count[e], offset[e] (exclusive prefix
@@ -15,11 +17,9 @@
 //                  (expert, pair index), its inverse, the list of active
 //                  experts and the expert kernels' work list (expert, tile
 //                  of 16 of its tokens)
-//   k_digits       fixed-point digit tables of the tokens' activations
 //   k_expert_mm<0> per active expert (and the shared expert, all tokens):
 //                  gate/up rows x that expert's tokens on the matrix cores,
-//                  SwiGLU -> h[pos]
-//   k_digits       digit tables of h
+//                  SwiGLU -> h[pos] as digit words, one step per scale group
 //   k_expert_mm<1> per active expert: down rows x its positions' h -> y[pos]
 //   k_combine_b    per token, in slot order: sum_k w_k y[pos(t,k)] + the
 //                  shared expert's y, then (layer mode) residual + RMSNorm
@@ -33,6 +33,62 @@ namespace {
 using namespace dev;
 
 // ---------------------------------------------------------------------------
+// Digit words of activations, one fixed-point step per (vector, scale group
+// of 64 values): the rule of a whole-vector table (largest magnitude times
+// 2^k below 2^22) applied to each group's own range.  The 16 lanes of a DPP
+// row convert one group: lane q takes the four values that share digit word
+// (code word q / SUBS, sub q % SUBS) of each plane.  A group's words are
+// kGroupWords consecutive ints (its chunks' digit words, plane-major within
+// a chunk), so a vector's groups are kGroupWords apart.
+constexpr int kGroupWords = 48;  // digit words per scale group (any bit width)
+
+template <int BITS>
+__device__ __forceinline__ int group_value(int q, int j)
+{
+    using C = Codes<BITS>;
+    return (q / C::SUBS) * C::PER_WORD + q % C::SUBS + C::SUBS * j;
+}
+
+// v: lane q's four values (group_value(q, 0..3)); dig: the group's words;
+// lane 0 writes the group's sum of values and its step 2^-k.
+template <int BITS>
+__device__ __forceinline__ void group_digits(const float v[4], int q, int *dig, float *gsum, float *ginv)
+{
+    using C = Codes<BITS>;
+    static_assert(C::DW * (kGroup / C::CODES) == kGroupWords && kGroup / 4 == 16, "16 lanes per scale group");
+    const float mx = group_max<16>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    const float sm = group_sum<16>((v[0] + v[1]) + (v[2] + v[3]));
+    float mul, inv;
+    fixed_scale(mx, mul, inv);
+    int w0, w1, w2;
+    digit_words(v[0], v[1], v[2], v[3], mul, w0, w1, w2);
+    const int kb = q / C::SUBS;
+    int *o = dig + (kb / 4) * C::DW + (kb % 4) * C::SUBS + q % C::SUBS;
+    o[0] = w0;
+    o[C::PW] = w1;
+    o[2 * C::PW] = w2;
+    if (q == 0) {
+        *gsum = sm;
+        *ginv = inv;
+    }
+}
+
+// Scale group g of the activations of tokens t0 + 4 wave + lane / 16 (each
+// DPP row one token) -> xdig / xcsum / xinv.
+template <int BITS>
+__device__ __forceinline__ void x_group_digits(const BatchArgs &a, int t0, int g, int lane, int wave)
+{
+    const int t = t0 + 4 * wave + (lane >> 4), q = lane & 15, ng = a.D / kGroup;
+    if (t >= a.T) return;  // whole DPP rows drop out
+    const float *xs = a.x + (size_t)t * a.D + g * kGroup;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = xs[group_value<BITS>(q, j)];
+    const size_t tg = (size_t)t * ng + g;
+    group_digits<BITS>(v, q, a.xdig + tg * kGroupWords, a.xcsum + tg, a.xinv + tg);
+}
+
+// ---------------------------------------------------------------------------
 // Router for T tokens on the matrix cores (fp32): a block owns a tile of 16
 // router rows x 16 tokens over one slice of the hidden dimension (slices
 // spread the router's bytes over enough CUs); its four waves take every
@@ -41,7 +97,11 @@ using namespace dev;
 // v_mfma_f32_16x16x4f32: lane l supplies row (A) / token (B) l % 16 at
 // k = l / 16; each lane loads 4 consecutive columns, so 4 instructions
 // cover 16 columns (A and B use the same column-to-instruction map).
+// The blocks of a (slice, token tile) also convert the slice's scale groups
+// of those tokens' activations to digit words, row tile r taking groups r,
+// r + row tiles, ...
 typedef float v4f __attribute__((ext_vector_type(4)));
+template <int BITS>
 __global__ void __launch_bounds__(256) k_route_m(BatchArgs a, int splits)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -85,6 +145,17 @@ __global__ void __launch_bounds__(256) k_route_m(BatchArgs a, int splits)
             if (e < E && t < T) out[(size_t)t * E + e] = v;
         }
     }
+    const int gps = D / splits / kGroup;
+    for (int gi = rem / ttiles; gi < gps; gi += rtiles) x_group_digits<BITS>(a, t0, sl * gps + gi, lane, wave);
+}
+
+// The activations' digit words alone (routing given by the caller): block
+// b converts scale group b % groups of token tile b / groups.
+template <int BITS>
+__global__ void __launch_bounds__(256) k_xdigits(BatchArgs a)
+{
+    const int ng = a.D / kGroup;
+    x_group_digits<BITS>(a, (blockIdx.x / ng) * 16, blockIdx.x % ng, threadIdx.x & 63, threadIdx.x >> 6);
 }
 
 // Hidden-dimension slices of the batched router: kRouteSplit when the
@@ -276,19 +347,6 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Digit tables of n vectors of length len (one block per vector).
-template <int BITS>
-__global__ void __launch_bounds__(256) k_digits(const float *v, int len, int *dig, float *csum, float *inv, int dig_stride,
-                                                 int csum_stride)
-{
-    __shared__ float red[16];
-    const int b = blockIdx.x;
-    const float r = block_digit_table<BITS>(v + (size_t)b * len, len, dig + (size_t)b * dig_stride,
-                                            csum + (size_t)b * csum_stride, red);
-    if (threadIdx.x == 0) inv[b] = r;
-}
-
 // Tokens of active item a: routed expert act[a] (positions offset..+count),
 // or, for a == n_act, the shared expert (positions T*K .. T*K+T-1, token j).
 struct Item {
@@ -397,24 +455,25 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
 // ---------------------------------------------------------------------------
 // Grouped expert contractions of a batch on the matrix cores, for every
 // item (each active routed expert, then the shared expert):
-//   MODE 0: the item's gate and up rows (I each) x the digit tables of its
-//           tokens' activations -> h[pos][i] = silu(g) * u
-//   MODE 1: its down rows (D) x the digit tables of its positions' h
+//   MODE 0: the item's gate and up rows (I each) x the digit words of its
+//           tokens' activations -> h[pos][i] = silu(g) * u, as digit words
+//   MODE 1: its down rows (D) x the digit words of its positions' h
 //           -> y[pos][o]
 // A block unit is one entry of the work list (item, tile of 16 of its
 // vectors) and one group of 64 WT rows; wave w takes WT tiles of 16 rows.
 // The contraction runs in stages of SG scale groups: the block loads a
-// stage's codes, scale words, digit words and group sums with coalesced
-// 16-byte loads into registers while it computes the previous stage from
-// LDS.  One v_mfma_i32_16x16x64_i8 per (plane, matrix, scale group) takes
+// stage's codes, scale words, digit words, group sums and steps with
+// coalesced 16-byte loads into registers while it computes the previous
+// stage from LDS.  One v_mfma_i32_16x16x64_i8 per (plane, matrix, scale group) takes
 // the vectors' digit words of the plane as A (vector l % 16, K-slice l / 16)
 // and the group's masked codes as B (row l % 16), so C arrives as vectors
 // 4 (l / 16) + r, row l % 16 and a lane needs only its own row's scale and
 // bias word.  The three plane sums are exact int32; the group's bf16 scale
-// multiplies their fp32 combination, its bias the vectors' group sums, and
-// each vector's fixed-point step 2^-k applies once at the end.
+// times the vector's step 2^-k for the group multiplies their fp32
+// combination, and the group's bias the vector's sum over the group.
+// MODE 0 leaves h as digit words (a unit's 64 rows are one scale group of
+// h), so the down rows read them as the gate/up rows read x's.
 typedef int v4i __attribute__((ext_vector_type(4)));
-constexpr int kGroupWords = 48;  // digit words per scale group (any bit width)
 
 template <int BITS, int SG>
 struct MmShape {
@@ -477,13 +536,14 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
     constexpr int SQ = UR * SG / 256;                         // scale words per thread, matrix and stage
     constexpr int DQ = 16 * SG * kGroupWords / 4 / 256;       // digit int4 per thread and stage
     static_assert(CQ >= 1 && SQ >= 1 && DQ >= 1 && 16 * SG <= 256, "stage split over 256 threads");
+    static_assert(MODE == 1 || UR == kGroup, "a gate/up unit's rows are one scale group of h");
     static_assert(UR * SG * S::GB % (16 * 256) == 0 && UR * SG % 256 == 0 && 16 * SG * kGroupWords % 1024 == 0,
                   "whole stage loads per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, h = lane >> 4;
     const int D = a.D, I = a.I;
     const int rows = MODE == 0 ? I : D, klen = MODE == 0 ? D : I;
-    const int ng = klen / kGroup, nch = klen / C::CODES;
+    const int ng = klen / kGroup;
     const int rgroups = (rows + UR - 1) / UR, nst = (ng + SG - 1) / SG;
     const int nact = *a.n_act, nunits = *a.n_mwork * rgroups;
     const uint64_t mat_q = (uint64_t)I * D * BITS / 8, row_q = (uint64_t)klen * BITS / 8;
@@ -496,6 +556,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
     __shared__ uint32_t s_sw[M][SG][UR];               // scale words [group][row]
     __shared__ __align__(16) int s_dig[16][S::DIGROW];
     __shared__ __align__(16) float s_gs[SG][16];       // group sums [group][vector]
+    __shared__ __align__(16) float s_inv[SG][16];      // group steps [group][vector]
     __shared__ int s_vec[16];                          // the tile's vectors (token or position), -1 past n
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int wk = a.mwork[u / rgroups];
@@ -514,7 +575,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
         uint4 rq[M][CQ];
         uint32_t rw[M][SQ];
         int4 rd[DQ];
-        float rg = 0.f;
+        float rg = 0.f, ri = 0.f;
         auto load = [&](int g0) {
 #pragma unroll
             for (int m = 0; m < M; ++m) {
@@ -542,14 +603,14 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                 const int rem = f - t * (SG * kGroupWords / 4), gl = rem / (kGroupWords / 4);
                 const int w4 = rem - gl * (kGroupWords / 4), g = g0 + gl, vec = s_vec[t];
                 const int vc = vec >= 0 ? vec : 0, gc = g < ng ? g : ng - 1;
-                rd[c] = *reinterpret_cast<const int4 *>(dsrc + (size_t)vc * nch * C::DW + gc * kGroupWords + 4 * w4);
+                rd[c] = *reinterpret_cast<const int4 *>(dsrc + ((size_t)vc * ng + gc) * kGroupWords + 4 * w4);
             }
             {
                 const int tt = tid & (16 * SG - 1);
                 const int t = tt / SG, gl = tt - t * SG, g = g0 + gl, vec = s_vec[t];
                 const int vc = vec >= 0 ? vec : 0, gc = g < ng ? g : ng - 1;
-                const float *cs = csrc + (size_t)vc * nch;
-                rg = BITS == 4 ? cs[2 * gc] + cs[2 * gc + 1] : cs[gc];
+                rg = csrc[(size_t)vc * ng + gc];
+                ri = isrc[(size_t)vc * ng + gc];
             }
         };
         auto store = [&](int g0) {
@@ -577,7 +638,9 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
             }
             if (tid < 16 * SG) {
                 const int t = tid / SG, gl = tid - t * SG;
-                s_gs[gl][t] = s_vec[t] >= 0 && g0 + gl < ng ? rg : 0.f;
+                const bool ok = s_vec[t] >= 0 && g0 + gl < ng;
+                s_gs[gl][t] = ok ? rg : 0.f;
+                s_inv[gl][t] = ok ? ri : 0.f;
             }
         };
         float acs[M][WT][4], acb[M][WT][4];
@@ -600,7 +663,8 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
 #pragma unroll
                 for (int p = 0; p < 3; ++p) da[p] = digits_of<BITS>(&s_dig[r16][0], gl, h, p);
                 const float4 gs = *reinterpret_cast<const float4 *>(&s_gs[gl][4 * h]);
-                const float gv[4] = {gs.x, gs.y, gs.z, gs.w};
+                const float4 gi = *reinterpret_cast<const float4 *>(&s_inv[gl][4 * h]);
+                const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, iv[4] = {gi.x, gi.y, gi.z, gi.w};
                 const v4i z = {0, 0, 0, 0};
 #pragma unroll
                 for (int m = 0; m < M; ++m)
@@ -618,7 +682,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                             // (c0 + 256 c1) is exact in int32 and rounds once to fp32, as the
                             // one-token path's fma(c1, 256, c0) does
                             const float ps = fmaf((float)c2[r], 65536.f, (float)(c0[r] + (c1[r] << 8)));
-                            acs[m][wt][r] = fmaf(sc, ps, acs[m][wt][r]);
+                            acs[m][wt][r] = fmaf(sc * iv[r], ps, acs[m][wt][r]);
                             acb[m][wt][r] = fmaf(bi, gv[r], acb[m][wt][r]);
                         }
                     }
@@ -629,21 +693,34 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                 __syncthreads();
             }
         }
-#pragma unroll
-        for (int wt = 0; wt < WT; ++wt) {
-            const int row = row0 + wrow0 + 16 * wt;
+        if constexpr (MODE == 0) {
+            // h of the unit's 64 rows (one scale group g of h) for its 16
+            // positions, through LDS, then as digit words: wave w converts
+            // vectors 4 w .. 4 w + 3, one per DPP row
+            __shared__ float s_h[16][kGroup + 1];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 4 * h + r, vec = s_vec[t];
-                if (vec < 0 || row >= rows) continue;
-                const float inv = isrc[vec];
-                const size_t pos = (size_t)it.pos0 + j0 + t;
-                if constexpr (MODE == 0) {
-                    const float g = fmaf(acs[0][wt][r], inv, acb[0][wt][r]);
-                    const float uu = fmaf(acs[1][wt][r], inv, acb[1][wt][r]);
-                    a.h[pos * I + row] = g / (1.f + expf(-g)) * uu;
-                } else {
-                    a.y[pos * D + row] = fmaf(acs[0][wt][r], inv, acb[0][wt][r]);
+                const float g = acs[0][0][r] + acb[0][0][r], uu = acs[1][0][r] + acb[1][0][r];
+                s_h[4 * h + r][wrow0] = g / (1.f + expf(-g)) * uu;
+            }
+            __syncthreads();
+            const int t = 4 * wave + h;
+            if (s_vec[t] >= 0) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = s_h[t][group_value<BITS>(r16, j)];
+                const size_t pg = ((size_t)it.pos0 + j0 + t) * (I / kGroup) + row0 / kGroup;
+                group_digits<BITS>(v, r16, a.hdig + pg * kGroupWords, a.hcsum + pg, a.hinv + pg);
+            }
+        } else {
+#pragma unroll
+            for (int wt = 0; wt < WT; ++wt) {
+                const int row = row0 + wrow0 + 16 * wt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * h + r;
+                    if (s_vec[t] < 0 || row >= rows) continue;
+                    a.y[((size_t)it.pos0 + j0 + t) * D + row] = acs[0][wt][r] + acb[0][wt][r];
                 }
             }
         }
@@ -654,21 +731,11 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
 template <int BITS>
 hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 {
-    using C = Codes<BITS>;
-    const int nchunks_d = a.D * BITS / 128, nchunks_i = a.I * BITS / 128;
     switch (stage) {
-    case 0:  // x digits
-        hipLaunchKernelGGL(k_digits<BITS>, dim3(a.T), dim3(256), 0, s, a.x, a.D, a.xdig, a.xcsum, a.xinv,
-                           nchunks_d * C::DW, nchunks_d);
-        break;
-    case 1:  // gate/up: 64-row units, 8 scale groups per stage
+    case 0:  // gate/up: 64-row units, 8 scale groups per stage
         hipLaunchKernelGGL((k_expert_mm<BITS, 0, 1, 8>), dim3(2048), dim3(256), 0, s, a);
         break;
-    case 2:  // h digits (all positions)
-        hipLaunchKernelGGL(k_digits<BITS>, dim3(a.T * a.src.n_slots), dim3(256), 0, s, a.h, a.I, a.hdig, a.hcsum,
-                           a.hinv, nchunks_i * C::DW, nchunks_i);
-        break;
-    case 3:  // down: 128-row units (the digit tables of h shared by more rows)
+    case 1:  // down: 128-row units (the digit tables of h shared by more rows)
         hipLaunchKernelGGL((k_expert_mm<BITS, 1, 2, (BITS == 4 ? 4 : 8)>), dim3(2048), dim3(256), 0, s, a);
         break;
     }
@@ -677,15 +744,28 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s)
+hipError_t launch_batch_route(const BatchArgs &a, int do_topk, int bits, hipStream_t s)
 {
+    const int ttiles = (a.T + 15) / 16;
     if (do_topk) {
         const int splits = route_splits(a.D);
-        hipLaunchKernelGGL(k_route_m, dim3(splits * ((a.E + 15) / 16) * ((a.T + 15) / 16)), dim3(256), 0, s, a, splits);
+        const dim3 grid(splits * ((a.E + 15) / 16) * ttiles);
+        if (bits == 4)
+            hipLaunchKernelGGL(k_route_m<4>, grid, dim3(256), 0, s, a, splits);
+        else
+            hipLaunchKernelGGL(k_route_m<2>, grid, dim3(256), 0, s, a, splits);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_topk_b, dim3((a.T + 3) / 4), dim3(256), 0, s, a, splits);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        const dim3 grid(ttiles * (a.D / kGroup));
+        if (bits == 4)
+            hipLaunchKernelGGL(k_xdigits<4>, grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_xdigits<2>, grid, dim3(256), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
@@ -693,7 +773,7 @@ hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s)
 
 hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s)
 {
-    for (int stage = 0; stage < 4; ++stage) {
+    for (int stage = 0; stage < 2; ++stage) {
         hipError_t e = bits == 4 ? batch_bits<4>(a, stage, s) : batch_bits<2>(a, stage, s);
         if (e != hipSuccess) return e;
     }

@@ -37,7 +37,8 @@ struct WsLayout {
     size_t lpart = 0;        // float [kRouteSplit][T][E] partial logits
     size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0;
     size_t mwork = 0, n_mwork = 0;  // expert-kernel work list: (item << 2 | 16-token tile), its length
-    size_t xdig = 0, xcsum = 0, xinv = 0, hb = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
+    // digit words of x and h, with each (vector, scale group)'s sum and step
+    size_t xdig = 0, xcsum = 0, xinv = 0, hdig = 0, hcsum = 0, hinv = 0, y = 0;
     size_t total = 0;
 };
 
@@ -115,13 +116,12 @@ struct BatchArgs {
     int32_t *mwork;          // [(E+1)*4] expert-kernel work: item ii (act[ii], or the shared expert for
                              // ii == n_act) << 2 | tile of 16 of its tokens
     int32_t *n_mwork;        // [1]
-    int *xdig;               // [T][D/chunk][DW] digit tables of x
-    float *xcsum;            // [T][D/chunk]
-    float *xinv;             // [T]
-    float *h;                // [positions][I]
-    int *hdig;               // [positions][I/chunk][DW]
-    float *hcsum;            // [positions][I/chunk]
-    float *hinv;             // [positions]
+    int *xdig;               // [T][D/64][48] digit words of x, per scale group
+    float *xcsum;            // [T][D/64] group sums of x
+    float *xinv;             // [T][D/64] group steps 2^-k
+    int *hdig;               // [positions][I/64][48] digit words of h
+    float *hcsum;            // [positions][I/64]
+    float *hinv;             // [positions][I/64]
     float *y;                // [positions][D]
     uint32_t *flags;
     int32_t T, D, E, K, I;
@@ -137,7 +137,7 @@ struct DownShape {
 DownShape down_shape(int I, int bits);
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
-hipError_t launch_batch_route(const BatchArgs &a, int do_topk, hipStream_t s);
+hipError_t launch_batch_route(const BatchArgs &a, int do_topk, int bits, hipStream_t s);
 hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s);
 hipError_t launch_gate_up(const GateUpArgs &a, int bits, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, int bits, hipStream_t s);

@@ -479,7 +479,9 @@ template <int BITS, int SG>
 struct MmShape {
     static constexpr int GB = 16 * BITS / 2;                       // code bytes per row and scale group
     static constexpr int ROWB = SG * GB + (BITS == 4 ? 32 : 16);   // LDS bytes per code row (padded)
-    static constexpr int DIGROW = SG * kGroupWords + 16;           // LDS words per vector (+16: 16 banks apart)
+    // LDS words per vector: a stride of 4 banks (mod 64) puts the 16 vectors
+    // of a 16-byte digit read on distinct banks
+    static constexpr int DIGROW = SG * kGroupWords + 4;
 };
 
 // A lane's 16 codes (K-slice h of scale group g) of an LDS code row, one per
@@ -537,6 +539,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
     constexpr int DQ = 16 * SG * kGroupWords / 4 / 256;       // digit int4 per thread and stage
     static_assert(CQ >= 1 && SQ >= 1 && DQ >= 1 && 16 * SG <= 256, "stage split over 256 threads");
     static_assert(MODE == 1 || UR == kGroup, "a gate/up unit's rows are one scale group of h");
+    static_assert(SG % 4 == 0, "bias products take four groups at a time");
     static_assert(UR * SG * S::GB % (16 * 256) == 0 && UR * SG % 256 == 0 && 16 * SG * kGroupWords % 1024 == 0,
                   "whole stage loads per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -569,12 +572,15 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
         }
         __syncthreads();
         // one stage's loads into registers (clamped rows, groups and
-        // vectors: every load is in bounds); what lies past ng or past the
-        // tile's vectors is zeroed when the stage is stored, after the data
-        // has arrived (a select on a load's registers would wait for it)
-        uint4 rq[M][CQ];
+        // vectors: every load is in bounds).  Codes, scales and digits of
+        // groups past ng are never multiplied (the group loop stops at ng),
+        // and the outputs of vectors past the tile's are dropped, so the
+        // clamped copies are stored as they are.
+        // (native vector types: a struct copy would become a memcpy that keeps
+        // these arrays in scratch memory)
+        v4i rq[M][CQ];
         uint32_t rw[M][SQ];
-        int4 rd[DQ];
+        v4i rd[DQ];
         float rg = 0.f, ri = 0.f;
         auto load = [&](int g0) {
 #pragma unroll
@@ -587,7 +593,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                     const int g = g0 + b16 * 16 / S::GB;
                     const uint64_t rr = row0 + row < rows ? row0 + row : rows - 1;
                     const uint64_t off = (uint64_t)(g < ng ? g : ng - 1) * S::GB + (uint64_t)(b16 * 16) % S::GB;
-                    rq[m][c] = *reinterpret_cast<const uint4 *>(mq + rr * row_q + off);
+                    rq[m][c] = *reinterpret_cast<const v4i *>(mq + rr * row_q + off);
                 }
                 const uint8_t *ms = it.blob + sb0 + (uint64_t)m * mat_sb;
 #pragma unroll
@@ -603,7 +609,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                 const int rem = f - t * (SG * kGroupWords / 4), gl = rem / (kGroupWords / 4);
                 const int w4 = rem - gl * (kGroupWords / 4), g = g0 + gl, vec = s_vec[t];
                 const int vc = vec >= 0 ? vec : 0, gc = g < ng ? g : ng - 1;
-                rd[c] = *reinterpret_cast<const int4 *>(dsrc + ((size_t)vc * ng + gc) * kGroupWords + 4 * w4);
+                rd[c] = *reinterpret_cast<const v4i *>(dsrc + ((size_t)vc * ng + gc) * kGroupWords + 4 * w4);
             }
             {
                 const int tt = tid & (16 * SG - 1);
@@ -620,22 +626,22 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                 for (int c = 0; c < CQ; ++c) {
                     const int f = tid + 256 * c, row = f / (SG * S::GB / 16);
                     const int b16 = f - row * (SG * S::GB / 16);
-                    const bool ok = g0 + b16 * 16 / S::GB < ng;
-                    *reinterpret_cast<uint4 *>(&s_code[m][row][16 * b16]) = ok ? rq[m][c] : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<v4i *>(&s_code[m][row][16 * b16]) = rq[m][c];
                 }
 #pragma unroll
                 for (int c = 0; c < SQ; ++c) {
                     const int f = tid + 256 * c, row = f / SG, gl = f - row * SG;
-                    s_sw[m][gl][row] = g0 + gl < ng ? rw[m][c] : 0u;
+                    s_sw[m][gl][row] = rw[m][c];
                 }
             }
 #pragma unroll
             for (int c = 0; c < DQ; ++c) {
                 const int f = tid + 256 * c, t = f / (SG * kGroupWords / 4);
-                const int rem = f - t * (SG * kGroupWords / 4), gl = rem / (kGroupWords / 4);
-                const bool ok = s_vec[t] >= 0 && g0 + gl < ng;
-                *reinterpret_cast<int4 *>(&s_dig[t][4 * rem]) = ok ? rd[c] : make_int4(0, 0, 0, 0);
+                const int rem = f - t * (SG * kGroupWords / 4);
+                *reinterpret_cast<v4i *>(&s_dig[t][4 * rem]) = rd[c];
             }
+            // group sums of groups past ng are zero: the bias products take
+            // a stage's groups four at a time
             if (tid < 16 * SG) {
                 const int t = tid / SG, gl = tid - t * SG;
                 const bool ok = s_vec[t] >= 0 && g0 + gl < ng;
@@ -643,13 +649,16 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                 s_inv[gl][t] = ok ? ri : 0.f;
             }
         };
-        float acs[M][WT][4], acb[M][WT][4];
+        float acs[M][WT][4];
+        v4f acb[M][WT];
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int wt = 0; wt < WT; ++wt)
+            for (int wt = 0; wt < WT; ++wt) {
+                acb[m][wt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acs[m][wt][r] = acb[m][wt][r] = 0.f;
+                for (int r = 0; r < 4; ++r) acs[m][wt][r] = 0.f;
+            }
         load(0);
         store(0);
         __syncthreads();
@@ -658,13 +667,12 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
             const int g0 = st * SG;
             if (st + 1 < nst) load(g0 + SG);  // in flight while this stage is computed
             const int gn = ng - g0 < SG ? ng - g0 : SG;
-            for (int gl = 0; gl < gn; ++gl) {
+            auto group = [&](int gl) {
                 v4i da[3];
 #pragma unroll
                 for (int p = 0; p < 3; ++p) da[p] = digits_of<BITS>(&s_dig[r16][0], gl, h, p);
-                const float4 gs = *reinterpret_cast<const float4 *>(&s_gs[gl][4 * h]);
                 const float4 gi = *reinterpret_cast<const float4 *>(&s_inv[gl][4 * h]);
-                const float gv[4] = {gs.x, gs.y, gs.z, gs.w}, iv[4] = {gi.x, gi.y, gi.z, gi.w};
+                const float iv[4] = {gi.x, gi.y, gi.z, gi.w};
                 const v4i z = {0, 0, 0, 0};
 #pragma unroll
                 for (int m = 0; m < M; ++m)
@@ -672,20 +680,47 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                     for (int wt = 0; wt < WT; ++wt) {
                         const int wr = wrow0 + 16 * wt;
                         const v4i bq = codes_of<BITS>(&s_code[m][wr][0], gl, h);
-                        const uint32_t w = s_sw[m][gl][wr];
+                        const float sc = bf16_lo(s_sw[m][gl][wr]);
                         const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[0], bq, z, 0, 0, 0);
                         const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[1], bq, z, 0, 0, 0);
                         const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[2], bq, z, 0, 0, 0);
-                        const float sc = bf16_lo(w), bi = bf16_hi(w);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            // (c0 + 256 c1) is exact in int32 and rounds once to fp32, as the
-                            // one-token path's fma(c1, 256, c0) does
-                            const float ps = fmaf((float)c2[r], 65536.f, (float)(c0[r] + (c1[r] << 8)));
+                            float ps;
+                            if constexpr (BITS == 2) {
+                                // |c0 + 256 c1 + 65536 c2| < 3 * 64 * 2^22 < 2^31: exact in
+                                // int32, one rounding to fp32
+                                ps = (float)((((c2[r] << 8) + c1[r]) << 8) + c0[r]);
+                            } else {
+                                // (c0 + 256 c1) is exact in int32 and rounds once to fp32, as
+                                // the one-token path's fma(c1, 256, c0) does
+                                ps = fmaf((float)c2[r], 65536.f, (float)(c0[r] + (c1[r] << 8)));
+                            }
                             acs[m][wt][r] = fmaf(sc * iv[r], ps, acs[m][wt][r]);
-                            acb[m][wt][r] = fmaf(bi, gv[r], acb[m][wt][r]);
                         }
                     }
+            };
+            if (BITS == 2 && gn == SG) {
+                // a whole stage: unrolled, so that one group's LDS reads and
+                // matrix-core work overlap the previous group's (at 4-bit the
+                // unrolled gate/up kernel would need more than 256 VGPRs)
+#pragma unroll
+                for (int gl = 0; gl < SG; ++gl) group(gl);
+            } else {
+                for (int gl = 0; gl < gn; ++gl) group(gl);
+            }
+            // the stage's bias terms, four groups per v_mfma_f32_16x16x4f32:
+            // A = group sums (vector l % 16, group l / 16), B = the rows' bias
+            // halves (group l / 16, row l % 16); groups past ng have zero sums
+#pragma unroll
+            for (int q = 0; q < SG / 4; ++q) {
+                const float ga = s_gs[4 * q + h][r16];
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int wt = 0; wt < WT; ++wt)
+                        acb[m][wt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            ga, bf16_hi(s_sw[m][4 * q + h][wrow0 + 16 * wt]), acb[m][wt], 0, 0, 0);
             }
             if (st + 1 < nst) {
                 __syncthreads();  // every wave is done with this stage

@@ -48,6 +48,8 @@ def _run_batch(cfg, T, token0=0, r_scale=None):
     ("noshared_T4", CFG["tiny"].replace(n_shared=0, seed=0x5EED00E4), 4),
     ("wide_T20", CFG["tiny"].replace(D=8192, I=64, E=8, K=2, seed=0x5EED00E5), 20),
     ("deep_inter_T6", CFG["tiny"].replace(D=128, I=4096, E=8, K=2, bits=2, seed=0x5EED00E6), 6),
+    # 2048 experts (more experts than the other cases by far; top-K over 32 keys per lane)
+    ("many_experts_T12", CFG["tiny"].replace(D=256, I=64, E=2048, K=4, seed=0x5EED00E7), 12),
 ])
 def test_batched_layer_step(name, cfg, T):
     print(f"[gpu case] batched layer {name}", flush=True)

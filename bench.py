@@ -254,6 +254,40 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
     per_token = L * st.slab_blobs * bb
     gbs = per_token * tps / 1e9
     log(f"streamed: {tokens} tokens in {wall:.3f} s = {tps:.2f} tok/s, {gbs:.1f} GB/s over the link, flags {flags}")
+
+    # hybrid residency: the first n layers keep their experts in HBM (the
+    # resident arena, which now holds the same bytes), the rest stream
+    hybrid = []
+    for n_res in (L // 2, 3 * L // 4):
+        for l in range(L):
+            st.set_resident(l, resident.arena.data_ptr() + l * E * bb if l < n_res else None,
+                            resident.shared.data_ptr() + l * bb if l < n_res and cfg.n_shared else None)
+        r.copy_(torch.from_numpy(v0.copy()).cuda().view(1, D))
+        x.copy_(r)
+        st.step(r, x)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(x, want)) and bool(torch.equal(st.topk_idx, resident.topk_idx))
+        if not same:
+            raise SystemExit(f"hybrid ({n_res} resident layers) output differs from the resident stack")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(tokens):
+            r.copy_(xin[warmup + t:warmup + t + 1])
+            x.copy_(xin[warmup + t:warmup + t + 1])
+            st.step(r, x)
+        torch.cuda.synchronize()
+        hw = time.perf_counter() - t0
+        hflags = int(st.workspace[:4].view(torch.int32).item())
+        h_tps = tokens / hw
+        h_bytes = (L - n_res) * st.slab_blobs * bb
+        log(f"streamed: hybrid, {n_res} of {L} layers resident: {h_tps:.2f} tok/s, "
+            f"{h_bytes * h_tps / 1e9:.1f} GB/s over the link, flags {hflags}")
+        hybrid.append({"resident_layers": n_res, "tokens_per_s": round(h_tps, 3),
+                       "ms_per_token": round(hw / tokens * 1e3, 3), "pcie_bytes_per_token": h_bytes,
+                       "pcie_gbs": round(h_bytes * h_tps / 1e9, 2), "bitwise_equal_resident": same,
+                       "device_flags": hflags})
+    for l in range(L):
+        st.set_resident(l, None)
     return {"workload": f"{L}-layer {cfg.bits}-bit stack, experts in pinned host RAM, K={cfg.K} + {cfg.n_shared} "
                         f"shared blobs per layer copied host->HBM per token, fresh N(0,1) input per token",
             "tokens": tokens, "tokens_per_s": round(tps, 3), "ms_per_token": round(wall / tokens * 1e3, 3),
@@ -261,7 +295,7 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
             "pcie_peak_measured_gbs": round(link, 2), "pcie_frac_measured": round(gbs / link, 4),
             "h2d_large_copy_gbs": round(max(big), 2), "h2d_streamer_pattern_gbs": round(pattern, 2),
             "arena_blobs": P, "arena_aliased": P != full, "bitwise_equal_resident": identical,
-            "device_flags": flags}
+            "device_flags": flags, "hybrid": hybrid}
 
 
 def resident_extra(cfg, steps, warmup):

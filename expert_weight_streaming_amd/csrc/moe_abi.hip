@@ -539,9 +539,13 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
     const int with_shared = layers[0].n_shared;
     if (st->slab_blobs != K + with_shared) return fail(MOE_ESTATE, "slab holds %d blobs, the layers need %d", st->slab_blobs, K + with_shared);
     for (int32_t l = 0; l < n_layers; ++l) {
-        if (layers[l].experts) return fail(MOE_EINVAL, "layer %d is not a streamed layer (experts != NULL)", l);
         if (layers[l].top_k != K || layers[l].n_shared != with_shared)
             return fail(MOE_EINVAL, "layer %d has another top_k / n_shared", l);
+        if (layers[l].experts) {
+            // a resident layer: its experts (and shared expert) in HBM
+            if (int rc = check_desc(&layers[l], 1)) return rc;
+            continue;
+        }
         moe_layer_desc d = layers[l];
         d.slab = st->slab[0];
         if (int rc = check_desc(&d, 1)) return rc;
@@ -554,12 +558,19 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
     hipEvent_t copy_done[2] = {(hipEvent_t)events[1], (hipEvent_t)events[2]};
     hipEvent_t compute_done[2] = {(hipEvent_t)events[3], (hipEvent_t)events[4]};
     hipError_t e;
+    int32_t j = 0;  // streamed layers so far: layer l, the j-th streamed one, uses slot j mod 2
     for (int32_t l = 0; l < n_layers; ++l) {
-        const int s = l & 1;
-        moe_layer_desc d = layers[l];
-        d.slab = st->slab[s];
         int32_t *idx = topk_idx + (size_t)l * K;
         float *w = topk_w + (size_t)l * K;
+        if (layers[l].experts) {
+            // resident: routing and experts stay on the device, no host wait
+            int rc = moe_layer_step(&layers[l], resid, x, 1, idx, w, workspace, ws_bytes, compute_stream);
+            if (rc) return rc;
+            continue;
+        }
+        const int s = j & 1;
+        moe_layer_desc d = layers[l];
+        d.slab = st->slab[s];
         // 1. routing, and its selections to the host (the one device->host wait per layer)
         int rc = moe_route(&d, x, 1, idx, w, nullptr, workspace, ws_bytes, compute_stream);
         if (rc) return rc;
@@ -567,22 +578,26 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
             return hip_fail(e, "selection copy");
         if ((e = hipEventRecord(route_done, cs)) != hipSuccess) return hip_fail(e, "event record");
         if ((e = hipEventSynchronize(route_done)) != hipSuccess) return hip_fail(e, "selection wait");
-        // 2. the selected experts into slot s, after the kernel that last read it (layer l-2)
-        if (l >= 2 && (e = hipStreamWaitEvent(ps, compute_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
-        rc = moe_stream_prefetch(st, l, host_ids, K, s, l == 0 ? with_shared : 0, copy_stream, copy_done[s]);
+        // 2. the selected experts into slot s, after the kernel that last read it (streamed layer j-2)
+        if (j >= 2 && (e = hipStreamWaitEvent(ps, compute_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
+        rc = moe_stream_prefetch(st, l, host_ids, K, s, j == 0 ? with_shared : 0, copy_stream, copy_done[s]);
         if (rc) return rc;
         // 3. the layer itself once its weights have landed
         if ((e = hipStreamWaitEvent(cs, copy_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
         rc = moe_layer_step(&d, resid, x, 1, idx, w, workspace, ws_bytes, compute_stream);
         if (rc) return rc;
         if ((e = hipEventRecord(compute_done[s], cs)) != hipSuccess) return hip_fail(e, "event record");
-        // 4. the next layer's shared expert needs no routing: queue it behind this layer's copies
-        if (with_shared && l + 1 < n_layers) {
-            const int s1 = (l + 1) & 1;
-            if (l >= 1 && (e = hipStreamWaitEvent(ps, compute_done[s1], 0)) != hipSuccess) return hip_fail(e, "wait");
-            rc = moe_stream_prefetch(st, l + 1, nullptr, 0, s1, 1, copy_stream, nullptr);
+        // 4. the next streamed layer's shared expert needs no routing: queue
+        // it behind this layer's copies, into the slot that layer will use
+        int32_t ln = l + 1;
+        while (ln < n_layers && layers[ln].experts) ++ln;
+        if (with_shared && ln < n_layers) {
+            const int s1 = (j + 1) & 1;
+            if (j >= 1 && (e = hipStreamWaitEvent(ps, compute_done[s1], 0)) != hipSuccess) return hip_fail(e, "wait");
+            rc = moe_stream_prefetch(st, ln, nullptr, 0, s1, 1, copy_stream, nullptr);
             if (rc) return rc;
         }
+        ++j;
     }
     return MOE_OK;
 }

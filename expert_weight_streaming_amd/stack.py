@@ -154,6 +154,24 @@ class StreamedStack:
     def host_shared_blob(self, l: int) -> torch.Tensor:
         return self.host_shared[l * self.bb:(l + 1) * self.bb]
 
+    def set_resident(self, l: int, experts, shared=None):
+        """Hybrid residency: layer l's E expert blobs at `experts` in HBM (a
+        device tensor or address, E * blob_bytes bytes in expert order) and
+        its shared blob at `shared`; the token pipeline then runs the layer
+        without copies or a host wait.  The bytes should equal what the layer
+        streams (host_blob(l, e), host_shared_blob(l)) for the output to equal
+        the streamed one.  experts=None makes the layer streamed again."""
+        from . import make_desc
+        resident = experts is not None
+        self.descs[l] = make_desc(hidden=self.D, n_experts=self.E, top_k=self.K, inter=self.I, n_shared=self.n_shared,
+                                  bits=self.bits, group=self.group, rms_eps=self.eps, router_w=self.router[l],
+                                  gamma=self.gamma[l], experts=experts if resident else None,
+                                  shared=shared if resident and self.n_shared else None,
+                                  slab=None if resident else self.slab[0], blob_bytes=self.bb)
+
+    def resident_layers(self) -> list[int]:
+        return [l for l in range(self.layers) if self.descs[l].experts]
+
     def step(self, resid, x, stream=None):
         """One token (resid, x: [1][D] device) through every layer; returns
         when the last layer is enqueued on `stream`."""

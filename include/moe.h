@@ -265,24 +265,29 @@ int moe_host_alloc(size_t bytes, void **out);
 int moe_host_free(void *p);
 
 /*
- * One decode token through n_layers streamed layers (the per-layer pipeline
- * of hakusoku.com, "パイプライン概要": routing, then the selected experts'
- * reads, then the expert forward with combine, residual and norm; the
- * expert work is queued without the host waiting for it, as the pages'
- * deferred command buffer).  For layer l, slot s = l mod 2:
+ * One decode token through n_layers layers, streamed or resident (the
+ * per-layer pipeline of hakusoku.com, "パイプライン概要": routing, then the
+ * selected experts' reads, then the expert forward with combine, residual
+ * and norm; the expert work is queued without the host waiting for it, as
+ * the pages' deferred command buffer).  A streamed layer l, the j-th
+ * streamed one, uses slot s = j mod 2:
  *   1. moe_route on compute_stream; the K selections are copied to
  *      host_ids (pinned host, K int32) and the host waits for them;
  *   2. moe_stream_prefetch of those experts into slab slot s on
- *      copy_stream, after the layer that last read the slot (l-2);
+ *      copy_stream, after the streamed layer that last read the slot (j-2);
  *   3. compute_stream waits for the copies, then moe_layer_step reads the
  *      slot (the step recomputes the same routing bit for bit);
- *   4. the shared expert of layer l+1 (independent of routing) is queued on
- *      copy_stream right behind layer l's copies, so the link stays busy
- *      while the host waits for layer l+1's routing.
- * layers: host array of n_layers descriptors in streamed form (experts ==
- * NULL; their slab field is replaced by st->slab[l mod 2]); all share top_k
- * and n_shared, and st->slab_blobs == top_k + n_shared.  resid, x: [D]
- * device, in/out.  topk_idx, topk_w: device [n_layers][K] outputs.
+ *   4. the shared expert of the next streamed layer (independent of
+ *      routing) is queued on copy_stream right behind layer l's copies, so
+ *      the link stays busy while the host waits for that layer's routing.
+ * A resident layer (descriptor with experts != NULL: its experts in HBM, as
+ * for moe_layer_step) runs moe_layer_step on compute_stream with no copy and
+ * no host wait, so a caller chooses per layer which ones stream (hybrid
+ * residency: the layers that fit in HBM stay there, the rest stream).
+ * layers: host array of n_layers descriptors; streamed ones have experts ==
+ * NULL and their slab field is replaced by st->slab[j mod 2]; all share
+ * top_k and n_shared, and st->slab_blobs == top_k + n_shared.  resid, x:
+ * [D] device, in/out.  topk_idx, topk_w: device [n_layers][K] outputs.
  * events: five hipEvent_t (route_done, copy_done[2], compute_done[2]).
  * Returns after the last layer has been enqueued; the caller synchronises
  * compute_stream for the result.

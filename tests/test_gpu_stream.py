@@ -1,8 +1,9 @@
 """GPU tests of the host-streamed path: the slab receives exactly the host
 bytes of the selected experts, and a streamed stack gives bit-identical
 outputs and selections to a resident stack holding the same bytes (same
-kernels, same inputs), including an aliased host arena and a stack without
-a shared expert."""
+kernels, same inputs), including an aliased host arena, a stack without
+a shared expert, and stacks where some layers stay resident (hybrid
+residency)."""
 import numpy as np
 import pytest
 
@@ -101,3 +102,40 @@ def test_streamed_matches_oracle_first_layer():
     ref = W.LayerRef(cfg, 0)
     W.check_layer(ref, x0, x0, st.topk_idx[0, 0].cpu().numpy(), st.topk_w[0, 0].cpu().numpy(),
                   r[0].cpu().numpy(), x[0].cpu().numpy(), {})
+
+
+@pytest.mark.parametrize("pattern", ["RSRRSS", "SRRSRS", "RRRRRR", "SSSSSR"])
+def test_hybrid_residency_equals_resident(pattern):
+    """Per-layer hybrid residency: layers marked R keep their experts in HBM
+    (pointing into the resident twin's arena, the same bytes), the others
+    stream.  Output, selections and weights equal the resident stack's bit
+    for bit, whichever layers stream (first streamed layer after resident
+    ones, resident runs in the middle and at the end, none streamed)."""
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=len(pattern), seed=0x5EED0E60)
+    print(f"[gpu case] hybrid residency {pattern}", flush=True)
+    st = W.build_streamed(cfg, layers=len(pattern), arena_blobs=29)
+    rs = W.resident_twin(st)
+    for l, c in enumerate(pattern):
+        if c == "R":
+            st.set_resident(l, rs.arena.data_ptr() + l * st.E * st.bb, rs.shared.data_ptr() + l * st.bb)
+    assert st.resident_layers() == [l for l, c in enumerate(pattern) if c == "R"]
+    v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
+    xs, xr = v.clone(), v.clone()
+    for t in range(3):
+        r_s, r_r = xs.clone(), xr.clone()
+        st.step(r_s, xs)
+        rs.step(r_r, xr)
+        torch.cuda.synchronize()
+        assert int(st.workspace[:4].view(torch.int32).item()) == 0
+        assert torch.equal(st.topk_idx, rs.topk_idx), t
+        assert torch.equal(st.topk_w, rs.topk_w), t
+        assert torch.equal(r_s, r_r) and torch.equal(xs, xr), t
+    # and back to fully streamed
+    for l in range(len(pattern)):
+        st.set_resident(l, None)
+    assert st.resident_layers() == []
+    r_s, r_r = xs.clone(), xr.clone()
+    st.step(r_s, xs)
+    rs.step(r_r, xr)
+    torch.cuda.synchronize()
+    assert torch.equal(xs, xr)

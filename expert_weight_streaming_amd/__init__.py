@@ -35,15 +35,21 @@ class LayerDesc(ctypes.Structure):
                 ("slab", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64)]
 
 
+class ExpertCache(ctypes.Structure):
+    _fields_ = [("slots", ctypes.c_void_p), ("n_slots", ctypes.c_int32), ("meta", ctypes.c_void_p),
+                ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64)]
+
+
 class Streamer(ctypes.Structure):
     _fields_ = [("host_arena", ctypes.c_void_p), ("host_shared", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64),
                 ("n_experts", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("arena_blobs", ctypes.c_int64),
-                ("shared_blobs", ctypes.c_int64), ("slab", ctypes.c_void_p * 2), ("slab_blobs", ctypes.c_int32)]
+                ("shared_blobs", ctypes.c_int64), ("slab", ctypes.c_void_p * 2), ("slab_blobs", ctypes.c_int32),
+                ("cache", ctypes.POINTER(ExpertCache))]
 
 
 EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_last_error", "moe_route",
            "moe_expert_forward", "moe_layer_step", "moe_stack_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
-           "moe_host_alloc", "moe_host_free"]
+           "moe_host_alloc", "moe_host_free", "moe_expert_cache_meta_bytes", "moe_expert_cache_reset"]
 
 _lib = None
 
@@ -84,6 +90,10 @@ def lib():
         L.moe_host_alloc.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
         L.moe_host_free.restype = ctypes.c_int
         L.moe_host_free.argtypes = [vp]
+        L.moe_expert_cache_meta_bytes.restype = sz
+        L.moe_expert_cache_meta_bytes.argtypes = [i32, i32, i32]
+        L.moe_expert_cache_reset.restype = ctypes.c_int
+        L.moe_expert_cache_reset.argtypes = [ctypes.POINTER(ExpertCache), i32, i32]
         _lib = L
     return _lib
 
@@ -193,6 +203,14 @@ def moe_stream_token(descs, streamer: Streamer, resid, x, topk_idx, topk_w, host
     _check(lib().moe_stream_token(descs, len(descs), ctypes.byref(streamer), _ptr(resid), _ptr(x), _ptr(topk_idx),
                                   _ptr(topk_w), _ptr(host_ids), _ptr(workspace), ws_bytes, _stream(compute_stream),
                                   _stream(copy_stream), ctypes.cast(ev, ctypes.c_void_p)))
+
+
+def moe_expert_cache_meta_bytes(n_slots: int, n_layers: int, n_experts: int) -> int:
+    return int(lib().moe_expert_cache_meta_bytes(n_slots, n_layers, n_experts))
+
+
+def moe_expert_cache_reset(cache: ExpertCache, n_layers: int, n_experts: int) -> None:
+    _check(lib().moe_expert_cache_reset(ctypes.byref(cache), n_layers, n_experts))
 
 
 class HostArena:

@@ -488,8 +488,74 @@ int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t 
     return MOE_OK;
 }
 
-int moe_stream_prefetch(const moe_streamer *st, int32_t layer, const int32_t *expert_ids, int32_t n_ids,
-                        int32_t slot, int32_t with_shared, void *copy_stream, void *done_event)
+// ---- HBM expert cache: host metadata laid out in the caller's meta block
+//   CacheHead | tag[n_slots] (int64 key, -1 free) | where[L*E + L] (int32:
+//   slot, -1 not cached) | prev[n_slots] | next[n_slots] (LRU list, most
+//   recent first).  Keys: layer*E + e for routed expert e of a layer,
+//   L*E + layer for the layer's shared expert.
+struct CacheHead {
+    int32_t n_layers, n_experts, n_slots, head, tail, pad;
+};
+struct CacheView {
+    CacheHead *h;
+    int64_t *tag;
+    int32_t *where, *prev, *next;
+};
+static CacheView cache_view(void *meta, int32_t n_slots, int32_t n_layers, int32_t n_experts)
+{
+    CacheView v;
+    uint8_t *p = static_cast<uint8_t *>(meta);
+    v.h = reinterpret_cast<CacheHead *>(p);
+    v.tag = reinterpret_cast<int64_t *>(p + sizeof(CacheHead));
+    v.where = reinterpret_cast<int32_t *>(v.tag + n_slots);
+    v.prev = v.where + (size_t)n_layers * (n_experts + 1);
+    v.next = v.prev + n_slots;
+    return v;
+}
+static void lru_unlink(CacheView &v, int32_t s)
+{
+    const int32_t p = v.prev[s], n = v.next[s];
+    if (p >= 0) v.next[p] = n; else v.h->head = n;
+    if (n >= 0) v.prev[n] = p; else v.h->tail = p;
+}
+static void lru_push_front(CacheView &v, int32_t s)
+{
+    v.prev[s] = -1;
+    v.next[s] = v.h->head;
+    if (v.h->head >= 0) v.prev[v.h->head] = s;
+    v.h->head = s;
+    if (v.h->tail < 0) v.h->tail = s;
+}
+
+size_t moe_expert_cache_meta_bytes(int32_t n_slots, int32_t n_layers, int32_t n_experts)
+{
+    if (n_slots <= 0 || n_layers <= 0 || n_experts <= 0) return 0;
+    return sizeof(CacheHead) + (size_t)n_slots * 8 + (size_t)n_layers * (n_experts + 1) * 4 + (size_t)n_slots * 8;
+}
+
+int moe_expert_cache_reset(moe_expert_cache *c, int32_t n_layers, int32_t n_experts)
+{
+    if (!c || !c->slots || !c->meta) return fail(MOE_EINVAL, "cache, its slots or its meta block is NULL");
+    if (c->n_slots <= 0 || n_layers <= 0 || n_experts <= 0)
+        return fail(MOE_EINVAL, "cache sizes must be positive (slots %d, layers %d, experts %d)", c->n_slots, n_layers, n_experts);
+    CacheView v = cache_view(c->meta, c->n_slots, n_layers, n_experts);
+    *v.h = CacheHead{n_layers, n_experts, c->n_slots, -1, -1, 0};
+    for (int32_t s = 0; s < c->n_slots; ++s) {
+        v.tag[s] = -1;
+        lru_push_front(v, s);
+    }
+    for (size_t k = 0; k < (size_t)n_layers * (n_experts + 1); ++k) v.where[k] = -1;
+    c->hits = c->misses = 0;
+    return MOE_OK;
+}
+
+static int stream_copies(const moe_streamer *st, int32_t layer, const int32_t *expert_ids, int32_t n_ids, int32_t slot,
+                         int32_t with_shared, hipStream_t cs, void *done_event, bool use_cache);
+
+// moe_stream_prefetch's checks, then its copies (through st->cache when
+// use_cache is set and the streamer has one)
+static int prefetch_impl(const moe_streamer *st, int32_t layer, const int32_t *expert_ids, int32_t n_ids, int32_t slot,
+                         int32_t with_shared, void *copy_stream, void *done_event, bool use_cache)
 {
     if (!st) return fail(MOE_ESTATE, "streamer is NULL");
     if (!st->host_arena || st->arena_blobs <= 0) return fail(MOE_ESTATE, "no host arena registered");
@@ -504,19 +570,65 @@ int moe_stream_prefetch(const moe_streamer *st, int32_t layer, const int32_t *ex
     for (int32_t j = 0; j < n_ids; ++j)
         if (expert_ids[j] < 0 || expert_ids[j] >= st->n_experts)
             return fail(MOE_ESTATE, "expert id %d out of range", expert_ids[j]);
-    hipStream_t cs = (hipStream_t)copy_stream;
+    return stream_copies(st, layer, expert_ids, n_ids, slot, with_shared, (hipStream_t)copy_stream, done_event,
+                         use_cache && st->cache);
+}
+
+int moe_stream_prefetch(const moe_streamer *st, int32_t layer, const int32_t *expert_ids, int32_t n_ids,
+                        int32_t slot, int32_t with_shared, void *copy_stream, void *done_event)
+{
+    return prefetch_impl(st, layer, expert_ids, n_ids, slot, with_shared, copy_stream, done_event, false);
+}
+
+// The copies of moe_stream_prefetch (checked already); with use_cache, the
+// routed blobs go through st->cache.
+static int stream_copies(const moe_streamer *st, int32_t layer, const int32_t *expert_ids, int32_t n_ids, int32_t slot,
+                         int32_t with_shared, hipStream_t cs, void *done_event, bool use_cache)
+{
     const uint64_t bb = st->blob_bytes;
-    for (int32_t j = 0; j < n_ids; ++j) {
-        const int64_t pb = ((int64_t)layer * st->n_experts + expert_ids[j]) % st->arena_blobs;
-        hipError_t e = hipMemcpyAsync(st->slab[slot] + (uint64_t)j * bb, st->host_arena + (uint64_t)pb * bb, bb,
-                                      hipMemcpyHostToDevice, cs);
+    moe_expert_cache *c = use_cache ? st->cache : nullptr;
+    CacheView v{};
+    if (c) v = cache_view(c->meta, c->n_slots, st->n_layers, st->n_experts);
+    // one blob into dst: from the cache on a hit, else from host memory
+    // `src` (and then into the least recently used slot, after every earlier
+    // copy out of that slot: all copies are on cs)
+    auto one = [&](uint8_t *dst, const uint8_t *src, int64_t key) -> int {
+        hipError_t e;
+        if (c && v.where[key] >= 0) {
+            const int32_t s = v.where[key];
+            e = hipMemcpyAsync(dst, c->slots + (uint64_t)s * bb, bb, hipMemcpyDeviceToDevice, cs);
+            if (e != hipSuccess) return hip_fail(e, "cached expert copy");
+            lru_unlink(v, s);
+            lru_push_front(v, s);
+            ++c->hits;
+            return MOE_OK;
+        }
+        e = hipMemcpyAsync(dst, src, bb, hipMemcpyHostToDevice, cs);
         if (e != hipSuccess) return hip_fail(e, "expert copy");
+        if (c) {
+            const int32_t s = v.h->tail;
+            if (v.tag[s] >= 0) v.where[v.tag[s]] = -1;
+            v.tag[s] = key;
+            v.where[key] = s;
+            lru_unlink(v, s);
+            lru_push_front(v, s);
+            e = hipMemcpyAsync(c->slots + (uint64_t)s * bb, dst, bb, hipMemcpyDeviceToDevice, cs);
+            if (e != hipSuccess) return hip_fail(e, "cache fill copy");
+            ++c->misses;
+        }
+        return MOE_OK;
+    };
+    const int64_t LE = (int64_t)st->n_layers * st->n_experts;
+    for (int32_t j = 0; j < n_ids; ++j) {
+        const int64_t key = (int64_t)layer * st->n_experts + expert_ids[j];
+        if (int rc = one(st->slab[slot] + (uint64_t)j * bb, st->host_arena + (uint64_t)(key % st->arena_blobs) * bb, key))
+            return rc;
     }
     if (with_shared) {
         const int64_t pb = (int64_t)layer % st->shared_blobs;
-        hipError_t e = hipMemcpyAsync(st->slab[slot] + (uint64_t)(st->slab_blobs - 1) * bb,
-                                      st->host_shared + (uint64_t)pb * bb, bb, hipMemcpyHostToDevice, cs);
-        if (e != hipSuccess) return hip_fail(e, "shared copy");
+        if (int rc = one(st->slab[slot] + (uint64_t)(st->slab_blobs - 1) * bb, st->host_shared + (uint64_t)pb * bb,
+                         LE + layer))
+            return rc;
     }
     if (done_event) {
         hipError_t e = hipEventRecord((hipEvent_t)done_event, cs);
@@ -553,6 +665,12 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
             return fail(MOE_ESTATE, "layer %d does not match the streamer's blob size / expert count", l);
     }
     if (int rc = check_ws(&layers[0], 1, workspace, ws_bytes)) return rc;
+    if (const moe_expert_cache *c = st->cache) {
+        if (!c->slots || !c->meta || c->n_slots <= 0) return fail(MOE_ESTATE, "expert cache without slots or meta block");
+        const CacheHead *h = static_cast<const CacheHead *>(c->meta);
+        if (h->n_layers != st->n_layers || h->n_experts != st->n_experts || h->n_slots != c->n_slots)
+            return fail(MOE_ESTATE, "expert cache not reset for this streamer (moe_expert_cache_reset)");
+    }
     hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
     hipEvent_t route_done = (hipEvent_t)events[0];
     hipEvent_t copy_done[2] = {(hipEvent_t)events[1], (hipEvent_t)events[2]};
@@ -580,7 +698,7 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
         if ((e = hipEventSynchronize(route_done)) != hipSuccess) return hip_fail(e, "selection wait");
         // 2. the selected experts into slot s, after the kernel that last read it (streamed layer j-2)
         if (j >= 2 && (e = hipStreamWaitEvent(ps, compute_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
-        rc = moe_stream_prefetch(st, l, host_ids, K, s, j == 0 ? with_shared : 0, copy_stream, copy_done[s]);
+        rc = prefetch_impl(st, l, host_ids, K, s, j == 0 ? with_shared : 0, copy_stream, copy_done[s], true);
         if (rc) return rc;
         // 3. the layer itself once its weights have landed
         if ((e = hipStreamWaitEvent(cs, copy_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
@@ -594,7 +712,7 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
         if (with_shared && ln < n_layers) {
             const int s1 = (j + 1) & 1;
             if (j >= 1 && (e = hipStreamWaitEvent(ps, compute_done[s1], 0)) != hipSuccess) return hip_fail(e, "wait");
-            rc = moe_stream_prefetch(st, ln, nullptr, 0, s1, 1, copy_stream, nullptr);
+            rc = prefetch_impl(st, ln, nullptr, 0, s1, 1, copy_stream, nullptr, true);
             if (rc) return rc;
         }
         ++j;

@@ -10,6 +10,8 @@ these workloads).
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import (HostArena, LayerDesc, make_desc, moe_blob_bytes, moe_layer_step, moe_stack_step, moe_workspace_bytes)
@@ -168,6 +170,32 @@ class StreamedStack:
                                   gamma=self.gamma[l], experts=experts if resident else None,
                                   shared=shared if resident and self.n_shared else None,
                                   slab=None if resident else self.slab[0], blob_bytes=self.bb)
+
+    def enable_cache(self, n_slots: int):
+        """An HBM cache of n_slots routed expert blobs for the streamed
+        layers (moe_expert_cache): moe_stream_token copies cached experts
+        device to device and fills the least recently used slot on a miss.
+        enable_cache(0) removes it.  Returns the cache (hits, misses)."""
+        import numpy as np
+        from . import ExpertCache, moe_expert_cache_meta_bytes, moe_expert_cache_reset
+        if n_slots <= 0:
+            self.streamer.cache = None
+            self._cache = self._cache_slots = self._cache_meta = None
+            return None
+        self._cache_slots = torch.empty(n_slots * self.bb, dtype=torch.uint8, device=self.slab.device)
+        # 8-byte aligned host block of the metadata's size
+        self._cache_meta = np.zeros((moe_expert_cache_meta_bytes(n_slots, self.layers, self.E) + 7) // 8,
+                                    dtype=np.uint64)
+        c = ExpertCache()
+        c.slots, c.n_slots, c.meta = self._cache_slots.data_ptr(), n_slots, self._cache_meta.ctypes.data
+        moe_expert_cache_reset(c, self.layers, self.E)
+        self._cache = c
+        self.streamer.cache = ctypes.pointer(c)
+        return c
+
+    @property
+    def cache(self):
+        return getattr(self, "_cache", None)
 
     def resident_layers(self) -> list[int]:
         return [l for l in range(self.layers) if self.descs[l].experts]

@@ -224,6 +224,43 @@ int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t 
  * slab_blobs blobs each receive one layer's selections while the other slot
  * is being computed on.
  */
+/*
+ * HBM-side cache of routed expert blobs for the streamed layers, the analog
+ * of the page cache that serves most expert reads on the pages' machine
+ * (toolarium.ru, "Flash-MoE: чистый C, Metal и никакого Python": caching is
+ * left to the OS page cache, which hits about 71% of reads).  n_slots blobs
+ * in HBM hold recently streamed blobs (a layer's routed expert, or its
+ * shared expert), replaced least recently used first.  moe_stream_token
+ * then copies a cached blob into the slab device to device instead of over
+ * the host link; a missed blob comes over the link into the slab and from
+ * there into the least recently used slot.  All copies run on the copy
+ * stream in issue order, so a slot is never refilled before earlier copies
+ * out of it.
+ *   slots:  device, n_slots * blob_bytes (caller-owned)
+ *   meta:   host, moe_expert_cache_meta_bytes(n_slots, n_layers, n_experts)
+ *           bytes (caller-owned): the (layer, expert) -> slot index and the
+ *           LRU list, written by moe_expert_cache_reset and moe_stream_token
+ *   hits, misses: blobs served from the cache / over the link
+ *           (moe_expert_cache_reset clears them)
+ * moe_stream_prefetch itself never uses the cache.  A cache belongs to one
+ * streamer (its n_layers and n_experts) and to one thread at a time.
+ */
+typedef struct moe_expert_cache {
+    uint8_t *slots;
+    int32_t n_slots;
+    void *meta;
+    uint64_t hits;
+    uint64_t misses;
+} moe_expert_cache;
+
+/* Bytes of host metadata for a cache of n_slots blobs over n_layers x
+ * (n_experts routed + 1 shared) blobs (0 for a non-positive argument). */
+size_t moe_expert_cache_meta_bytes(int32_t n_slots, int32_t n_layers, int32_t n_experts);
+
+/* Empty the cache: every slot free, nothing indexed, counters zero.
+ * MOE_EINVAL for a NULL cache, slots or meta, or a non-positive size. */
+int moe_expert_cache_reset(moe_expert_cache *c, int32_t n_layers, int32_t n_experts);
+
 typedef struct moe_streamer {
     const uint8_t *host_arena;  /* host, pinned: routed blobs, blob_bytes apart */
     const uint8_t *host_shared; /* host, pinned: shared blobs, blob_bytes apart, or NULL */
@@ -237,6 +274,7 @@ typedef struct moe_streamer {
     int64_t shared_blobs;
     uint8_t *slab[2];           /* device: two slots of slab_blobs blobs */
     int32_t slab_blobs;         /* blobs per slot (top_k + 1) */
+    moe_expert_cache *cache;    /* HBM expert cache used by moe_stream_token, or NULL */
 } moe_streamer;
 
 /*
@@ -274,7 +312,9 @@ int moe_host_free(void *p);
  *   1. moe_route on compute_stream; the K selections are copied to
  *      host_ids (pinned host, K int32) and the host waits for them;
  *   2. moe_stream_prefetch of those experts into slab slot s on
- *      copy_stream, after the streamed layer that last read the slot (j-2);
+ *      copy_stream, after the streamed layer that last read the slot (j-2)
+ *      (with st->cache set, cached experts are copied from HBM instead, see
+ *      moe_expert_cache);
  *   3. compute_stream waits for the copies, then moe_layer_step reads the
  *      slot (the step recomputes the same routing bit for bit);
  *   4. the shared expert of the next streamed layer (independent of

@@ -125,7 +125,7 @@ def test_stream_token_misuse_rejected():
     assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), ctypes.cast(bad_ev, ctypes.c_void_p))) \
         == ews.MOE_EINVAL
     resident = (ews.LayerDesc * 2)(mk(), mk(experts=1 << 20))
-    assert L.moe_stream_token(*args(resident, 2, ctypes.byref(st), evp)) == ews.MOE_EINVAL    # not streamed
+    assert L.moe_stream_token(*args(resident, 2, ctypes.byref(st), evp)) == ews.MOE_EINVAL    # resident, no shared
     other_k = (ews.LayerDesc * 2)(mk(), mk(top_k=3))
     assert L.moe_stream_token(*args(other_k, 2, ctypes.byref(st), evp)) == ews.MOE_EINVAL
     st.slab_blobs = K
@@ -134,6 +134,35 @@ def test_stream_token_misuse_rejected():
     small_ws = args(descs, 2, ctypes.byref(st), evp)
     small_ws = small_ws[:9] + (256,) + small_ws[10:]
     assert L.moe_stream_token(*small_ws) == ews.MOE_EINVAL                                    # workspace
+    # an expert cache that was not reset for this streamer
+    meta = (ctypes.c_uint64 * 64)()
+    cache = ews.ExpertCache(1 << 22, 4, ctypes.addressof(meta), 0, 0)
+    st.cache = ctypes.pointer(cache)
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp)) == ews.MOE_ESTATE
+    ews.moe_expert_cache_reset(cache, 1, E)                                                  # another layer count
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp)) == ews.MOE_ESTATE
+    cache.slots = None
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp)) == ews.MOE_ESTATE
+
+
+def test_expert_cache_meta_and_reset():
+    L = ews.lib()
+    assert ews.moe_expert_cache_meta_bytes(0, 2, 16) == 0
+    assert ews.moe_expert_cache_meta_bytes(4, 0, 16) == 0
+    n1 = ews.moe_expert_cache_meta_bytes(4, 2, 16)
+    # grows by 4 bytes per indexed blob (a layer's 16 routed experts and its
+    # shared one) and 16 per slot
+    assert ews.moe_expert_cache_meta_bytes(4, 3, 16) - n1 == 17 * 4
+    assert ews.moe_expert_cache_meta_bytes(5, 2, 16) - n1 == 16
+    meta = (ctypes.c_uint64 * (n1 // 8 + 1))()
+    c = ews.ExpertCache(1 << 22, 4, ctypes.addressof(meta), 7, 9)
+    ews.moe_expert_cache_reset(c, 2, 16)
+    assert (c.hits, c.misses) == (0, 0)
+    assert L.moe_expert_cache_reset(None, 2, 16) == ews.MOE_EINVAL
+    for bad in (ews.ExpertCache(None, 4, ctypes.addressof(meta), 0, 0), ews.ExpertCache(1 << 22, 4, None, 0, 0),
+                ews.ExpertCache(1 << 22, 0, ctypes.addressof(meta), 0, 0)):
+        assert L.moe_expert_cache_reset(ctypes.byref(bad), 2, 16) == ews.MOE_EINVAL
+    assert L.moe_expert_cache_reset(ctypes.byref(c), 0, 16) == ews.MOE_EINVAL
 
 
 def test_host_alloc_rejects_bad_arguments():

@@ -164,7 +164,9 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
     # so the default arena is 56 GiB, aliased
     want = (56 << 30) if arena_gb is None else int(arena_gb * 2**30)
     room = mem_available() - 32 * 2**30
-    P = int(min(full, max(E, min(want, room) // bb)))
+    # whole layers' worth of blobs, so that the zero-copy descriptors (each
+    # layer's experts contiguous in the arena) apply too
+    P = int(min(full, max(E, min(want, room) // bb))) // E * E
     st = None
     while st is None:
         log(f"streamed: pinning a {P * bb / 2**30:.1f} GiB host arena ({P} of {full} blobs; host MemAvailable "
@@ -177,7 +179,7 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
             if P <= E:
                 raise
             log(f"streamed: {err}; halving the arena")
-            P = max(E, P // 2)
+            P = max(E, P // 2 // E * E)
     log(f"streamed: pinned in {time.time() - t0:.1f} s")
     t0 = time.time()
     chunk = max(1, (2 << 30) // bb)
@@ -254,6 +256,36 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
     per_token = L * st.slab_blobs * bb
     gbs = per_token * tps / 1e9
     log(f"streamed: {tokens} tokens in {wall:.3f} s = {tps:.2f} tok/s, {gbs:.1f} GB/s over the link, flags {flags}")
+
+    # GPU-initiated streaming: the stack kernel reads the selected experts
+    # from the pinned arena itself (one launch per token, no copies, no host
+    # round trip per layer)
+    r.copy_(torch.from_numpy(v0.copy()).cuda().view(1, D))
+    x.copy_(r)
+    st.step_zero_copy(r, x)
+    torch.cuda.synchronize()
+    zc_same = bool(torch.equal(x, want)) and bool(torch.equal(st.topk_idx, resident.topk_idx))
+    if not zc_same:
+        raise SystemExit("zero-copy output differs from the resident stack holding the same bytes")
+    for t in range(warmup):
+        r.copy_(xin[t:t + 1])
+        x.copy_(xin[t:t + 1])
+        st.step_zero_copy(r, x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        r.copy_(xin[warmup + t:warmup + t + 1])
+        x.copy_(xin[warmup + t:warmup + t + 1])
+        st.step_zero_copy(r, x)
+    torch.cuda.synchronize()
+    zw = time.perf_counter() - t0
+    zflags = int(st.workspace[:4].view(torch.int32).item())
+    z_tps = tokens / zw
+    log(f"streamed: zero-copy (kernel loads from pinned host memory): {z_tps:.2f} tok/s, "
+        f"{per_token * z_tps / 1e9:.1f} GB/s over the link, flags {zflags}")
+    zero_copy = {"tokens_per_s": round(z_tps, 3), "ms_per_token": round(zw / tokens * 1e3, 3),
+                 "pcie_gbs": round(per_token * z_tps / 1e9, 2), "bitwise_equal_resident": zc_same,
+                 "device_flags": zflags}
 
     # hybrid residency: the first n layers keep their experts in HBM (the
     # resident arena, which now holds the same bytes), the rest stream
@@ -342,7 +374,7 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
             "pcie_peak_measured_gbs": round(link, 2), "pcie_frac_measured": round(gbs / link, 4),
             "h2d_large_copy_gbs": round(max(big), 2), "h2d_streamer_pattern_gbs": round(pattern, 2),
             "arena_blobs": P, "arena_aliased": P != full, "bitwise_equal_resident": identical,
-            "device_flags": flags, "hybrid": hybrid, "expert_cache": cache_out}
+            "device_flags": flags, "zero_copy": zero_copy, "hybrid": hybrid, "expert_cache": cache_out}
 
 
 def resident_extra(cfg, steps, warmup):

@@ -197,6 +197,30 @@ class StreamedStack:
     def cache(self):
         return getattr(self, "_cache", None)
 
+    def zero_copy_descs(self):
+        """Descriptors whose experts and shared expert are the pinned host
+        arenas themselves: the kernels' own loads fetch each selected expert
+        over the link (GPU-initiated streaming), so a token needs no copies
+        and no host round trip and runs as one persistent moe_stack_step
+        launch.  Layer l's E blobs must be contiguous in the arena, which
+        holds when arena_blobs is a multiple of n_experts."""
+        from . import make_desc
+        if self.P % self.E:
+            raise ValueError(f"arena_blobs {self.P} is not a multiple of n_experts {self.E}")
+        descs = [make_desc(hidden=self.D, n_experts=self.E, top_k=self.K, inter=self.I, n_shared=self.n_shared,
+                           bits=self.bits, group=self.group, rms_eps=self.eps, router_w=self.router[l],
+                           gamma=self.gamma[l], experts=self._arena.ptr + (l * self.E) % self.P * self.bb,
+                           shared=(self._shared.ptr + l * self.bb) if self.n_shared else None, blob_bytes=self.bb)
+                 for l in range(self.layers)]
+        return (LayerDesc * self.layers)(*descs)
+
+    def step_zero_copy(self, resid, x, stream=None):
+        """One token through every layer reading the experts from host
+        memory in the kernel (zero_copy_descs): one launch, no host wait."""
+        if getattr(self, "_zc", None) is None:
+            self._zc = self.zero_copy_descs()
+        moe_stack_step(self._zc, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
+
     def resident_layers(self) -> list[int]:
         return [l for l in range(self.layers) if self.descs[l].experts]
 

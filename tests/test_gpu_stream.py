@@ -198,3 +198,34 @@ def test_expert_cache_equals_resident(n_slots, pattern):
         assert cache.misses == len(set(keys))  # every repeat served from HBM
     st.enable_cache(0)
     assert st.streamer.cache is None or not st.streamer.cache
+
+
+@pytest.mark.parametrize("arena_blobs", [None, 32])
+def test_zero_copy_equals_resident(arena_blobs):
+    """GPU-initiated streaming: the stack kernel reads the selected experts
+    straight from the pinned host arena (one launch per token, no copies, no
+    host wait).  Outputs and selections equal the resident stack's holding
+    the same bytes, bit for bit, with a full and an aliased arena (32 blobs =
+    two layers' experts)."""
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=5, seed=0x5EED0E80)
+    print(f"[gpu case] zero-copy arena_blobs={arena_blobs}", flush=True)
+    st = W.build_streamed(cfg, layers=5, arena_blobs=arena_blobs)
+    rs = W.resident_twin(st)
+    v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
+    xz, xr = v.clone(), v.clone()
+    for t in range(3):
+        r_z, r_r = xz.clone(), xr.clone()
+        st.step_zero_copy(r_z, xz)
+        rs.step(r_r, xr)
+        torch.cuda.synchronize()
+        assert int(st.workspace[:4].view(torch.int32).item()) == 0
+        assert torch.equal(st.topk_idx, rs.topk_idx), t
+        assert torch.equal(st.topk_w, rs.topk_w), t
+        assert torch.equal(r_z, r_r) and torch.equal(xz, xr), t
+
+
+def test_zero_copy_needs_whole_layers():
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=3, seed=0x5EED0E81)
+    st = W.build_streamed(cfg, layers=3, arena_blobs=cfg.E + 3)
+    with pytest.raises(ValueError):
+        st.zero_copy_descs()

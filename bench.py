@@ -346,7 +346,7 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
                 x.copy_(r)
                 st.step(r, x)
             torch.cuda.synchronize()
-            h0, m0 = c.hits, c.misses
+            h0, m0, f0 = c.hits, c.misses, c.spec_fills
             t0 = time.perf_counter()
             for t in range(tokens):
                 r.copy_(inputs(warmup + t))
@@ -354,17 +354,41 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
                 st.step(r, x)
             torch.cuda.synchronize()
             w_ = time.perf_counter() - t0
-            h, m = c.hits - h0, c.misses - m0
+            h, m, f = c.hits - h0, c.misses - m0, c.spec_fills - f0
             return {"tokens_per_s": round(tokens / w_, 3), "ms_per_token": round(w_ / tokens * 1e3, 3),
-                    "hit_rate": round(h / max(1, h + m), 4), "pcie_bytes_per_token": int(m / tokens * bb)}
+                    "hit_rate": round(h / max(1, h + m), 4), "pcie_bytes_per_token": int((m + f) / tokens * bb),
+                    "speculative_fills_per_token": round(f / tokens, 2)}
         fresh = timed(lambda t: xin[t:t + 1])
         repeat = timed(lambda t: v0t)
+        # the same fresh inputs with the temporal guess of the next layer's experts
+        c.speculate = 1
+        spec = timed(lambda t: xin[t:t + 1])
+        c.speculate = 0
         cflags = int(st.workspace[:4].view(torch.int32).item())
+        # a cache smaller than one token's blobs (half of L * (K + 1)): LRU
+        # alone keeps little, the guess fetches the next layer's likely
+        # experts while the current layer runs
+        small = {}
+        st.enable_cache(0)
+        c = st.enable_cache(L * (cfg.K + cfg.n_shared) // 2)
+        small["slots"] = c.n_slots
+        small["fresh_inputs"] = timed(lambda t: xin[t:t + 1])
+        c.speculate = 1
+        small["fresh_inputs_speculative"] = timed(lambda t: xin[t:t + 1])
+        cflags |= int(st.workspace[:4].view(torch.int32).item())
+        log(f"streamed: expert cache of {c.n_slots} blobs: fresh inputs {small['fresh_inputs']['tokens_per_s']:.2f} "
+            f"tok/s at {small['fresh_inputs']['hit_rate']:.1%} hits; with the next-layer guess "
+            f"{small['fresh_inputs_speculative']['tokens_per_s']:.2f} tok/s at "
+            f"{small['fresh_inputs_speculative']['hit_rate']:.1%} hits, "
+            f"{small['fresh_inputs_speculative']['speculative_fills_per_token']:.1f} guessed blobs per token")
         log(f"streamed: expert cache of {n_slots} blobs ({n_slots * bb / 2**30:.1f} GiB HBM): fresh inputs "
             f"{fresh['tokens_per_s']:.2f} tok/s at {fresh['hit_rate']:.1%} hits; one input repeated "
-            f"{repeat['tokens_per_s']:.2f} tok/s at {repeat['hit_rate']:.1%} hits, flags {cflags}")
+            f"{repeat['tokens_per_s']:.2f} tok/s at {repeat['hit_rate']:.1%} hits; fresh inputs with the "
+            f"next-layer guess {spec['tokens_per_s']:.2f} tok/s at {spec['hit_rate']:.1%} hits, "
+            f"{spec['speculative_fills_per_token']:.1f} guessed blobs per token, flags {cflags}")
         cache_out = {"slots": n_slots, "hbm_bytes": n_slots * bb, "policy": "LRU over (layer, expert)",
-                     "fresh_inputs": fresh, "repeated_input": repeat, "bitwise_equal_resident": same,
+                     "fresh_inputs": fresh, "repeated_input": repeat, "fresh_inputs_speculative": spec,
+                     "small_cache": small, "bitwise_equal_resident": same,
                      "device_flags": cflags}
         st.enable_cache(0)
     return {"workload": f"{L}-layer {cfg.bits}-bit stack, experts in pinned host RAM, K={cfg.K} + {cfg.n_shared} "

@@ -37,7 +37,8 @@ class LayerDesc(ctypes.Structure):
 
 class ExpertCache(ctypes.Structure):
     _fields_ = [("slots", ctypes.c_void_p), ("n_slots", ctypes.c_int32), ("meta", ctypes.c_void_p),
-                ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64)]
+                ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64), ("speculate", ctypes.c_int32),
+                ("spec_fills", ctypes.c_uint64)]
 
 
 class Streamer(ctypes.Structure):

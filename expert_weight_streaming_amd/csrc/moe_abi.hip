@@ -491,15 +491,16 @@ int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t 
 // ---- HBM expert cache: host metadata laid out in the caller's meta block
 //   CacheHead | tag[n_slots] (int64 key, -1 free) | where[L*E + L] (int32:
 //   slot, -1 not cached) | prev[n_slots] | next[n_slots] (LRU list, most
-//   recent first).  Keys: layer*E + e for routed expert e of a layer,
-//   L*E + layer for the layer's shared expert.
+//   recent first) | pred[L][kMaxTopK] (int32: the previous token's
+//   selection per layer, -1 none).  Keys: layer*E + e for routed expert e of
+//   a layer, L*E + layer for the layer's shared expert.
 struct CacheHead {
     int32_t n_layers, n_experts, n_slots, head, tail, pad;
 };
 struct CacheView {
     CacheHead *h;
     int64_t *tag;
-    int32_t *where, *prev, *next;
+    int32_t *where, *prev, *next, *pred;
 };
 static CacheView cache_view(void *meta, int32_t n_slots, int32_t n_layers, int32_t n_experts)
 {
@@ -510,6 +511,7 @@ static CacheView cache_view(void *meta, int32_t n_slots, int32_t n_layers, int32
     v.where = reinterpret_cast<int32_t *>(v.tag + n_slots);
     v.prev = v.where + (size_t)n_layers * (n_experts + 1);
     v.next = v.prev + n_slots;
+    v.pred = v.next + n_slots;
     return v;
 }
 static void lru_unlink(CacheView &v, int32_t s)
@@ -530,7 +532,8 @@ static void lru_push_front(CacheView &v, int32_t s)
 size_t moe_expert_cache_meta_bytes(int32_t n_slots, int32_t n_layers, int32_t n_experts)
 {
     if (n_slots <= 0 || n_layers <= 0 || n_experts <= 0) return 0;
-    return sizeof(CacheHead) + (size_t)n_slots * 8 + (size_t)n_layers * (n_experts + 1) * 4 + (size_t)n_slots * 8;
+    return sizeof(CacheHead) + (size_t)n_slots * 8 + (size_t)n_layers * (n_experts + 1) * 4 + (size_t)n_slots * 8 +
+           (size_t)n_layers * moe::kMaxTopK * 4;
 }
 
 int moe_expert_cache_reset(moe_expert_cache *c, int32_t n_layers, int32_t n_experts)
@@ -545,7 +548,8 @@ int moe_expert_cache_reset(moe_expert_cache *c, int32_t n_layers, int32_t n_expe
         lru_push_front(v, s);
     }
     for (size_t k = 0; k < (size_t)n_layers * (n_experts + 1); ++k) v.where[k] = -1;
-    c->hits = c->misses = 0;
+    for (size_t k = 0; k < (size_t)n_layers * moe::kMaxTopK; ++k) v.pred[k] = -1;
+    c->hits = c->misses = c->spec_fills = 0;
     return MOE_OK;
 }
 
@@ -696,6 +700,11 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
             return hip_fail(e, "selection copy");
         if ((e = hipEventRecord(route_done, cs)) != hipSuccess) return hip_fail(e, "event record");
         if ((e = hipEventSynchronize(route_done)) != hipSuccess) return hip_fail(e, "selection wait");
+        if (moe_expert_cache *c = st->cache) {
+            // this token's selection: the next token's guess for layer l
+            int32_t *pred = cache_view(c->meta, c->n_slots, st->n_layers, st->n_experts).pred + (size_t)l * moe::kMaxTopK;
+            for (int k = 0; k < K; ++k) pred[k] = host_ids[k];
+        }
         // 2. the selected experts into slot s, after the kernel that last read it (streamed layer j-2)
         if (j >= 2 && (e = hipStreamWaitEvent(ps, compute_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
         rc = prefetch_impl(st, l, host_ids, K, s, j == 0 ? with_shared : 0, copy_stream, copy_done[s], true);
@@ -714,6 +723,28 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
             if (j >= 1 && (e = hipStreamWaitEvent(ps, compute_done[s1], 0)) != hipSuccess) return hip_fail(e, "wait");
             rc = prefetch_impl(st, ln, nullptr, 0, s1, 1, copy_stream, nullptr, true);
             if (rc) return rc;
+        }
+        // 5. the guess for the next streamed layer (the previous token's
+        // selection there) into the cache, behind every copy above
+        if (moe_expert_cache *c = st->cache; c && c->speculate && ln < n_layers) {
+            CacheView v = cache_view(c->meta, c->n_slots, st->n_layers, st->n_experts);
+            const uint64_t bb = st->blob_bytes;
+            for (int k = 0; k < K; ++k) {
+                const int32_t pe = v.pred[(size_t)ln * moe::kMaxTopK + k];
+                if (pe < 0 || pe >= st->n_experts) continue;
+                const int64_t key = (int64_t)ln * st->n_experts + pe;
+                if (v.where[key] >= 0) continue;
+                const int32_t slot_c = v.h->tail;
+                if (v.tag[slot_c] >= 0) v.where[v.tag[slot_c]] = -1;
+                v.tag[slot_c] = key;
+                v.where[key] = slot_c;
+                lru_unlink(v, slot_c);
+                lru_push_front(v, slot_c);
+                if ((e = hipMemcpyAsync(c->slots + (uint64_t)slot_c * bb, st->host_arena + (uint64_t)(key % st->arena_blobs) * bb,
+                                        bb, hipMemcpyHostToDevice, ps)) != hipSuccess)
+                    return hip_fail(e, "speculative copy");
+                ++c->spec_fills;
+            }
         }
         ++j;
     }

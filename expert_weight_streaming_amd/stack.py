@@ -171,11 +171,14 @@ class StreamedStack:
                                   shared=shared if resident and self.n_shared else None,
                                   slab=None if resident else self.slab[0], blob_bytes=self.bb)
 
-    def enable_cache(self, n_slots: int):
-        """An HBM cache of n_slots routed expert blobs for the streamed
-        layers (moe_expert_cache): moe_stream_token copies cached experts
-        device to device and fills the least recently used slot on a miss.
-        enable_cache(0) removes it.  Returns the cache (hits, misses)."""
+    def enable_cache(self, n_slots: int, speculate: bool = False):
+        """An HBM cache of n_slots expert blobs for the streamed layers
+        (moe_expert_cache): moe_stream_token copies cached experts device to
+        device and fills the least recently used slot on a miss; with
+        speculate, it also copies the previous token's selection of the next
+        streamed layer into the cache ahead of that layer's routing.
+        enable_cache(0) removes it.  Returns the cache (hits, misses,
+        spec_fills)."""
         import numpy as np
         from . import ExpertCache, moe_expert_cache_meta_bytes, moe_expert_cache_reset
         if n_slots <= 0:
@@ -188,6 +191,7 @@ class StreamedStack:
                                     dtype=np.uint64)
         c = ExpertCache()
         c.slots, c.n_slots, c.meta = self._cache_slots.data_ptr(), n_slots, self._cache_meta.ctypes.data
+        c.speculate = 1 if speculate else 0
         moe_expert_cache_reset(c, self.layers, self.E)
         self._cache = c
         self.streamer.cache = ctypes.pointer(c)

@@ -242,6 +242,14 @@ int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t 
  *           LRU list, written by moe_expert_cache_reset and moe_stream_token
  *   hits, misses: blobs served from the cache / over the link
  *           (moe_expert_cache_reset clears them)
+ *   speculate: when nonzero, right after a streamed layer's copies are
+ *           queued, the routed experts the previous token selected in the
+ *           next streamed layer (a temporal guess of the routing; the same
+ *           article lists route prediction among the variants that were
+ *           slower than the page cache there) that are not cached are
+ *           copied host -> HBM into the cache, ahead of that layer's own
+ *           routing
+ *   spec_fills: blobs copied by that guess (moe_expert_cache_reset clears it)
  * moe_stream_prefetch itself never uses the cache.  A cache belongs to one
  * streamer (its n_layers and n_experts) and to one thread at a time.
  */
@@ -251,6 +259,8 @@ typedef struct moe_expert_cache {
     void *meta;
     uint64_t hits;
     uint64_t misses;
+    int32_t speculate;
+    uint64_t spec_fills;
 } moe_expert_cache;
 
 /* Bytes of host metadata for a cache of n_slots blobs over n_layers x

@@ -151,13 +151,13 @@ def test_expert_cache_meta_and_reset():
     assert ews.moe_expert_cache_meta_bytes(4, 0, 16) == 0
     n1 = ews.moe_expert_cache_meta_bytes(4, 2, 16)
     # grows by 4 bytes per indexed blob (a layer's 16 routed experts and its
-    # shared one) and 16 per slot
-    assert ews.moe_expert_cache_meta_bytes(4, 3, 16) - n1 == 17 * 4
+    # shared one) and per remembered selection (8 per layer), 16 per slot
+    assert ews.moe_expert_cache_meta_bytes(4, 3, 16) - n1 == (17 + 8) * 4
     assert ews.moe_expert_cache_meta_bytes(5, 2, 16) - n1 == 16
     meta = (ctypes.c_uint64 * (n1 // 8 + 1))()
-    c = ews.ExpertCache(1 << 22, 4, ctypes.addressof(meta), 7, 9)
+    c = ews.ExpertCache(1 << 22, 4, ctypes.addressof(meta), 7, 9, 1, 5)
     ews.moe_expert_cache_reset(c, 2, 16)
-    assert (c.hits, c.misses) == (0, 0)
+    assert (c.hits, c.misses, c.spec_fills, c.speculate) == (0, 0, 0, 1)
     assert L.moe_expert_cache_reset(None, 2, 16) == ews.MOE_EINVAL
     for bad in (ews.ExpertCache(None, 4, ctypes.addressof(meta), 0, 0), ews.ExpertCache(1 << 22, 4, None, 0, 0),
                 ews.ExpertCache(1 << 22, 0, ctypes.addressof(meta), 0, 0)):

@@ -141,40 +141,48 @@ def test_hybrid_residency_equals_resident(pattern):
     assert torch.equal(xs, xr)
 
 
-def _lru(keys, n_slots):
-    """Hits and misses of an LRU cache of n_slots over the key sequence."""
+def _lru(events, n_slots):
+    """Hits, misses and speculative fills of an LRU cache of n_slots over a
+    sequence of ("get", key) requests and ("fill", key) guesses (a guess
+    fills an uncached key and leaves a cached one alone)."""
     from collections import OrderedDict
-    od, hits, misses = OrderedDict(), 0, 0
-    for k in keys:
+    od, hits, misses, fills = OrderedDict(), 0, 0, 0
+    for kind, k in events:
         if k in od:
-            hits += 1
-            od.move_to_end(k)
-        else:
+            if kind == "get":
+                hits += 1
+                od.move_to_end(k)
+            continue
+        if kind == "get":
             misses += 1
-            if len(od) >= n_slots:
-                od.popitem(last=False)
-            od[k] = True
-    return hits, misses
+        else:
+            fills += 1
+        if len(od) >= n_slots:
+            od.popitem(last=False)
+        od[k] = True
+    return hits, misses, fills
 
 
-@pytest.mark.parametrize("n_slots,pattern", [(5, "SSSS"), (64, "SSSS"), (3, "SRSS")])
-def test_expert_cache_equals_resident(n_slots, pattern):
+@pytest.mark.parametrize("n_slots,pattern,speculate", [(5, "SSSS", False), (64, "SSSS", False), (3, "SRSS", False),
+                                                       (6, "SSSS", True), (64, "SRSS", True)])
+def test_expert_cache_equals_resident(n_slots, pattern, speculate):
     """The HBM expert cache: outputs equal the resident stack's bit for bit
     (cached blobs come from HBM, missed ones over the link), and the hit and
     miss counts equal an LRU of n_slots over the streamed blobs in the order
     the token pipeline requests them: a streamed layer's selections (the
     first streamed layer's shared blob right after them), then the next
-    streamed layer's shared blob.  Tokens repeat, so a cache that holds
-    every blob serves the repeats entirely from HBM."""
+    streamed layer's shared blob, then (speculate) the previous token's
+    selection of that layer as guesses.  Tokens repeat, so a cache that
+    holds every blob serves the repeats entirely from HBM."""
     cfg = seedgen.CONFIGS["tiny"].replace(layers=len(pattern), seed=0x5EED0E70)
-    print(f"[gpu case] expert cache slots={n_slots} {pattern}", flush=True)
+    print(f"[gpu case] expert cache slots={n_slots} {pattern} speculate={speculate}", flush=True)
     st = W.build_streamed(cfg, layers=len(pattern), arena_blobs=31)
     rs = W.resident_twin(st)
     for l, c in enumerate(pattern):
         if c == "R":
             st.set_resident(l, rs.arena.data_ptr() + l * st.E * st.bb, rs.shared.data_ptr() + l * st.bb)
-    cache = st.enable_cache(n_slots)
-    keys = []
+    cache = st.enable_cache(n_slots, speculate=speculate)
+    events, pred = [], {}
     inputs = [seedgen.activation(cfg, t) for t in (0, 1, 0, 0, 1)]
     for t, v0 in enumerate(inputs):
         v = torch.from_numpy(v0).cuda().view(1, -1)
@@ -187,15 +195,21 @@ def test_expert_cache_equals_resident(n_slots, pattern):
         assert torch.equal(r_s, r_r) and torch.equal(x_s, x_r), t
         sel = st.topk_idx.cpu().numpy()
         streamed = [l for l, c in enumerate(pattern) if c == "S"]
+        LE = len(pattern) * cfg.E
         for j, l in enumerate(streamed):
-            keys += [l * cfg.E + int(e) for e in sel[l, 0]]
+            events += [("get", l * cfg.E + int(e)) for e in sel[l, 0]]
             if j == 0:
-                keys.append(len(pattern) * cfg.E + l)        # its own shared blob
+                events.append(("get", LE + l))                  # its own shared blob
+            pred[l] = [int(e) for e in sel[l, 0]]
             if j + 1 < len(streamed):
-                keys.append(len(pattern) * cfg.E + streamed[j + 1])  # the next streamed layer's
-    assert (cache.hits, cache.misses) == _lru(keys, n_slots)
-    if n_slots >= len(set(keys)):
-        assert cache.misses == len(set(keys))  # every repeat served from HBM
+                ln = streamed[j + 1]
+                events.append(("get", LE + ln))                 # the next streamed layer's shared blob
+                if speculate and ln in pred:
+                    events += [("fill", ln * cfg.E + e) for e in pred[ln]]
+    assert (cache.hits, cache.misses, cache.spec_fills) == _lru(events, n_slots)
+    keys = {k for kind, k in events if kind == "get"}
+    if n_slots >= len(keys):
+        assert cache.misses == len(keys)  # every repeat served from HBM
     st.enable_cache(0)
     assert st.streamer.cache is None or not st.streamer.cache
 

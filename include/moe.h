@@ -20,7 +20,9 @@
  *  - Status: MOE_OK (0) or a negative MOE_E* code.  On an error nothing has
  *    been enqueued.  moe_last_error() gives a message for the calling thread.
  *  - Memory: every buffer belongs to the caller.  The library allocates and
- *    frees nothing.  Pointers are device pointers unless marked "host".
+ *    frees nothing, except the pinned host memory that moe_host_alloc and
+ *    moe_host_free exist for.  Pointers are device pointers unless marked
+ *    "host".
  *  - Asynchrony: calls enqueue work on the given HIP stream (passed as
  *    void*, a hipStream_t; NULL = the legacy default stream) and return;
  *    results are valid once the stream has been synchronised.  No call
@@ -97,7 +99,11 @@ typedef struct moe_layer_desc {
     const float *router_w; /* [E][D] fp32 row-major */
     const float *gamma;    /* [D] fp32 RMSNorm weight */
     /* Resident mode: E canonical blobs, blob_bytes apart, expert e at
-     * experts + e*blob_bytes, and the shared blob at `shared`.
+     * experts + e*blob_bytes, and the shared blob at `shared`.  Both may
+     * also point into pinned host memory from moe_host_alloc (mapped into
+     * the device's address space): the kernels then read the selected
+     * experts over the host link themselves (zero-copy streaming, one
+     * launch per token with moe_stack_step, no copies, no host wait).
      * Streamed mode: experts == NULL and slab != NULL: slab holds top_k+1
      * blobs, blob_bytes apart: slot k = the token's k-th selected expert,
      * slot top_k = the shared expert (streamed mode needs n_tokens == 1). */
@@ -225,7 +231,7 @@ int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t 
  * is being computed on.
  */
 /*
- * HBM-side cache of routed expert blobs for the streamed layers, the analog
+ * HBM-side cache of expert blobs for the streamed layers, the analog
  * of the page cache that serves most expert reads on the pages' machine
  * (toolarium.ru, "Flash-MoE: чистый C, Metal и никакого Python": caching is
  * left to the OS page cache, which hits about 71% of reads).  n_slots blobs

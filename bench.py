@@ -283,8 +283,34 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
     z_tps = tokens / zw
     log(f"streamed: zero-copy (kernel loads from pinned host memory): {z_tps:.2f} tok/s, "
         f"{per_token * z_tps / 1e9:.1f} GB/s over the link, flags {zflags}")
+    # zero-copy with the first half of the layers in HBM (per-layer residency, still one launch per token)
+    n_res = L // 2
+    zh = st.zero_copy_hybrid_descs(n_res, lambda l: resident.arena.data_ptr() + l * E * bb,
+                                   lambda l: resident.shared.data_ptr() + l * bb)
+    r.copy_(torch.from_numpy(v0.copy()).cuda().view(1, D))
+    x.copy_(r)
+    st.step_zero_copy(r, x, descs=zh)
+    torch.cuda.synchronize()
+    zh_same = bool(torch.equal(x, want)) and bool(torch.equal(st.topk_idx, resident.topk_idx))
+    if not zh_same:
+        raise SystemExit("zero-copy hybrid output differs from the resident stack")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        r.copy_(xin[warmup + t:warmup + t + 1])
+        x.copy_(xin[warmup + t:warmup + t + 1])
+        st.step_zero_copy(r, x, descs=zh)
+    torch.cuda.synchronize()
+    zhw = time.perf_counter() - t0
+    zflags |= int(st.workspace[:4].view(torch.int32).item())
+    zh_bytes = (L - n_res) * st.slab_blobs * bb
+    log(f"streamed: zero-copy with {n_res} of {L} layers in HBM: {tokens / zhw:.2f} tok/s, "
+        f"{zh_bytes * tokens / zhw / 1e9:.1f} GB/s over the link")
     zero_copy = {"tokens_per_s": round(z_tps, 3), "ms_per_token": round(zw / tokens * 1e3, 3),
                  "pcie_gbs": round(per_token * z_tps / 1e9, 2), "bitwise_equal_resident": zc_same,
+                 "hybrid": {"resident_layers": n_res, "tokens_per_s": round(tokens / zhw, 3),
+                            "pcie_bytes_per_token": zh_bytes, "pcie_gbs": round(zh_bytes * tokens / zhw / 1e9, 2),
+                            "bitwise_equal_resident": zh_same},
                  "device_flags": zflags}
 
     # hybrid residency: the first n layers keep their experts in HBM (the

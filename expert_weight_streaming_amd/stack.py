@@ -218,12 +218,28 @@ class StreamedStack:
                  for l in range(self.layers)]
         return (LayerDesc * self.layers)(*descs)
 
-    def step_zero_copy(self, resid, x, stream=None):
+    def zero_copy_hybrid_descs(self, n_resident, experts_of, shared_of):
+        """zero_copy_descs with layers 0..n_resident-1 reading HBM instead:
+        experts_of(l) / shared_of(l) give their device addresses (the same
+        bytes as the host arena's for that layer).  One launch per token
+        still, no copies."""
+        from . import make_desc
+        zc = self.zero_copy_descs()
+        for l in range(n_resident):
+            zc[l] = make_desc(hidden=self.D, n_experts=self.E, top_k=self.K, inter=self.I, n_shared=self.n_shared,
+                              bits=self.bits, group=self.group, rms_eps=self.eps, router_w=self.router[l],
+                              gamma=self.gamma[l], experts=experts_of(l),
+                              shared=shared_of(l) if self.n_shared else None, blob_bytes=self.bb)
+        return zc
+
+    def step_zero_copy(self, resid, x, stream=None, descs=None):
         """One token through every layer reading the experts from host
         memory in the kernel (zero_copy_descs): one launch, no host wait."""
-        if getattr(self, "_zc", None) is None:
-            self._zc = self.zero_copy_descs()
-        moe_stack_step(self._zc, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
+        if descs is None:
+            if getattr(self, "_zc", None) is None:
+                self._zc = self.zero_copy_descs()
+            descs = self._zc
+        moe_stack_step(descs, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
 
     def resident_layers(self) -> list[int]:
         return [l for l in range(self.layers) if self.descs[l].experts]

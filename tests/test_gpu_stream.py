@@ -236,6 +236,15 @@ def test_zero_copy_equals_resident(arena_blobs):
         assert torch.equal(st.topk_idx, rs.topk_idx), t
         assert torch.equal(st.topk_w, rs.topk_w), t
         assert torch.equal(r_z, r_r) and torch.equal(xz, xr), t
+    # layers 0 and 1 from HBM (the twin's arena), the rest from host memory, one launch
+    zh = st.zero_copy_hybrid_descs(2, lambda l: rs.arena.data_ptr() + l * st.E * st.bb,
+                                   lambda l: rs.shared.data_ptr() + l * st.bb)
+    r_z, r_r = xz.clone(), xr.clone()
+    st.step_zero_copy(r_z, xz, descs=zh)
+    rs.step(r_r, xr)
+    torch.cuda.synchronize()
+    assert torch.equal(st.topk_idx, rs.topk_idx)
+    assert torch.equal(r_z, r_r) and torch.equal(xz, xr)
 
 
 def test_zero_copy_needs_whole_layers():

@@ -32,7 +32,7 @@ class LayerDesc(ctypes.Structure):
                 ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("router_w", ctypes.c_void_p),
                 ("gamma", ctypes.c_void_p), ("experts", ctypes.c_void_p), ("shared", ctypes.c_void_p),
-                ("slab", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64)]
+                ("slab", ctypes.c_void_p), ("blob_bytes", ctypes.c_uint64), ("expert_addr", ctypes.c_void_p)]
 
 
 class ExpertCache(ctypes.Structure):
@@ -122,10 +122,10 @@ def _check(rc: int) -> None:
 
 
 def make_desc(*, hidden, n_experts, top_k, inter, n_shared, bits, group=64, rms_eps=1e-6, router_w, gamma,
-              experts=None, shared=None, slab=None, blob_bytes=None) -> LayerDesc:
+              experts=None, shared=None, slab=None, blob_bytes=None, expert_addr=None) -> LayerDesc:
     bb = blob_bytes if blob_bytes is not None else moe_blob_bytes(hidden, inter, bits, group)
     return LayerDesc(hidden, n_experts, top_k, inter, n_shared, bits, group, rms_eps, _ptr(router_w), _ptr(gamma),
-                     _ptr(experts), _ptr(shared), _ptr(slab), bb)
+                     _ptr(experts), _ptr(shared), _ptr(slab), bb, _ptr(expert_addr))
 
 
 def moe_blob_bytes(hidden: int, inter: int, bits: int, group: int = 64) -> int:

@@ -58,6 +58,14 @@ int check_desc(const moe_layer_desc *d, int32_t T)
                     (unsigned long long)blob_bytes_of(d->hidden, d->inter, d->bits, d->group));
     if (!d->router_w || !aligned16(d->router_w)) return fail(MOE_EINVAL, "router_w NULL or not 16-byte aligned");
     if (!d->gamma || !aligned16(d->gamma)) return fail(MOE_EINVAL, "gamma NULL or not 16-byte aligned");
+    if (d->expert_addr) {
+        if (d->experts || d->slab) return fail(MOE_EINVAL, "expert_addr excludes experts and slab");
+        if (!aligned16(d->expert_addr)) return fail(MOE_EINVAL, "expert_addr not 16-byte aligned");
+        if (d->n_shared && (!d->shared || !aligned16(d->shared)))
+            return fail(MOE_EINVAL, "n_shared=1 needs a 16-byte aligned shared blob");
+        if (T != 1) return fail(MOE_EUNSUPPORTED, "address-table mode takes one token per call");
+        return MOE_OK;
+    }
     const bool streamed = d->experts == nullptr;
     if (streamed) {
         if (!d->slab || !aligned16(d->slab)) return fail(MOE_EINVAL, "streamed mode needs a 16-byte aligned slab");
@@ -214,19 +222,23 @@ int enqueue_forward(const moe_layer_desc *d, const float *x, const int32_t *idx,
 moe::StackLayer stack_layer(const moe_layer_desc *d)
 {
     moe::StackLayer y;
+    const bool on_device = d->experts || d->expert_addr;
     y.router = d->router_w;
     y.gamma = d->gamma;
     y.experts = d->experts;
-    y.shared = d->experts ? d->shared : nullptr;
-    y.slab = d->experts ? nullptr : d->slab;
+    y.addr = d->expert_addr;
+    y.shared = on_device ? d->shared : nullptr;
+    y.slab = on_device ? nullptr : d->slab;
     return y;
 }
 
-hipError_t stack_plan_or_launch(const moe::StackArgs *a, const moe_layer_desc *d, hipStream_t s, moe::LayerPlan *p)
+// tables: some layer of the launch is in address-table mode
+hipError_t stack_plan_or_launch(const moe::StackArgs *a, const moe_layer_desc *d, bool tables, hipStream_t s,
+                                moe::LayerPlan *p)
 {
     const int S = d->top_k + d->n_shared;
-    return d->bits == 4 ? moe::stack_bits4(a, d->hidden, d->n_experts, d->inter, S, s, p)
-                        : moe::stack_bits2(a, d->hidden, d->n_experts, d->inter, S, s, p);
+    return d->bits == 4 ? moe::stack_bits4(a, d->hidden, d->n_experts, d->inter, S, tables, s, p)
+                        : moe::stack_bits2(a, d->hidden, d->n_experts, d->inter, S, tables, s, p);
 }
 
 // n layers of one token (batch 1).  Persistent launches of up to
@@ -238,10 +250,23 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
 {
     const moe_layer_desc *d = &ds[0];
     const int D = d->hidden, K = d->top_k;
+    for (int32_t j = 0; j < n; ++j)
+        if (ds[j].expert_addr) {
+            // address tables are read by the fused kernel only
+            moe::LayerPlan p;
+            hipError_t e = stack_plan_or_launch(nullptr, d, true, s, &p);
+            if (e != hipSuccess) return hip_fail(e, "stack plan");
+            if (p.grid == 0) return fail(MOE_EUNSUPPORTED, "address-table mode needs the fused stack, which this shape has no plan for");
+            break;
+        }
     for (int32_t l0 = 0; l0 < n; l0 += moe::kMaxStackLayers) {
         const int cnt = n - l0 < moe::kMaxStackLayers ? n - l0 : moe::kMaxStackLayers;
         moe::StackArgs a;
-        for (int j = 0; j < cnt; ++j) a.layer[j] = stack_layer(&ds[l0 + j]);
+        bool tables = false;
+        for (int j = 0; j < cnt; ++j) {
+            a.layer[j] = stack_layer(&ds[l0 + j]);
+            tables = tables || ds[l0 + j].expert_addr;
+        }
         a.resid = resid;
         a.x = x;
         a.topk_idx = idx + (size_t)l0 * K;
@@ -263,7 +288,7 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
         a.n_slots = K + d->n_shared;
         a.eps = d->rms_eps;
         moe::LayerPlan p;
-        hipError_t e = stack_plan_or_launch(&a, d, s, &p);
+        hipError_t e = stack_plan_or_launch(&a, d, tables, s, &p);
         if (e == hipSuccess) continue;
         if (e != hipErrorNotSupported) return hip_fail(e, "stack launch");
         // no resident-grid plan for this shape: three launches per layer
@@ -388,6 +413,7 @@ int moe_expert_forward(const moe_layer_desc *desc, const float *x, int32_t n_tok
         (rc = check_ptr(y, "y")))
         return rc;
     if ((rc = check_ws(desc, n_tokens, workspace, ws_bytes))) return rc;
+    if (desc->expert_addr) return fail(MOE_EUNSUPPORTED, "moe_expert_forward does not take address-table mode");
     const moe::WsLayout L = layout(desc, n_tokens);
     if (n_tokens > 1) {
         moe::BatchArgs b = batch_args(desc, n_tokens, x, const_cast<int32_t *>(topk_idx), const_cast<float *>(topk_w),
@@ -460,7 +486,7 @@ int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out)
     if (rc) return rc;
     if (!out) return fail(MOE_EINVAL, "out is NULL");
     moe::LayerPlan p;
-    hipError_t e = stack_plan_or_launch(nullptr, desc, nullptr, &p);
+    hipError_t e = stack_plan_or_launch(nullptr, desc, desc->expert_addr != nullptr, nullptr, &p);
     if (e != hipSuccess) return hip_fail(e, "layer plan");
     out[0] = p.grid > 0 && n_tokens == 1 ? 1 : 0;
     out[1] = p.grid;
@@ -657,7 +683,7 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
     for (int32_t l = 0; l < n_layers; ++l) {
         if (layers[l].top_k != K || layers[l].n_shared != with_shared)
             return fail(MOE_EINVAL, "layer %d has another top_k / n_shared", l);
-        if (layers[l].experts) {
+        if (layers[l].experts || layers[l].expert_addr) {
             // a resident layer: its experts (and shared expert) in HBM
             if (int rc = check_desc(&layers[l], 1)) return rc;
             continue;
@@ -684,7 +710,7 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
     for (int32_t l = 0; l < n_layers; ++l) {
         int32_t *idx = topk_idx + (size_t)l * K;
         float *w = topk_w + (size_t)l * K;
-        if (layers[l].experts) {
+        if (layers[l].experts || layers[l].expert_addr) {
             // resident: routing and experts stay on the device, no host wait
             int rc = moe_layer_step(&layers[l], resid, x, 1, idx, w, workspace, ws_bytes, compute_stream);
             if (rc) return rc;
@@ -717,7 +743,7 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
         // 4. the next streamed layer's shared expert needs no routing: queue
         // it behind this layer's copies, into the slot that layer will use
         int32_t ln = l + 1;
-        while (ln < n_layers && layers[ln].experts) ++ln;
+        while (ln < n_layers && (layers[ln].experts || layers[ln].expert_addr)) ++ln;
         if (with_shared && ln < n_layers) {
             const int s1 = (j + 1) & 1;
             if (j >= 1 && (e = hipStreamWaitEvent(ps, compute_done[s1], 0)) != hipSuccess) return hip_fail(e, "wait");

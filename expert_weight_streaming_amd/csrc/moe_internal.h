@@ -155,8 +155,9 @@ constexpr int kStackThreads = 512;
 struct StackLayer {
     const float *router;     // [E][D]
     const float *gamma;      // [D]
-    const uint8_t *experts;  // resident arena of E blobs, or NULL (streamed)
-    const uint8_t *shared;   // resident shared blob, or NULL
+    const uint8_t *experts;  // resident arena of E blobs, or NULL
+    const uint64_t *addr;    // or: [E] blob addresses (HBM or pinned host), or NULL
+    const uint8_t *shared;   // shared blob (resident or address-table mode), or NULL
     const uint8_t *slab;     // streamed: slot k = selection k, slot K = shared
 };
 
@@ -218,8 +219,9 @@ __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bi
 // shape has no resident-grid plan (scratch or LDS limits).
 // a == NULL: only fill the plan (grid 0: no plan, the caller takes the
 // three-launch path).
-hipError_t stack_bits4(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p);
-hipError_t stack_bits2(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p);
+// tables: some layer of the launch is in address-table mode
+hipError_t stack_bits4(const StackArgs *a, int D, int E, int I, int S, bool tables, hipStream_t s, LayerPlan *p);
+hipError_t stack_bits2(const StackArgs *a, int D, int E, int I, int S, bool tables, hipStream_t s, LayerPlan *p);
 
 int down_blocks(int D, int I, int bits);
 int gate_up_blocks_per_slot(int I, int n_slots);

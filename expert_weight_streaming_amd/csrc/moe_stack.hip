@@ -79,12 +79,16 @@ __device__ __forceinline__ KArgs kargs()
     asm volatile("" : "+s"(p));
     return p;
 }
+// TBL: the launch has layers in address-table mode (a separate
+// instantiation, so that the other launches pay nothing for it)
+template <bool TBL>
 __device__ __forceinline__ StackLayer layer_of(KArgs A, int l)
 {
     StackLayer y;
     y.router = A->layer[l].router;
     y.gamma = A->layer[l].gamma;
     y.experts = A->layer[l].experts;
+    y.addr = TBL ? A->layer[l].addr : nullptr;
     y.shared = A->layer[l].shared;
     y.slab = A->layer[l].slab;
     return y;
@@ -114,6 +118,7 @@ __device__ __forceinline__ Views views(unsigned char *smem, int D, int E, int I,
 }
 
 // Slot k's blob of layer Ly under the selection sel (LDS).
+template <bool TBL>
 __device__ __forceinline__ const uint8_t *slot_blob(KArgs A, const StackLayer &Ly, const int *sel, int k)
 {
     const uint64_t bb = A->blob_bytes;
@@ -124,6 +129,8 @@ __device__ __forceinline__ const uint8_t *slot_blob(KArgs A, const StackLayer &L
         atomicOr(A->flags, MOE_DEVERR_EXPERT_RANGE);
         return nullptr;
     }
+    if constexpr (TBL)
+        if (Ly.addr) return reinterpret_cast<const uint8_t *>(Ly.addr[e]);
     return Ly.experts + (uint64_t)e * bb;
 }
 __device__ __forceinline__ const uint8_t *shared_blob(KArgs A, const StackLayer &Ly)
@@ -178,7 +185,7 @@ __device__ __forceinline__ float poll_residual(KArgs A, int q0, int D, int NB, u
     return t;
 }
 
-template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS>
+template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS, bool TBL>
 __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
 {
     using C = Codes<BITS>;
@@ -214,7 +221,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         const int NB = gridDim.x, b = blockIdx.x;
         const int D = A->D, E = A->E, I = A->I;
         const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rs = wave / RSL, sw = wave % RSL;
-        const StackLayer Ly = layer_of(A, l);
+        const StackLayer Ly = layer_of<TBL>(A, l);
         const int e = b + NB * rs;
         rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
         const int su = (wave - 1) * NB + b;
@@ -230,7 +237,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         const int NB = gridDim.x, b = blockIdx.x;
         const int gw = wave * NB + b, GW = NWB * NB;
         const int D = A->D, E = A->E, K = A->K, I = A->I, S = A->n_slots;
-        const StackLayer Ly = layer_of(A, l);
+        const StackLayer Ly = layer_of<TBL>(A, l);
         const Views v = views<BITS>(smem, D, E, I, S);
         int *sel = reinterpret_cast<int *>(v.misc);  // the block's selection [8]
         float *selw = v.misc + 8;                     // and its weights [8]
@@ -336,9 +343,9 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             const int upe = (I + RX - 1) / RX;
             for (int u = gw; u < K * upe; u += GW) {
                 const int k = u / upe, i0 = (u - k * upe) * RX;
-                if (Ly.experts) wait_selected(rdy, k, l + 1, A->flags);
+                if (TBL ? !Ly.slab : Ly.experts != nullptr) wait_selected(rdy, k, l + 1, A->flags);
                 GuRegs<BITS, GCPL, RX> gb;
-                gu_load<BITS, GCPL, RX>(gb, slot_blob(A, Ly, sel, k), D, I, i0, lane);
+                gu_load<BITS, GCPL, RX>(gb, slot_blob<TBL>(A, Ly, sel, k), D, I, i0, lane);
                 float hv[RX];
                 gu_finish_c<BITS, GCPL, RX>(gb, v.dig, v.csum, v.xcinv, D, lane, hv);
                 if (lane == 0) {
@@ -351,10 +358,10 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         // the down rows of every slot (first round): they stream while the
         // other blocks finish their gate/up rows
         DnRegs<BITS, DCPL> dn[MAXS];
-        if (Ly.experts) wait_selected(rdy, K - 1, l + 1, A->flags);
+        if (TBL ? !Ly.slab : Ly.experts != nullptr) wait_selected(rdy, K - 1, l + 1, A->flags);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k)
-            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? slot_blob(A, Ly, sel, k) : nullptr, D, I, gw * RPU, lane);
+            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? slot_blob<TBL>(A, Ly, sel, k) : nullptr, D, I, gw * RPU, lane);
 
         // ---- phase C: h of every slot (polled until all of it carries this
         // layer's epoch) as digit tables; then the next layer's router and
@@ -398,7 +405,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             if (j > 0) {
 #pragma unroll
                 for (int k = 0; k < MAXS; ++k)
-                    dn_load<BITS, LPR, DCPL>(dn[k], k < S ? slot_blob(A, Ly, sel, k) : nullptr, D, I, o0, lane);
+                    dn_load<BITS, LPR, DCPL>(dn[k], k < S ? slot_blob<TBL>(A, Ly, sel, k) : nullptr, D, I, o0, lane);
             }
             // slot partials weighted per lane, in slot order, then one
             // reduction over the row's lanes
@@ -477,10 +484,10 @@ struct StackPlanCache {
     int ready = 0, vgprs = 0, scratch = 0, n_cu = 0;
 };
 
-template <int GCPL, int RX, int LPR, int DCPL, int MAXS>
+template <int GCPL, int RX, int LPR, int DCPL, int MAXS, bool TBL>
 hipError_t stack_launch(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
 {
-    auto kern = k_stack<MOE_STACK_BITS, GCPL, RX, LPR, DCPL, MAXS>;
+    auto kern = k_stack<MOE_STACK_BITS, GCPL, RX, LPR, DCPL, MAXS, TBL>;
     static StackPlanCache cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -523,15 +530,15 @@ hipError_t stack_launch(const StackArgs *a, int D, int E, int I, int S, hipStrea
 // Shape -> instantiation.  Gate/up: GCPL chunks per lane and row, RX rows
 // per wave unit.  Down: the smallest power-of-two LPR >= the row's chunks
 // (8..64), DCPL chunks per lane.
-template <int GCPL>
+template <int GCPL, bool TBL>
 hipError_t stack_g(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
 {
     constexpr int RX = GCPL <= 2 ? 2 : 1;
     const int nch = I * MOE_STACK_BITS / 128;
     const bool wide = S > 5;
 #define MOE_S(LPR_, DCPL_)                                                                                              \
-    return wide ? stack_launch<GCPL, RX, LPR_, DCPL_, kMaxSlots>(a, D, E, I, S, s, p)                                   \
-                : stack_launch<GCPL, RX, LPR_, DCPL_, 5>(a, D, E, I, S, s, p);
+    return wide ? stack_launch<GCPL, RX, LPR_, DCPL_, kMaxSlots, TBL>(a, D, E, I, S, s, p)                              \
+                : stack_launch<GCPL, RX, LPR_, DCPL_, 5, TBL>(a, D, E, I, S, s, p);
     if (nch <= 8) MOE_S(8, 1)
     if (nch <= 16) MOE_S(16, 1)
     if (nch <= 32) MOE_S(32, 1)
@@ -542,20 +549,28 @@ hipError_t stack_g(const StackArgs *a, int D, int E, int I, int S, hipStream_t s
 
 }  // namespace
 
-#if MOE_STACK_BITS == 4
-hipError_t stack_bits4(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
-#else
-hipError_t stack_bits2(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
-#endif
+namespace {
+template <bool TBL>
+hipError_t stack_bits_t(const StackArgs *a, int D, int E, int I, int S, hipStream_t s, LayerPlan *p)
 {
     const int nch = D * MOE_STACK_BITS / 128;
-    if (nch <= 64) return stack_g<1>(a, D, E, I, S, s, p);
+    if (nch <= 64) return stack_g<1, TBL>(a, D, E, I, S, s, p);
     if constexpr (MOE_STACK_BITS == 4) {
-        if (nch <= 128) return stack_g<2>(a, D, E, I, S, s, p);
-        return stack_g<4>(a, D, E, I, S, s, p);
+        if (nch <= 128) return stack_g<2, TBL>(a, D, E, I, S, s, p);
+        return stack_g<4, TBL>(a, D, E, I, S, s, p);
     } else {
-        return stack_g<2>(a, D, E, I, S, s, p);
+        return stack_g<2, TBL>(a, D, E, I, S, s, p);
     }
+}
+}  // namespace
+
+#if MOE_STACK_BITS == 4
+hipError_t stack_bits4(const StackArgs *a, int D, int E, int I, int S, bool tables, hipStream_t s, LayerPlan *p)
+#else
+hipError_t stack_bits2(const StackArgs *a, int D, int E, int I, int S, bool tables, hipStream_t s, LayerPlan *p)
+#endif
+{
+    return tables ? stack_bits_t<true>(a, D, E, I, S, s, p) : stack_bits_t<false>(a, D, E, I, S, s, p);
 }
 
 }  // namespace moe

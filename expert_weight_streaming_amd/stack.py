@@ -241,6 +241,55 @@ class StreamedStack:
             descs = self._zc
         moe_stack_step(descs, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
 
+    # ---- per-expert residency through device address tables (one launch per token)
+    def host_addr(self, l: int, e: int) -> int:
+        return self._arena.ptr + ((l * self.E + e) % self.P) * self.bb
+
+    def place_experts(self, n_slots: int, hot, shared_in_hbm: bool = True):
+        """Per-expert residency: the (layer, expert) pairs in `hot` (most
+        wanted first; at most n_slots of them) get a copy in an HBM pool of
+        n_slots blobs, every other expert is read from the pinned host arena
+        by the kernel itself.  Each layer's descriptor carries a device table
+        of its experts' blob addresses (address-table mode), so a token is
+        still one moe_stack_step launch with no copies and no host wait.
+        With shared_in_hbm the layers' shared experts are copied to HBM too.
+        Returns the set of (layer, expert) pairs placed in HBM."""
+        import numpy as np
+        from . import make_desc
+        dev = self.slab.device
+        if getattr(self, "_pool", None) is None or self._pool.numel() < n_slots * self.bb:
+            self._pool = torch.empty(max(1, n_slots) * self.bb, dtype=torch.uint8, device=dev)
+        if shared_in_hbm and self.n_shared and getattr(self, "_shared_hbm", None) is None:
+            self._shared_hbm = torch.empty(self.layers * self.bb, dtype=torch.uint8, device=dev)
+            self._shared_hbm.copy_(self.host_shared[:self.layers * self.bb])
+        addr = np.empty((self.layers, self.E), dtype=np.uint64)
+        for l in range(self.layers):
+            for e in range(self.E):
+                addr[l, e] = self.host_addr(l, e)
+        placed = []
+        for slot, (l, e) in enumerate(list(hot)[:n_slots]):
+            self._pool[slot * self.bb:(slot + 1) * self.bb].copy_(self.host_blob(l, e))
+            addr[l, e] = self._pool.data_ptr() + slot * self.bb
+            placed.append((l, e))
+        self._tables = torch.from_numpy(addr.view(np.int64)).to(dev)
+        sh = self._shared_hbm if shared_in_hbm and self.n_shared else None
+        descs = []
+        for l in range(self.layers):
+            shared = (sh.data_ptr() + l * self.bb) if sh is not None else (
+                (self._shared.ptr + l * self.bb) if self.n_shared else None)
+            descs.append(make_desc(hidden=self.D, n_experts=self.E, top_k=self.K, inter=self.I,
+                                   n_shared=self.n_shared, bits=self.bits, group=self.group, rms_eps=self.eps,
+                                   router_w=self.router[l], gamma=self.gamma[l], shared=shared,
+                                   expert_addr=self._tables[l], blob_bytes=self.bb))
+        self._table_descs = (LayerDesc * self.layers)(*descs)
+        torch.cuda.synchronize()
+        return set(placed)
+
+    def step_placed(self, resid, x, stream=None):
+        """One token through every layer in address-table mode (after
+        place_experts): one launch, HBM or host per expert."""
+        moe_stack_step(self._table_descs, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
+
     def resident_layers(self) -> list[int]:
         return [l for l in range(self.layers) if self.descs[l].experts]
 

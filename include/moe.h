@@ -106,11 +106,21 @@ typedef struct moe_layer_desc {
      * launch per token with moe_stack_step, no copies, no host wait).
      * Streamed mode: experts == NULL and slab != NULL: slab holds top_k+1
      * blobs, blob_bytes apart: slot k = the token's k-th selected expert,
-     * slot top_k = the shared expert (streamed mode needs n_tokens == 1). */
+     * slot top_k = the shared expert (streamed mode needs n_tokens == 1).
+     * Address-table mode: experts == NULL, slab == NULL and expert_addr !=
+     * NULL: expert_addr is a device array of n_experts blob addresses, each
+     * 16-byte aligned, in HBM or in pinned host memory from moe_host_alloc
+     * (per-expert residency: frequently routed experts in HBM, the rest
+     * read over the host link, in one launch); the shared blob is at
+     * `shared`.  Only the single-token fused stack takes it (moe_layer_step
+     * with n_tokens == 1 and moe_stack_step on a shape moe_layer_plan reports
+     * as fused); other uses return MOE_EUNSUPPORTED.  The table is read on
+     * the device by the launch: change it only between launches. */
     const uint8_t *experts;
     const uint8_t *shared;
     const uint8_t *slab;
     uint64_t blob_bytes;   /* must equal moe_blob_bytes(hidden, inter, bits, group) */
+    const uint64_t *expert_addr;
 } moe_layer_desc;
 
 /* Workspace bytes that moe_route / moe_expert_forward / moe_layer_step need

@@ -145,6 +145,25 @@ def test_stream_token_misuse_rejected():
     assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp)) == ews.MOE_ESTATE
 
 
+def test_address_table_mode_validation():
+    """Address-table descriptors: only with experts and slab NULL, one
+    token, and not for moe_expert_forward (nothing is enqueued)."""
+    L = ews.lib()
+    D, E, K, I = 256, 16, 2, 128
+    mk = lambda **kw: ews.make_desc(**{**dict(hidden=D, n_experts=E, top_k=K, inter=I, n_shared=1, bits=4,
+                                               router_w=1 << 12, gamma=1 << 13, shared=1 << 14,
+                                               expert_addr=1 << 15), **kw})
+    ws = ews.moe_workspace_bytes(mk(), 1)
+    assert ws > 0 and ews.moe_workspace_bytes(mk(), 2) == 0           # one token only
+    assert ews.moe_workspace_bytes(mk(experts=1 << 16), 1) == 0        # excludes experts
+    assert ews.moe_workspace_bytes(mk(slab=1 << 16), 1) == 0           # and slab
+    assert ews.moe_workspace_bytes(mk(shared=None), 1) == 0            # shared blob needed
+    assert ews.moe_workspace_bytes(mk(expert_addr=(1 << 15) + 8), 1) == 0  # alignment
+    d = mk()
+    rc = L.moe_expert_forward(ctypes.byref(d), 1 << 20, 1, 1 << 21, 1 << 22, 1 << 23, 1 << 24, ws, None)
+    assert rc == ews.MOE_EUNSUPPORTED
+
+
 def test_expert_cache_meta_and_reset():
     L = ews.lib()
     assert ews.moe_expert_cache_meta_bytes(0, 2, 16) == 0

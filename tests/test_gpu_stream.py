@@ -252,3 +252,35 @@ def test_zero_copy_needs_whole_layers():
     st = W.build_streamed(cfg, layers=3, arena_blobs=cfg.E + 3)
     with pytest.raises(ValueError):
         st.zero_copy_descs()
+
+
+@pytest.mark.parametrize("arena_blobs,n_slots", [(None, 40), (32, 7)])
+def test_address_tables_equal_resident(arena_blobs, n_slots):
+    """Per-expert residency: each layer's descriptor carries a device table of
+    blob addresses, the placed experts in an HBM pool, the others in the
+    pinned host arena, read by the stack kernel itself (one launch per
+    token).  Outputs equal the resident stack's bit for bit; one layer
+    through moe_layer_step in the same mode does too."""
+    import expert_weight_streaming_amd as ews
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=4, seed=0x5EED0E90)
+    print(f"[gpu case] address tables arena={arena_blobs} slots={n_slots}", flush=True)
+    st = W.build_streamed(cfg, layers=4, arena_blobs=arena_blobs)
+    rs = W.resident_twin(st)
+    hot = [(l, e) for l in range(4) for e in range(cfg.E) if (l + e) % 3 == 0]
+    placed = st.place_experts(n_slots, hot)
+    assert len(placed) == min(n_slots, len(hot))
+    v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
+    xp, xr = v.clone(), v.clone()
+    for t in range(3):
+        r_p, r_r = xp.clone(), xr.clone()
+        st.step_placed(r_p, xp)
+        rs.step(r_r, xr)
+        torch.cuda.synchronize()
+        assert int(st.workspace[:4].view(torch.int32).item()) == 0
+        assert torch.equal(st.topk_idx, rs.topk_idx), t
+        assert torch.equal(r_p, r_r) and torch.equal(xp, xr), t
+    r_p, r_r, x_p, x_r = v.clone(), v.clone(), v.clone(), v.clone()
+    ews.moe_layer_step(st._table_descs[0], r_p, x_p, 1, st.topk_idx[0], st.topk_w[0], st.workspace)
+    rs.layer_step(0, r_r, x_r)
+    torch.cuda.synchronize()
+    assert torch.equal(r_p, r_r) and torch.equal(x_p, x_r)

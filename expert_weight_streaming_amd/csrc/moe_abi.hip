@@ -565,6 +565,7 @@ size_t moe_expert_cache_meta_bytes(int32_t n_slots, int32_t n_layers, int32_t n_
 int moe_expert_cache_reset(moe_expert_cache *c, int32_t n_layers, int32_t n_experts)
 {
     if (!c || !c->slots || !c->meta) return fail(MOE_EINVAL, "cache, its slots or its meta block is NULL");
+    if (reinterpret_cast<uintptr_t>(c->meta) & 7u) return fail(MOE_EINVAL, "cache meta block not 8-byte aligned");
     if (c->n_slots <= 0 || n_layers <= 0 || n_experts <= 0)
         return fail(MOE_EINVAL, "cache sizes must be positive (slots %d, layers %d, experts %d)", c->n_slots, n_layers, n_experts);
     CacheView v = cache_view(c->meta, c->n_slots, n_layers, n_experts);

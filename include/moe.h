@@ -254,7 +254,7 @@ int moe_workspace_grouping(const moe_layer_desc *desc, int32_t n_tokens, size_t 
  * out of it.
  *   slots:  device, n_slots * blob_bytes (caller-owned)
  *   meta:   host, moe_expert_cache_meta_bytes(n_slots, n_layers, n_experts)
- *           bytes (caller-owned): the (layer, expert) -> slot index and the
+ *           bytes, 8-byte aligned (caller-owned): the blob -> slot index and the
  *           LRU list, written by moe_expert_cache_reset and moe_stream_token
  *   hits, misses: blobs served from the cache / over the link
  *           (moe_expert_cache_reset clears them)
@@ -284,7 +284,8 @@ typedef struct moe_expert_cache {
 size_t moe_expert_cache_meta_bytes(int32_t n_slots, int32_t n_layers, int32_t n_experts);
 
 /* Empty the cache: every slot free, nothing indexed, counters zero.
- * MOE_EINVAL for a NULL cache, slots or meta, or a non-positive size. */
+ * MOE_EINVAL for a NULL cache, slots or meta, a meta block that is not
+ * 8-byte aligned, or a non-positive size. */
 int moe_expert_cache_reset(moe_expert_cache *c, int32_t n_layers, int32_t n_experts);
 
 typedef struct moe_streamer {

@@ -182,6 +182,8 @@ def test_expert_cache_meta_and_reset():
                 ews.ExpertCache(1 << 22, 0, ctypes.addressof(meta), 0, 0)):
         assert L.moe_expert_cache_reset(ctypes.byref(bad), 2, 16) == ews.MOE_EINVAL
     assert L.moe_expert_cache_reset(ctypes.byref(c), 0, 16) == ews.MOE_EINVAL
+    odd = ews.ExpertCache(1 << 22, 4, ctypes.addressof(meta) + 4, 0, 0)
+    assert L.moe_expert_cache_reset(ctypes.byref(odd), 2, 16) == ews.MOE_EINVAL
 
 
 def test_host_alloc_rejects_bad_arguments():

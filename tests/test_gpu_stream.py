@@ -163,9 +163,10 @@ def _lru(events, n_slots):
     return hits, misses, fills
 
 
-@pytest.mark.parametrize("n_slots,pattern,speculate", [(5, "SSSS", False), (64, "SSSS", False), (3, "SRSS", False),
-                                                       (6, "SSSS", True), (64, "SRSS", True)])
-def test_expert_cache_equals_resident(n_slots, pattern, speculate):
+@pytest.mark.parametrize("n_slots,pattern,speculate,bits", [(5, "SSSS", False, 4), (64, "SSSS", False, 4),
+                                                            (3, "SRSS", False, 4), (6, "SSSS", True, 4),
+                                                            (64, "SRSS", True, 4), (9, "SSSS", True, 2)])
+def test_expert_cache_equals_resident(n_slots, pattern, speculate, bits):
     """The HBM expert cache: outputs equal the resident stack's bit for bit
     (cached blobs come from HBM, missed ones over the link), and the hit and
     miss counts equal an LRU of n_slots over the streamed blobs in the order
@@ -174,8 +175,8 @@ def test_expert_cache_equals_resident(n_slots, pattern, speculate):
     streamed layer's shared blob, then (speculate) the previous token's
     selection of that layer as guesses.  Tokens repeat, so a cache that
     holds every blob serves the repeats entirely from HBM."""
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=len(pattern), seed=0x5EED0E70)
-    print(f"[gpu case] expert cache slots={n_slots} {pattern} speculate={speculate}", flush=True)
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=len(pattern), bits=bits, seed=0x5EED0E70 + bits)
+    print(f"[gpu case] expert cache slots={n_slots} {pattern} speculate={speculate} bits={bits}", flush=True)
     st = W.build_streamed(cfg, layers=len(pattern), arena_blobs=31)
     rs = W.resident_twin(st)
     for l, c in enumerate(pattern):
@@ -214,15 +215,15 @@ def test_expert_cache_equals_resident(n_slots, pattern, speculate):
     assert st.streamer.cache is None or not st.streamer.cache
 
 
-@pytest.mark.parametrize("arena_blobs", [None, 32])
-def test_zero_copy_equals_resident(arena_blobs):
+@pytest.mark.parametrize("arena_blobs,bits", [(None, 4), (32, 4), (32, 2)])
+def test_zero_copy_equals_resident(arena_blobs, bits):
     """GPU-initiated streaming: the stack kernel reads the selected experts
     straight from the pinned host arena (one launch per token, no copies, no
     host wait).  Outputs and selections equal the resident stack's holding
     the same bytes, bit for bit, with a full and an aliased arena (32 blobs =
     two layers' experts)."""
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=5, seed=0x5EED0E80)
-    print(f"[gpu case] zero-copy arena_blobs={arena_blobs}", flush=True)
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=5, bits=bits, seed=0x5EED0E80 + bits)
+    print(f"[gpu case] zero-copy arena_blobs={arena_blobs} bits={bits}", flush=True)
     st = W.build_streamed(cfg, layers=5, arena_blobs=arena_blobs)
     rs = W.resident_twin(st)
     v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
@@ -254,16 +255,16 @@ def test_zero_copy_needs_whole_layers():
         st.zero_copy_descs()
 
 
-@pytest.mark.parametrize("arena_blobs,n_slots", [(None, 40), (32, 7)])
-def test_address_tables_equal_resident(arena_blobs, n_slots):
+@pytest.mark.parametrize("arena_blobs,n_slots,bits", [(None, 40, 4), (32, 7, 4), (None, 20, 2)])
+def test_address_tables_equal_resident(arena_blobs, n_slots, bits):
     """Per-expert residency: each layer's descriptor carries a device table of
     blob addresses, the placed experts in an HBM pool, the others in the
     pinned host arena, read by the stack kernel itself (one launch per
     token).  Outputs equal the resident stack's bit for bit; one layer
     through moe_layer_step in the same mode does too."""
     import expert_weight_streaming_amd as ews
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=4, seed=0x5EED0E90)
-    print(f"[gpu case] address tables arena={arena_blobs} slots={n_slots}", flush=True)
+    cfg = seedgen.CONFIGS["tiny"].replace(layers=4, bits=bits, seed=0x5EED0E90 + bits)
+    print(f"[gpu case] address tables arena={arena_blobs} slots={n_slots} bits={bits}", flush=True)
     st = W.build_streamed(cfg, layers=4, arena_blobs=arena_blobs)
     rs = W.resident_twin(st)
     hot = [(l, e) for l in range(4) for e in range(cfg.E) if (l + e) % 3 == 0]

@@ -285,3 +285,25 @@ def test_address_tables_equal_resident(arena_blobs, n_slots, bits):
     rs.layer_step(0, r_r, x_r)
     torch.cuda.synchronize()
     assert torch.equal(r_p, r_r) and torch.equal(x_p, x_r)
+
+
+def test_zero_copy_and_tables_hidden4096():
+    """The hidden-4096 shape (the 60-layer stack's kernel instantiation):
+    zero-copy and address-table tokens equal the resident stack bit for
+    bit."""
+    cfg = seedgen.CONFIGS["layer"].replace(E=24, layers=3, seed=0x5EED0EA0)
+    print("[gpu case] zero-copy and tables hidden-4096", flush=True)
+    st = W.build_streamed(cfg, layers=3)
+    rs = W.resident_twin(st)
+    st.place_experts(20, [(l, e) for l in range(3) for e in range(0, cfg.E, 3)])
+    v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
+    for step in (st.step_zero_copy, st.step_placed):
+        xs, xr = v.clone(), v.clone()
+        for t in range(2):
+            r_s, r_r = xs.clone(), xr.clone()
+            step(r_s, xs)
+            rs.step(r_r, xr)
+            torch.cuda.synchronize()
+            assert int(st.workspace[:4].view(torch.int32).item()) == 0
+            assert torch.equal(st.topk_idx, rs.topk_idx), (step.__name__, t)
+            assert torch.equal(r_s, r_r) and torch.equal(xs, xr), (step.__name__, t)

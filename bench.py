@@ -161,7 +161,7 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
     bb, L, E = cfg.blob_bytes, cfg.layers, cfg.E
     full = L * E
     # the driver pins at most ~65 GiB in all on the machines measured so far,
-    # so the default arena is 56 GiB, aliased
+    # so the default arena is at most 56 GiB (rounded down to whole layers), aliased
     want = (56 << 30) if arena_gb is None else int(arena_gb * 2**30)
     room = mem_available() - 32 * 2**30
     # whole layers' worth of blobs, so that the zero-copy descriptors (each

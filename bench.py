@@ -130,10 +130,27 @@ def cpu_baseline(cfg, v0, seconds, check_rows):
         if time.time() - t_start > seconds and l + 1 >= check_rows:
             break
     per_layer = sum(times) / len(times)
-    return {"value": 1.0 / (per_layer * cfg.layers), "unit": "tokens/s", "cores": oracle.get_threads(),
+    all_cores = oracle.get_threads()
+    # the same oracle on one core, over the first layers of the same token
+    oracle.set_threads(1)
+    r, x = v0.copy(), v0.copy()
+    t1 = []
+    for l in range(min(3, cfg.layers)):
+        ref = W.LayerRef(cfg, l)
+        for e in oracle.topk(oracle.router(ref.Wr, x.astype(np.float64)), cfg.K)[0]:
+            ref.blob(int(e))
+        t0 = time.time()
+        res = ref.run(r, x)
+        t1.append(time.time() - t0)
+        r, x = res["r"].astype(np.float32), res["x"].astype(np.float32)
+    oracle.set_threads(cores)
+    one = sum(t1) / len(t1)
+    return {"value": 1.0 / (per_layer * cfg.layers), "unit": "tokens/s", "cores": all_cores,
             "kind": "oracle",
             "sample": f"token 0, layers 0..{len(times) - 1} of {cfg.layers} (fp64 oracle, blob generation excluded), "
-                      f"{per_layer * 1e3:.1f} ms per layer, extrapolated to the full stack"}, outs
+                      f"{per_layer * 1e3:.1f} ms per layer, extrapolated to the full stack",
+            "single_core": {"value": 1.0 / (one * cfg.layers), "cores": 1,
+                            "sample": f"token 0, layers 0..{len(t1) - 1}, {one * 1e3:.1f} ms per layer, extrapolated"}}, outs
 
 
 def mem_available():

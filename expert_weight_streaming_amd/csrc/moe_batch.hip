@@ -768,10 +768,13 @@ hipError_t batch_bits(const BatchArgs &a, int stage, hipStream_t s)
 {
     switch (stage) {
     case 0:  // gate/up: 64-row units, 8 scale groups per stage
-        hipLaunchKernelGGL((k_expert_mm<BITS, 0, 1, 8>), dim3(2048), dim3(256), 0, s, a);
+        // 512 blocks (two per CU at these kernels' registers); blocks take
+        // further units in turn (2048 blocks measured 1 us slower for the
+        // down rows of a 32-token step, 256 blocks 9 us slower)
+        hipLaunchKernelGGL((k_expert_mm<BITS, 0, 1, 8>), dim3(512), dim3(256), 0, s, a);
         break;
     case 1:  // down: 128-row units (the digit tables of h shared by more rows)
-        hipLaunchKernelGGL((k_expert_mm<BITS, 1, 2, (BITS == 4 ? 4 : 8)>), dim3(2048), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_expert_mm<BITS, 1, 2, (BITS == 4 ? 4 : 8)>), dim3(512), dim3(256), 0, s, a);
         break;
     }
     return hipGetLastError();

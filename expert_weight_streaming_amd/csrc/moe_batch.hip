@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
 {
     const int tid = threadIdx.x;
     const int T = a.T, K = a.K, E = a.E, P = T * K;
-    __shared__ int s_idx[64 * kMaxTopK];
+    __shared__ __align__(16) int s_idx[64 * kMaxTopK];
     __shared__ int s_count[4096];
     __shared__ int s_off[4096];
     __shared__ int s_flag[4096];
@@ -339,8 +339,16 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
             a.pos_of_pair[p] = -1;
             continue;
         }
-        int rank = 0;
-        for (int q = 0; q < p; ++q) rank += s_idx[q] == e;
+        // rank among the expert's pairs: earlier pairs with the same id,
+        // four ids per 16-byte LDS read
+        int rank = 0, q = 0;
+        const int4 *s4 = reinterpret_cast<const int4 *>(s_idx);
+#pragma unroll 4
+        for (; q + 4 <= p; q += 4) {
+            const int4 v = s4[q >> 2];
+            rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+        }
+        for (; q < p; ++q) rank += s_idx[q] == e;
         const int pos = s_off[e] + rank;
         a.perm[pos] = p;
         a.pos_of_pair[p] = pos;

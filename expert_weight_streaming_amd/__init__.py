@@ -48,7 +48,7 @@ class Streamer(ctypes.Structure):
                 ("cache", ctypes.POINTER(ExpertCache))]
 
 
-EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_last_error", "moe_route",
+EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_workspace_state_bytes", "moe_strerror", "moe_last_error", "moe_route",
            "moe_expert_forward", "moe_layer_step", "moe_stack_step", "moe_layer_plan", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
            "moe_host_alloc", "moe_host_free", "moe_expert_cache_meta_bytes", "moe_expert_cache_reset"]
 
@@ -66,6 +66,8 @@ def lib():
         L.moe_blob_bytes.argtypes = [i32, i32, i32, i32]
         L.moe_workspace_bytes.restype = sz
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), i32]
+        L.moe_workspace_state_bytes.restype = sz
+        L.moe_workspace_state_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
         L.moe_strerror.restype = cp
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = cp
@@ -86,7 +88,7 @@ def lib():
         L.moe_stream_prefetch.argtypes = [ctypes.POINTER(Streamer), i32, vp, i32, i32, i32, vp, vp]
         L.moe_stream_token.restype = ctypes.c_int
         L.moe_stream_token.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(Streamer), vp, vp, vp, vp, vp, vp,
-                                       sz, vp, vp, vp]
+                                       vp, sz, vp, vp, vp]
         L.moe_host_alloc.restype = ctypes.c_int
         L.moe_host_alloc.argtypes = [sz, ctypes.POINTER(ctypes.c_void_p)]
         L.moe_host_free.restype = ctypes.c_int
@@ -134,6 +136,10 @@ def moe_blob_bytes(hidden: int, inter: int, bits: int, group: int = 64) -> int:
 
 def moe_workspace_bytes(desc: LayerDesc, n_tokens: int) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(desc), n_tokens))
+
+
+def moe_workspace_state_bytes(desc: LayerDesc) -> int:
+    return int(lib().moe_workspace_state_bytes(ctypes.byref(desc)))
 
 
 def moe_strerror(status: int) -> str:
@@ -194,15 +200,17 @@ def moe_stream_prefetch(streamer: Streamer, layer: int, expert_ids, slot: int, w
 
 
 def moe_stream_token(descs, streamer: Streamer, resid, x, topk_idx, topk_w, host_ids, workspace, compute_stream,
-                     copy_stream, events, ws_bytes=None) -> None:
+                     copy_stream, events, ws_bytes=None, record=None) -> None:
     """descs: a ctypes array of LayerDesc (streamed form); host_ids: pinned
-    int32 tensor of K; events: five torch.cuda.Event."""
+    int32 tensor of K; events: five torch.cuda.Event; record: None or a
+    device tensor [layers + 1][2][D]."""
     ws_bytes = workspace.numel() * workspace.element_size() if ws_bytes is None else ws_bytes
     if any(not e.cuda_event for e in events):
         raise ValueError("every event must have been recorded once (its HIP event is created lazily)")
     ev = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
     _check(lib().moe_stream_token(descs, len(descs), ctypes.byref(streamer), _ptr(resid), _ptr(x), _ptr(topk_idx),
-                                  _ptr(topk_w), _ptr(host_ids), _ptr(workspace), ws_bytes, _stream(compute_stream),
+                                  _ptr(topk_w), _ptr(record), _ptr(host_ids), _ptr(workspace), ws_bytes,
+                                  _stream(compute_stream),
                                   _stream(copy_stream), ctypes.cast(ev, ctypes.c_void_p)))
 
 

@@ -94,35 +94,29 @@ moe::WsLayout layout(const moe_layer_desc *d, int32_t T)
 {
     moe::WsLayout L;
     size_t off = 256;
-    L.logits = off;
-    off = round_up(off + (size_t)T * d->n_experts * 4, 256);
-    L.h = off;
-    off = round_up(off + (size_t)T * (d->top_k + d->n_shared) * d->inter * 4, 256);
-    L.ss = off;
+    auto take = [&](size_t &field, size_t bytes) {
+        field = off;
+        off = round_up(off + bytes, 256);
+    };
+    const size_t S = (size_t)d->top_k + d->n_shared;
+    // state carried from call to call: offsets independent of T
+    take(L.slots, (size_t)moe::kMaxLayerBlocks * moe::kSlotWords * 4);
+    take(L.tss, (size_t)moe::kMaxLayerBlocks * 8);
+    take(L.tlog, (size_t)d->n_experts * 8);
+    take(L.th, S * d->inter * 8);
+    take(L.tres, (size_t)d->hidden * 8);
+    L.state = off;
+    // per-call scratch
     const size_t nss = (size_t)moe::kMaxLayerBlocks > (size_t)moe::down_blocks(d->hidden, d->inter, d->bits)
                            ? (size_t)moe::kMaxLayerBlocks
                            : (size_t)moe::down_blocks(d->hidden, d->inter, d->bits);
-    off = round_up(off + nss * 4, 256);
-    L.slots = off;
-    off = round_up(off + (size_t)moe::kMaxLayerBlocks * moe::kSlotWords * 4, 256);
-    L.rbuf = off;
-    off = round_up(off + (size_t)d->hidden * 4, 256);
-    L.tlog = off;
-    off = round_up(off + (size_t)d->n_experts * 8, 256);
-    L.th = off;
-    off = round_up(off + (size_t)(d->top_k + d->n_shared) * d->inter * 8, 256);
-    L.tres = off;
-    off = round_up(off + (size_t)d->hidden * 8, 256);
-    L.tss = off;
-    off = round_up(off + (size_t)moe::kMaxLayerBlocks * 8, 256);
+    take(L.ss, nss * 4);
+    take(L.logits, (size_t)T * d->n_experts * 4);
+    take(L.h, (size_t)T * S * d->inter * 4);
     if (T > 1) {
         const size_t E = d->n_experts, K = d->top_k, D = d->hidden, I = d->inter;
         const size_t P = (size_t)T * (K + d->n_shared);
         const size_t G = moe::kGroup;  // activations per scale group
-        auto take = [&](size_t &field, size_t bytes) {
-            field = off;
-            off = round_up(off + bytes, 256);
-        };
         take(L.lpart, (size_t)moe::kRouteSplit * T * E * 4);
         take(L.count, E * 4);
         take(L.offset, (E + 1) * 4);
@@ -302,7 +296,9 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
                     (e = hipMemcpyAsync(rj + D, x, (size_t)D * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
                     return hip_fail(e, "record copy");
             }
-            int rc = enqueue_route(dj, x, ij, wj, nullptr, ws, L, s);
+            // a streamed layer's routing is the one its slab was filled for (given)
+            const bool slab = !dj->experts && !dj->expert_addr;
+            int rc = slab ? MOE_OK : enqueue_route(dj, x, ij, wj, nullptr, ws, L, s);
             if (rc) return rc;
             if ((rc = enqueue_forward(dj, x, ij, wj, nullptr, resid, x, ws, L, s))) return rc;
         }
@@ -370,6 +366,12 @@ size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens)
 {
     if (check_desc(desc, n_tokens) != MOE_OK) return 0;
     return layout(desc, n_tokens).total;
+}
+
+size_t moe_workspace_state_bytes(const moe_layer_desc *desc)
+{
+    if (check_desc(desc, 1) != MOE_OK) return 0;
+    return layout(desc, 1).state;
 }
 
 const char *moe_strerror(int status)
@@ -669,8 +671,8 @@ static int stream_copies(const moe_streamer *st, int32_t layer, const int32_t *e
 }
 
 int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_streamer *st, float *resid, float *x,
-                     int32_t *topk_idx, float *topk_w, int32_t *host_ids, void *workspace, size_t ws_bytes,
-                     void *compute_stream, void *copy_stream, void *const *events)
+                     int32_t *topk_idx, float *topk_w, float *record, int32_t *host_ids, void *workspace,
+                     size_t ws_bytes, void *compute_stream, void *copy_stream, void *const *events)
 {
     if (!layers || n_layers < 1) return fail(MOE_EINVAL, "no layers");
     if (!st || !st->slab[0] || !st->slab[1]) return fail(MOE_ESTATE, "streamer has no slab");
@@ -696,6 +698,10 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
             return fail(MOE_ESTATE, "layer %d does not match the streamer's blob size / expert count", l);
     }
     if (int rc = check_ws(&layers[0], 1, workspace, ws_bytes)) return rc;
+    if (record && !aligned16(record)) return fail(MOE_EINVAL, "record not 16-byte aligned");
+    const size_t D = (size_t)layers[0].hidden;
+    for (int32_t l = 1; l < n_layers; ++l)
+        if ((size_t)layers[l].hidden != D) return fail(MOE_EINVAL, "layer %d has another hidden size", l);
     if (const moe_expert_cache *c = st->cache) {
         if (!c->slots || !c->meta || c->n_slots <= 0) return fail(MOE_ESTATE, "expert cache without slots or meta block");
         const CacheHead *h = static_cast<const CacheHead *>(c->meta);
@@ -707,10 +713,20 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
     hipEvent_t copy_done[2] = {(hipEvent_t)events[1], (hipEvent_t)events[2]};
     hipEvent_t compute_done[2] = {(hipEvent_t)events[3], (hipEvent_t)events[4]};
     hipError_t e;
+    // (resid, x) entering layer l (l == n_layers: the output) into record
+    auto rec = [&](int32_t l) -> int {
+        if (!record) return MOE_OK;
+        float *rl = record + (size_t)l * 2 * D;
+        if ((e = hipMemcpyAsync(rl, resid, D * 4, hipMemcpyDeviceToDevice, cs)) != hipSuccess ||
+            (e = hipMemcpyAsync(rl + D, x, D * 4, hipMemcpyDeviceToDevice, cs)) != hipSuccess)
+            return hip_fail(e, "record copy");
+        return MOE_OK;
+    };
     int32_t j = 0;  // streamed layers so far: layer l, the j-th streamed one, uses slot j mod 2
     for (int32_t l = 0; l < n_layers; ++l) {
         int32_t *idx = topk_idx + (size_t)l * K;
         float *w = topk_w + (size_t)l * K;
+        if (int rc = rec(l)) return rc;
         if (layers[l].experts || layers[l].expert_addr) {
             // resident: routing and experts stay on the device, no host wait
             int rc = moe_layer_step(&layers[l], resid, x, 1, idx, w, workspace, ws_bytes, compute_stream);
@@ -736,7 +752,8 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
         if (j >= 2 && (e = hipStreamWaitEvent(ps, compute_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
         rc = prefetch_impl(st, l, host_ids, K, s, j == 0 ? with_shared : 0, copy_stream, copy_done[s], true);
         if (rc) return rc;
-        // 3. the layer itself once its weights have landed
+        // 3. the layer itself once its weights have landed, under the routing
+        // the copies followed (idx, w: read by the streamed step, not recomputed)
         if ((e = hipStreamWaitEvent(cs, copy_done[s], 0)) != hipSuccess) return hip_fail(e, "wait");
         rc = moe_layer_step(&d, resid, x, 1, idx, w, workspace, ws_bytes, compute_stream);
         if (rc) return rc;
@@ -775,7 +792,7 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
         }
         ++j;
     }
-    return MOE_OK;
+    return rec(n_layers);
 }
 
 int moe_host_alloc(size_t bytes, void **out)

@@ -690,6 +690,36 @@ __device__ __forceinline__ float rt_finish(const RtRegs<N> &r, const float *x, i
     return acc0 + acc1;
 }
 
+// One wave's slice sw (of kRouterSlices) of a router row: the dot of row
+// (fp32 [D]) with x over float4 columns [sw*Q, min(D/4, sw*Q + Q)), Q =
+// ceil(D/4 / kRouterSlices), in rounds of 64*RN float4, reduced over the
+// wave; the full slice sum in every lane.  `loaded`: the first round's
+// weights are already in r (loaded ahead with the same bounds).  The row's
+// logit is the kRouterSlices slice sums added in slice order; every router
+// GEMV of one token (the fused stack kernel's and k_route's) runs through
+// this function, so they agree bit for bit.
+template <int RN>
+__device__ __forceinline__ float router_slice(RtRegs<RN> &r, bool loaded, const float *row, const float *x, int D,
+                                              int sw, int lane)
+{
+    const int nc4 = D / 4, Q = (nc4 + kRouterSlices - 1) / kRouterSlices;
+    const int c_hi = min(nc4, sw * Q + Q);
+    float acc = 0.f;
+    for (int c0 = 0; c0 < Q; c0 += 64 * RN) {
+        const int c_lo = sw * Q + c0;
+        if (!loaded || c0 > 0) rt_load<RN>(r, row, c_lo, c_hi, lane);
+        acc += rt_finish<RN>(r, x, c_lo, c_hi, lane);
+    }
+    return group_sum<64>(acc);
+}
+// The first round of router_slice's loads, issued ahead.
+template <int RN>
+__device__ __forceinline__ void router_slice_load(RtRegs<RN> &r, const float *row, int D, int sw, int lane)
+{
+    const int nc4 = D / 4, Q = (nc4 + kRouterSlices - 1) / kRouterSlices;
+    rt_load<RN>(r, row, sw * Q, min(nc4, sw * Q + Q), lane);
+}
+
 // One wave: STEPS x (64/LPR) consecutive rows o0.. of one expert's down
 // matrix times h; LPR lanes per row.  A lane turns its slice of h into
 // digits once (fixed-point step shared by the LPR lanes of a row, so that
@@ -807,21 +837,28 @@ __device__ __forceinline__ void topk_weights(const float (&vals)[kMaxTopK], int 
     for (int k = 0; k < kMaxTopK; ++k) w[k] = k < K ? expf(vals[k] - vals[0]) / z : 0.f;
 }
 
-// Routing candidates as 64-bit keys: the logit's bits mapped to an
-// unsigned order (high word), the complement of the expert index (low
-// word).  A larger key is a larger logit, then the lower index; 0 is below
-// every real key.
+// The order of fp32 logits as unsigned keys: a larger key is a larger
+// value; -0 and +0 map to the same key (they tie, and the lower index wins,
+// as for any other equal values).  0 is below every real key.
+__device__ __forceinline__ uint32_t order_key(uint32_t u)
+{
+    u = u == 0x80000000u ? 0u : u;
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return o ? o : 1u;
+}
+__device__ __forceinline__ float order_value(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Routing candidates as 64-bit keys: order_key of the logit (high word), the
+// complement of the expert index (low word).  A larger key is a larger
+// logit, then the lower index.
 __device__ __forceinline__ uint64_t route_key(float v, int e)
 {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
+    return ((uint64_t)order_key(__float_as_uint(v)) << 32) | (uint32_t)~(uint32_t)e;
 }
-__device__ __forceinline__ float key_value(uint64_t k)
-{
-    const uint32_t ord = (uint32_t)(k >> 32);
-    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
+__device__ __forceinline__ float key_value(uint64_t k) { return order_value((uint32_t)(k >> 32)); }
 __device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
 
 template <int CTRL, int ROWS>
@@ -890,45 +927,19 @@ __device__ __forceinline__ void wait_selected(const int *rdy, int k, int tag, ui
     }
 }
 
-// Top K of logits[0..E) (E <= 64 * KPL) by one wave, from the tagged logits
-// themselves (agent-coherent loads, lane l holding elements l + 64 j; the
-// wave polls until every logit carries epoch `ltag`).
-// Order: the larger logit (the float's bits mapped to an unsigned order,
-// as route_key does), then the lower index.  Each lane keeps its best
-// element (the lowest j on equal bits); a round takes the wave's largest
-// order value, the lowest index among the lanes holding it, and that lane
-// moves to its next best.  sel/selw (LDS) receive the indices in rank order
-// and the routing weights (lanes k < K write).  Each index is published as
-// soon as its round ends: sel[k] is written, then rdy[k] = tag (LDS), so
-// that other waves can start on slot k before the later rounds finish.
+// Top K of E logits (E <= 64 * KPL) by one wave, from order keys: lane l
+// holds ord[j] = order_key of element l + 64 j (0: no element).  Order: the
+// larger key, then the lower index.  Each lane keeps its best element (the
+// lowest j on equal keys); a round takes the wave's largest key, the lowest
+// index among the lanes holding it, and that lane moves to its next best.
+// sel/selw (LDS) receive the indices in rank order and the routing weights
+// (lanes k < K write).  Each index is published as soon as its round ends:
+// sel[k] is written, then rdy[k] = tag (LDS), so that other waves can start
+// on slot k before the later rounds finish.
 template <int KPL>
-__device__ __forceinline__ void wave_topk_global(const uint64_t *tlog, uint32_t ltag, int E, int K, int *sel,
-                                                 float *selw, int *rdy, int tag, int lane, uint32_t *flags)
+__device__ __forceinline__ void topk_select(uint32_t (&ord)[KPL], int K, int *sel, float *selw, int *rdy, int tag,
+                                            int lane)
 {
-    // every load in flight before the first use (clamped indices, masked
-    // afterwards)
-    uint32_t ord[KPL];
-    for (uint32_t spins = 0;;) {
-        bool ok = true;
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-            const uint64_t w = __hip_atomic_load(tlog + min(lane + 64 * j, E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ord[j] = (uint32_t)w;
-            ok &= (uint32_t)(w >> 32) == ltag;
-        }
-        if (__all(ok)) break;
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins == (1u << 16)) {
-            atomicOr(flags, MOE_DEVERR_BARRIER_TIMEOUT);
-            break;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-        const uint32_t u = ord[j];
-        const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-        ord[j] = lane + 64 * j < E ? (o ? o : 1u) : 0u;  // 0 marks "no element"
-    }
     uint32_t bo = 0u;
     int bj = 0;
 #pragma unroll
@@ -954,7 +965,7 @@ __device__ __forceinline__ void wave_topk_global(const uint64_t *tlog, uint32_t 
             e = (int)udpp_min(bo == m ? (uint32_t)(bj * 64 + lane) : 0xFFFFFFFFu);
         }
         idx[k] = e;
-        vals[k] = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+        vals[k] = order_value(m);
         if (lane == 0) {
             __hip_atomic_store(sel + k, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_store(rdy + k, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -976,21 +987,46 @@ __device__ __forceinline__ void wave_topk_global(const uint64_t *tlog, uint32_t 
     }
     // routing weights: softmax over the selected logits, lane k < K taking
     // selection k (one exp per lane), the sum in rank order
-    int mi = 0;
     float mv = vals[0];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
-        if (lane == k) {
-            mi = idx[k];
-            mv = vals[k];
-        }
+        if (lane == k) mv = vals[k];
     const float ex = lane < K ? expf(mv - vals[0]) : 0.f;
     float z = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k)
         if (k < K) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), k));
-    (void)mi;
     if (lane < K) selw[lane] = ex / z;
+}
+
+// topk_select over the tagged logits of a persistent launch (agent-coherent
+// loads, lane l holding elements l + 64 j; the wave polls until every logit
+// carries epoch `ltag`).
+template <int KPL>
+__device__ __forceinline__ void wave_topk_global(const uint64_t *tlog, uint32_t ltag, int E, int K, int *sel,
+                                                 float *selw, int *rdy, int tag, int lane, uint32_t *flags)
+{
+    // every load in flight before the first use (clamped indices, masked
+    // afterwards)
+    uint32_t ord[KPL];
+    for (uint32_t spins = 0;;) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const uint64_t w = __hip_atomic_load(tlog + min(lane + 64 * j, E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ord[j] = (uint32_t)w;
+            ok &= (uint32_t)(w >> 32) == ltag;
+        }
+        if (__all(ok)) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == (1u << 16)) {
+            atomicOr(flags, MOE_DEVERR_BARRIER_TIMEOUT);
+            break;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) ord[j] = lane + 64 * j < E ? order_key(ord[j]) : 0u;
+    topk_select<KPL>(ord, K, sel, selw, rdy, tag, lane);
 }
 
 }  // namespace dev

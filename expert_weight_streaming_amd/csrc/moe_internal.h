@@ -17,22 +17,37 @@ constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
 // grouped kernels, the others the dot-product ones.
 constexpr int kRouteSplit = 4;  // hidden-dimension slices of the batched router (partial logits)
 
-// Workspace layout (byte offsets), all 64-byte aligned.
+// Router GEMV of one token (shared by the fused stack kernel and k_route, so
+// that both produce the same fp32 logits bit for bit): RSL waves per router
+// row, wave s owning float4 columns [s*Q, min(D/4, s*Q + Q)), Q = ceil(D/4 /
+// RSL), fetched in rounds of 64*RN float4; the wave's partial sums are reduced
+// across the wave and the RSL slice sums added in slice order.
+constexpr int kRouterRN = 4;
+constexpr int kRouterSlices = 4;
+
+// Workspace layout (byte offsets), all 64-byte aligned.  The leading
+// `state` bytes hold what a call hands to the next one on the same workspace
+// (error flags, self-resetting arrival counters, the fused step's grid size,
+// per-block epochs and tagged exchange words); their offsets depend on the
+// layer shape only, never on the token count, so calls with different token
+// counts can share one workspace.  Everything after `state` is per-call
+// scratch.
 struct WsLayout {
     size_t flags = 0;        // uint32 device error bits (OR-ed)
     size_t ctr_route = 64;   // uint32 arrival counter of the route kernel
     size_t hdr = 128;        // uint32 grid size of the persistent stack kernel last run on this workspace
     size_t ctr_down = 192;   // uint32 arrival counter of the down kernel (layer mode)
-    size_t logits = 0;       // float [T][E]
-    size_t h = 0;            // float [T][slots][I]
-    size_t ss = 0;           // float [kMaxLayerBlocks]
-    size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] barrier epochs of the stack kernel
-    size_t rbuf = 0;         // float [D] residual stream handed between layers of one stack launch
+    size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] epochs reached by each block of the stack kernel
     // the stack kernel's exchanges: (value, epoch) pairs, uint64
+    size_t tss = 0;          // [kMaxLayerBlocks] per-block sums of squares
     size_t tlog = 0;         // [E] logits
     size_t th = 0;           // [slots][I] h
     size_t tres = 0;         // [D] residual rows
-    size_t tss = 0;          // [kMaxLayerBlocks] per-block sums of squares
+    size_t state = 0;        // end of the state carried from call to call
+    // per-call scratch
+    size_t ss = 0;           // float [max(kMaxLayerBlocks, down blocks)] partial sums of squares (k_down)
+    size_t logits = 0;       // float [T][E]
+    size_t h = 0;            // float [T][slots][I]
     // batches (T > 1)
     size_t lpart = 0;        // float [kRouteSplit][T][E] partial logits
     size_t count = 0, offset = 0, perm = 0, pos_of_pair = 0, act = 0, n_act = 0;

@@ -6,8 +6,8 @@
 //                shared expert, SwiGLU fused, h kept in the workspace;
 //   k_down       dequantised down GEMV for all slots of one output row block,
 //                weighted combine in slot order.
-// moe_layer_step runs the same building blocks fused in one persistent
-// launch (moe_layer.hip).
+// moe_layer_step and moe_stack_step run the same building blocks fused in
+// one persistent launch (moe_stack.hip).
 #include "moe_device.h"
 
 namespace moe {
@@ -15,16 +15,33 @@ namespace {
 
 using namespace dev;
 
-// Router: one row per wave, 4 waves per block.  The last block to arrive
-// selects the top K and writes the weights.
-__global__ void __launch_bounds__(256) k_route(RouteArgs a)
+// Router: kRouterSlices waves per row (router_slice, the same reduction as
+// the fused stack kernel's router, so that both give the same logits bit for
+// bit), two rows per 512-thread block.  The last block to arrive selects the
+// top K and writes the weights (topk_select for E <= 512, the stack kernel's
+// selection; wave_topk beyond).
+constexpr int kRouteThreads = 512;
+constexpr int kRouteRows = kRouteThreads / 64 / kRouterSlices;
+
+__global__ void __launch_bounds__(kRouteThreads) k_route(RouteArgs a)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = blockIdx.x * 4 + wave;
+    const int rr = wave / kRouterSlices, sw = wave % kRouterSlices;
+    const int row = blockIdx.x * kRouteRows + rr;
+    __shared__ float part[kRouteThreads / 64];
     __shared__ int is_last;
-    if (row < a.E) {
-        const float acc = wave_router_row(a.router + (size_t)row * a.D, a.x, a.D, lane);
-        if (lane == 0) xstore(a.logits + row, acc);
+    {
+        RtRegs<kRouterRN> r;
+        const float acc = router_slice<kRouterRN>(r, false, row < a.E ? a.router + (size_t)row * a.D : nullptr, a.x,
+                                                  a.D, sw, lane);
+        if (lane == 0) part[wave] = acc;
+    }
+    __syncthreads();
+    if (tid < kRouteRows && blockIdx.x * kRouteRows + tid < a.E) {
+        float s = part[tid * kRouterSlices];
+#pragma unroll
+        for (int q = 1; q < kRouterSlices; ++q) s += part[tid * kRouterSlices + q];
+        xstore(a.logits + blockIdx.x * kRouteRows + tid, s);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -33,12 +50,29 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
         is_last = prev == gridDim.x - 1;
     }
     __syncthreads();
-    if (!is_last) return;
+    if (!is_last || wave != 0) return;
 
-    __shared__ float lg[4096];
-    for (int e = tid; e < a.E; e += 256) lg[e] = xload(a.logits + e);
-    __syncthreads();
-    if (wave == 0) {
+    if (a.E <= 64 * 8) {
+        __shared__ int sel[kMaxTopK], rdy[kMaxTopK];
+        __shared__ float selw[kMaxTopK];
+        uint32_t ord[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int e = lane + 64 * j;
+            ord[j] = e < a.E ? order_key(__float_as_uint(xload(a.logits + e))) : 0u;
+        }
+        topk_select<8>(ord, a.K, sel, selw, rdy, 1, lane);
+        __builtin_amdgcn_wave_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane < a.K) {
+            a.topk_idx[lane] = sel[lane];
+            a.topk_w[lane] = selw[lane];
+        }
+    } else {
+        __shared__ float lg[4096];
+        for (int e = lane; e < a.E; e += 64) lg[e] = xload(a.logits + e);
+        __builtin_amdgcn_wave_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         int idx[kMaxTopK];
         float vals[kMaxTopK], w[kMaxTopK];
         wave_topk(lg, a.E, a.K, lane, idx, vals);
@@ -50,9 +84,9 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a)
                 a.topk_idx[k] = idx[k];
                 a.topk_w[k] = w[k];
             }
-            *a.counter = 0u;
         }
     }
+    if (lane == 0) *a.counter = 0u;
 }
 
 constexpr int kGateUpRows = 2;  // rows per wave unit
@@ -257,7 +291,7 @@ int down_blocks(int D, int I, int bits)
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_route, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route, dim3((a.E + kRouteRows - 1) / kRouteRows), dim3(kRouteThreads), 0, s, a);
     return hipGetLastError();
 }
 

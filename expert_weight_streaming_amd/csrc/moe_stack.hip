@@ -54,8 +54,8 @@ using namespace dev;
 
 constexpr int NT = kStackThreads;  // threads per block
 constexpr int NWB = NT / 64;       // waves per block
-constexpr int RN = 4;              // router float4 per lane and load round
-constexpr int RSL = 4;             // waves per router row
+constexpr int RN = kRouterRN;      // router float4 per lane and load round
+constexpr int RSL = kRouterSlices; // waves per router row
 constexpr int RPB = NWB / RSL;     // router rows per block and round
 constexpr int XV = 2;              // x float4 per thread and round
 constexpr int HV = 3;              // h float4 per thread and round
@@ -220,10 +220,10 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int NB = gridDim.x, b = blockIdx.x;
         const int D = A->D, E = A->E, I = A->I;
-        const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rs = wave / RSL, sw = wave % RSL;
+        const int rs = wave / RSL, sw = wave % RSL;
         const StackLayer Ly = layer_of<TBL>(A, l);
         const int e = b + NB * rs;
-        rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, sw * Q, min(nc4, sw * Q + Q), lane);
+        router_slice_load<RN>(ra, e < E && !Ly.slab ? Ly.router + (size_t)e * D : nullptr, D, sw, lane);
         const int su = (wave - 1) * NB + b;
         gu_load<BITS, GCPL, 1>(ga, wave > 0 && su < I ? shared_blob(A, Ly) : nullptr, D, I, su, lane);
     };
@@ -292,19 +292,15 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         lds_barrier();
 
         // router rows: RSL waves per row, RPB rows per block and round, the
-        // slices added in a fixed order; the logits go out tagged
-        const int nr = b < E ? (E - b + NB * RPB - 1) / (NB * RPB) : 0;
+        // slices added in a fixed order; the logits go out tagged.  A
+        // streamed layer (slab) takes the routing its slab was filled for
+        // and computes no logits.
+        const int nr = b < E && !Ly.slab ? (E - b + NB * RPB - 1) / (NB * RPB) : 0;
         {
-            const int nc4 = D / 4, Q = (nc4 + RSL - 1) / RSL, rsr = wave / RSL, sw = wave % RSL;
+            const int rsr = wave / RSL, sw = wave % RSL;
             for (int j = 0; j < nr; ++j) {
                 const int e = b + NB * (RPB * j + rsr);
-                float acc = 0.f;
-                for (int c0 = 0; c0 < Q; c0 += 64 * RN) {
-                    const int c_lo = sw * Q + c0, c_hi = min(nc4, sw * Q + Q);
-                    if (j > 0 || c0 > 0) rt_load<RN>(ra, e < E ? Ly.router + (size_t)e * D : nullptr, c_lo, c_hi, lane);
-                    acc += rt_finish<RN>(ra, v.xs, c_lo, c_hi, lane);
-                }
-                acc = group_sum<64>(acc);
+                const float acc = router_slice<RN>(ra, j == 0, e < E ? Ly.router + (size_t)e * D : nullptr, v.xs, D, sw, lane);
                 if (lane == 0) v.u[j * NWB + wave] = acc;
             }
         }
@@ -326,10 +322,21 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         // every wave its unit of routed gate/up rows (RX rows) as soon as its
         // slot's expert is known
         if (wave == 0) {
-            wave_topk_global<KPL>(A->tlog, t_log, E, K, sel, selw, rdy, l + 1, lane, A->flags);
-            if (b == 0 && lane < K) {
-                A->topk_idx[l * K + lane] = sel[lane];
-                A->topk_w[l * K + lane] = selw[lane];
+            if (Ly.slab) {
+                // streamed: the slab holds the experts of topk_idx (in that
+                // order, e.g. as moe_route chose them); take that routing as it is
+                if (lane < K) {
+                    sel[lane] = A->topk_idx[l * K + lane];
+                    selw[lane] = A->topk_w[l * K + lane];
+                }
+                __builtin_amdgcn_wave_barrier();
+                if (lane < K) __hip_atomic_store(rdy + lane, l + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                wave_topk_global<KPL>(A->tlog, t_log, E, K, sel, selw, rdy, l + 1, lane, A->flags);
+                if (b == 0 && lane < K) {
+                    A->topk_idx[l * K + lane] = sel[lane];
+                    A->topk_w[l * K + lane] = selw[lane];
+                }
             }
         } else if (const uint8_t *sh = shared_blob(A, Ly)) {
             for (int u = (wave - 1) * NB + b, j = 0; u < I; u += (NWB - 1) * NB, ++j) {

@@ -232,14 +232,14 @@ class StreamedStack:
                               shared=shared_of(l) if self.n_shared else None, blob_bytes=self.bb)
         return zc
 
-    def step_zero_copy(self, resid, x, stream=None, descs=None):
+    def step_zero_copy(self, resid, x, stream=None, descs=None, record=None):
         """One token through every layer reading the experts from host
         memory in the kernel (zero_copy_descs): one launch, no host wait."""
         if descs is None:
             if getattr(self, "_zc", None) is None:
                 self._zc = self.zero_copy_descs()
             descs = self._zc
-        moe_stack_step(descs, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
+        moe_stack_step(descs, resid, x, self.topk_idx, self.topk_w, self.workspace, record, stream)
 
     # ---- per-expert residency through device address tables (one launch per token)
     def host_addr(self, l: int, e: int) -> int:
@@ -285,18 +285,20 @@ class StreamedStack:
         torch.cuda.synchronize()
         return set(placed)
 
-    def step_placed(self, resid, x, stream=None):
+    def step_placed(self, resid, x, stream=None, record=None):
         """One token through every layer in address-table mode (after
         place_experts): one launch, HBM or host per expert."""
-        moe_stack_step(self._table_descs, resid, x, self.topk_idx, self.topk_w, self.workspace, None, stream)
+        moe_stack_step(self._table_descs, resid, x, self.topk_idx, self.topk_w, self.workspace, record, stream)
 
     def resident_layers(self) -> list[int]:
         return [l for l in range(self.layers) if self.descs[l].experts]
 
-    def step(self, resid, x, stream=None):
+    def step(self, resid, x, stream=None, record=None):
         """One token (resid, x: [1][D] device) through every layer; returns
-        when the last layer is enqueued on `stream`."""
+        when the last layer is enqueued on `stream`.  record (optional)
+        [layers+1][2][1][D] receives every layer's (resid, x) input and the
+        output."""
         from . import moe_stream_token
         cs = torch.cuda.current_stream() if stream is None else stream
         moe_stream_token(self.descs, self.streamer, resid, x, self.topk_idx, self.topk_w, self.host_ids,
-                         self.workspace, cs, self.copy_stream, self.events)
+                         self.workspace, cs, self.copy_stream, self.events, record=record)

@@ -39,10 +39,11 @@
  *    blob_bytes == moe_blob_bytes(...).
  *  - Device-side faults: an expert index outside [0, n_experts) met on the
  *    device sets bit MOE_DEVERR_EXPERT_RANGE in workspace word 0 and that
- *    expert's contribution is skipped; a grid-wide wait inside a fused layer
- *    step that does not complete within a few seconds sets
- *    MOE_DEVERR_BARRIER_TIMEOUT and the kernel runs to its end (its results
- *    are then invalid).  Word 0 is only ever OR-ed into.
+ *    expert's contribution is skipped; a wait of a fused layer step for
+ *    data from other workgroups is bounded (2^16 polls with a short sleep
+ *    between them, some tens of milliseconds): when it runs out,
+ *    MOE_DEVERR_BARRIER_TIMEOUT is set and the kernel runs to its end (its
+ *    results are then invalid).  Word 0 is only ever OR-ed into.
  *  - Thread safety: calls are reentrant.  Two calls that share a workspace
  *    must be ordered on one stream (they reuse its scratch and counters).
  */
@@ -127,11 +128,19 @@ typedef struct moe_layer_desc {
  * for this layer shape and token count (0 for an invalid descriptor).
  * The caller zero-fills a workspace once after allocating it; the library
  * keeps its counters consistent from call to call.  A workspace serves one
- * layer shape (hidden, inter, bits, top_k + n_shared) on one device: the
+ * layer shape (hidden, n_experts, inter, bits, top_k + n_shared) on one
+ * device, with any token count up to the one it was sized for: the
  * grid-barrier state of the fused layer step belongs to that shape's grid,
  * and a fused step on a workspace last used with another grid sets
  * MOE_DEVERR_WORKSPACE and does nothing. */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t n_tokens);
+
+/* The leading bytes of a workspace that carry state from one call to the
+ * next (error word, self-resetting arrival counters, the fused step's grid
+ * size, per-workgroup epochs and its exchange words).  They sit at the same
+ * offsets for every token count; every byte after them is scratch of one
+ * call.  0 for an invalid descriptor. */
+size_t moe_workspace_state_bytes(const moe_layer_desc *desc);
 
 /* Human-readable text of a status code; static storage. */
 const char *moe_strerror(int status);
@@ -175,7 +184,10 @@ int moe_expert_forward(const moe_layer_desc *desc, const float *x, int32_t n_tok
  *   resid <- resid + c
  *   x <- resid / sqrt(mean_d(resid^2) + rms_eps) * gamma
  * resid, x: [T][D], in/out, must not overlap.  topk_idx/topk_w: [T][K]
- * outputs (the routing used).
+ * outputs (the routing used), except in streamed mode (slab): there they are
+ * inputs, the routing the slab was filled for (slot k holds the expert
+ * topk_idx[k], typically moe_route's choice), and the step applies that
+ * routing and its weights as given, without routing again.
  */
 int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n_tokens,
                    int32_t *topk_idx, float *topk_w, void *workspace, size_t ws_bytes, void *stream);
@@ -193,9 +205,10 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
  * layers: host array of n_layers descriptors with the same hidden,
  * n_experts, top_k, inter, n_shared, bits and rms_eps (MOE_EINVAL
  * otherwise); each may be resident or streamed (its slab must then already
- * hold the layer's selected experts in selection order, as moe_layer_step
- * requires).  resid, x: [D] device, in/out, must not overlap.
- * topk_idx/topk_w: [n_layers][K] device outputs.  record: NULL or device
+ * hold the experts its row of topk_idx names, in that order, and that row
+ * and its topk_w row are inputs, as for moe_layer_step).  resid, x: [D]
+ * device, in/out, must not overlap.  topk_idx/topk_w: [n_layers][K] device,
+ * outputs for the resident layers.  record: NULL or device
  * [n_layers + 1][2][D], 16-byte aligned, receiving (resid, x) entering every
  * layer and the final output.  workspace: as moe_workspace_bytes(&layers[0],
  * 1).
@@ -343,7 +356,9 @@ int moe_host_free(void *p);
  *      (with st->cache set, cached experts are copied from HBM instead, see
  *      moe_expert_cache);
  *   3. compute_stream waits for the copies, then moe_layer_step reads the
- *      slot (the step recomputes the same routing bit for bit);
+ *      slot under the routing of step 1 (the slab's experts, in the order
+ *      they were copied, with step 1's weights; the step does not route
+ *      again);
  *   4. the shared expert of the next streamed layer (independent of
  *      routing) is queued on copy_stream right behind layer l's copies, so
  *      the link stays busy while the host waits for that layer's routing.
@@ -355,12 +370,14 @@ int moe_host_free(void *p);
  * NULL and their slab field is replaced by st->slab[j mod 2]; all share
  * top_k and n_shared, and st->slab_blobs == top_k + n_shared.  resid, x:
  * [D] device, in/out.  topk_idx, topk_w: device [n_layers][K] outputs.
+ * record: NULL or device [n_layers + 1][2][D], 16-byte aligned, receiving
+ * (resid, x) entering every layer and the final output.
  * events: five hipEvent_t (route_done, copy_done[2], compute_done[2]).
  * Returns after the last layer has been enqueued; the caller synchronises
  * compute_stream for the result.
  */
 int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_streamer *st, float *resid,
-                     float *x, int32_t *topk_idx, float *topk_w, int32_t *host_ids, void *workspace,
+                     float *x, int32_t *topk_idx, float *topk_w, float *record, int32_t *host_ids, void *workspace,
                      size_t ws_bytes, void *compute_stream, void *copy_stream, void *const *events);
 
 #ifdef __cplusplus

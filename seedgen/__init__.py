@@ -26,7 +26,7 @@ _DEV_SO = os.path.join(_HERE, "libseedgen_dev.so")
 # Expert id used for a layer's shared expert in the generator's keying.
 SHARED_ID = 0x7FFFFFFF
 # Stream ids inside a (seed, layer, expert) key.
-_STREAM_Q, _STREAM_SB, _STREAM_ROUTER, _STREAM_ACT = 0, 1, 2, 3
+_STREAM_Q, _STREAM_SB, _STREAM_ROUTER, _STREAM_ACT, _STREAM_GAMMA = 0, 1, 2, 3, 4
 
 
 def build(force: bool = False) -> None:
@@ -104,6 +104,7 @@ class Config:
     b_lo: float = -0.1
     b_hi: float = 0.0
     eps: float = 1e-6
+    gamma_sigma: float = 0.0  # RMSNorm weight: 1 + N(0, gamma_sigma^2) per element and layer (0: all ones)
     seed: int = 0x5EED0000
     feedback: bool = False   # next step's input = this step's output
     streamed: bool = False
@@ -183,8 +184,14 @@ def activations(cfg: Config, token0: int, n: int) -> np.ndarray:
     return np.stack([activation(cfg, token0 + t) for t in range(n)])
 
 
-def gamma(cfg: Config) -> np.ndarray:
-    return np.ones(cfg.D, dtype=np.float32)
+def gamma(cfg: Config, layer: int = 0) -> np.ndarray:
+    """RMSNorm weight of a layer, fp32 [D]: all ones (the workloads' value),
+    or with cfg.gamma_sigma > 0 the seeded 1 + N(0, gamma_sigma^2), distinct
+    per layer, for tests that must tell the layers' weights apart."""
+    if cfg.gamma_sigma == 0.0:
+        return np.ones(cfg.D, dtype=np.float32)
+    g = normal(key(cfg.seed, layer, 0, _STREAM_GAMMA), cfg.D, cfg.gamma_sigma)
+    return (np.float32(1.0) + g).astype(np.float32)
 
 
 def dev_blobs(cfg: Config, layer: int, expert0: int, n: int, dst_ptr: int, stream_ptr: int = 0,

@@ -42,6 +42,29 @@ def _desc(**kw):
     return ews.make_desc(**base)
 
 
+def test_workspace_state_is_independent_of_token_count():
+    """The state a call hands to the next (flags, counters, the fused step's
+    epochs and exchange words) leads the workspace at fixed offsets; every
+    per-call region of any token count lies after it."""
+    for shape in (dict(), dict(hidden=4096, n_experts=512, top_k=4, inter=1024), dict(bits=2, top_k=8, n_experts=64),
+                  dict(n_shared=0, hidden=448, inter=320)):
+        d = _desc(**shape)
+        d.blob_bytes = ews.moe_blob_bytes(d.hidden, d.inter, d.bits, 64)
+        state = ews.moe_workspace_state_bytes(d)
+        assert state > 0 and state % 256 == 0
+        S = d.top_k + d.n_shared
+        # epochs of up to 1024 workgroups and the tagged logits, h, residual rows and sums of squares
+        assert state >= 1024 * 64 + 8 * (1024 + d.n_experts + S * d.inter + d.hidden)
+        prev = 0
+        for T in range(1, 65):
+            total = ews.moe_workspace_bytes(d, T)
+            assert total > state and total >= prev
+            prev = total
+            if T >= 2:
+                assert min(ews.moe_workspace_grouping(d, T).values()) >= state
+    assert ews.moe_workspace_state_bytes(_desc(bits=3)) == 0
+
+
 def test_workspace_bytes():
     d = _desc()
     n = ews.moe_workspace_bytes(d, 1)
@@ -117,7 +140,8 @@ def test_stream_token_misuse_rejected():
     ev = (ctypes.c_void_p * 5)(*([1 << 4] * 5))
     evp = ctypes.cast(ev, ctypes.c_void_p)
     ws = 1 << 16
-    args = lambda d, n, s, e: (d, n, s, 1 << 8, 1 << 9, 1 << 10, 1 << 11, 1 << 14, ws, 1 << 30, None, None, e)
+    args = lambda d, n, s, e, rec=None: (d, n, s, 1 << 8, 1 << 9, 1 << 10, 1 << 11, rec, 1 << 14, ws, 1 << 30, None,
+                                         None, e)
     assert L.moe_stream_token(*args(descs, 0, ctypes.byref(st), evp)) == ews.MOE_EINVAL       # no layers
     assert L.moe_stream_token(*args(descs, 3, ctypes.byref(st), evp)) == ews.MOE_ESTATE       # > streamer layers
     assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), None)) == ews.MOE_EINVAL      # events
@@ -132,8 +156,9 @@ def test_stream_token_misuse_rejected():
     assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp)) == ews.MOE_ESTATE       # slab size
     st.slab_blobs = K + 1
     small_ws = args(descs, 2, ctypes.byref(st), evp)
-    small_ws = small_ws[:9] + (256,) + small_ws[10:]
+    small_ws = small_ws[:10] + (256,) + small_ws[11:]
     assert L.moe_stream_token(*small_ws) == ews.MOE_EINVAL                                    # workspace
+    assert L.moe_stream_token(*args(descs, 2, ctypes.byref(st), evp, (1 << 20) + 8)) == ews.MOE_EINVAL  # record
     # an expert cache that was not reset for this streamer
     meta = (ctypes.c_uint64 * 64)()
     cache = ews.ExpertCache(1 << 22, 4, ctypes.addressof(meta), 0, 0)

@@ -43,7 +43,7 @@ def run_and_check(cfg, layers, tokens, feedback=True, stats=None):
 
 @pytest.mark.parametrize("bits", [4, 2])
 def test_tiny_stack_feedback(bits):
-    cfg = seedgen.CONFIGS["tiny"].replace(bits=bits, layers=6, seed=0x5EED00D0 + bits)
+    cfg = seedgen.CONFIGS["tiny"].replace(bits=bits, layers=6, gamma_sigma=0.25, eps=3e-4, seed=0x5EED00D0 + bits)
     print(f"[gpu case] tiny stack bits={bits}", flush=True)
     _, stats = run_and_check(cfg, 6, 5)
     assert stats["layers"] == 30
@@ -51,7 +51,7 @@ def test_tiny_stack_feedback(bits):
 
 
 def test_wide_stack_fresh_tokens():
-    cfg = seedgen.CONFIGS["layer"].replace(E=32, layers=4, seed=0x5EED00D7)
+    cfg = seedgen.CONFIGS["layer"].replace(E=32, layers=4, gamma_sigma=0.25, eps=1e-4, seed=0x5EED00D7)
     print("[gpu case] hidden-4096 stack", flush=True)
     _, stats = run_and_check(cfg, 4, 3, feedback=False)
     assert stats["layers"] == 12
@@ -90,7 +90,7 @@ def test_stack_launch_equals_layer_by_layer(name, bits, layers):
     """moe_stack_step (persistent launches of up to 64 layers) gives the same
     bits as one moe_layer_step per layer, records included."""
     base = seedgen.CONFIGS["layer"].replace(E=32) if name == "layer32" else seedgen.CONFIGS[name]
-    cfg = base.replace(bits=bits, layers=layers, seed=0x5EED00E0 + layers + bits)
+    cfg = base.replace(bits=bits, layers=layers, gamma_sigma=0.25, seed=0x5EED00E0 + layers + bits)
     print(f"[gpu case] stack launch vs layer steps {name} bits={bits} layers={layers}", flush=True)
     st = W.build_stack(cfg, layers=layers)
     v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)

@@ -3,7 +3,9 @@ bytes of the selected experts, and a streamed stack gives bit-identical
 outputs and selections to a resident stack holding the same bytes (same
 kernels, same inputs), including an aliased host arena, a stack without
 a shared expert, and stacks where some layers stay resident (hybrid
-residency)."""
+residency).  Every mode's recorded layers are also checked against the
+oracle, each on the (resid, x) the GPU recorded entering it, with a
+distinct non-unit RMSNorm weight per layer and a non-default epsilon."""
 import numpy as np
 import pytest
 
@@ -42,33 +44,57 @@ def test_prefetch_copies_selected_blobs():
         ews.moe_stream_prefetch(st.streamer, 3, [0], 0, False, cs)
 
 
+def _g(cfg):
+    """The config with a distinct non-unit RMSNorm weight per layer and a
+    non-default epsilon."""
+    return cfg.replace(gamma_sigma=0.25, eps=3e-4)
+
+
+def _refs(cfg, st):
+    return [W.LayerRef(cfg, l, arena_blobs=st.P) for l in range(st.layers)]
+
+
+def _rec(st):
+    return torch.zeros(st.layers + 1, 2, 1, st.D, dtype=torch.float32, device="cuda")
+
+
+def _check(refs, st, rec, stats):
+    W.check_record(refs, rec.cpu().numpy(), st.topk_idx.cpu().numpy(), st.topk_w.cpu().numpy(), stats)
+
+
 def run_pair(cfg, layers, tokens, arena_blobs=None):
     st = W.build_streamed(cfg, layers=layers, arena_blobs=arena_blobs)
     rs = W.resident_twin(st)
+    refs = _refs(cfg, st)
+    rec_s, rec_r = _rec(st), _rec(st)
+    stats = {}
     v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
     xs, xr = v.clone(), v.clone()
     for t in range(tokens):
         r_s, r_r = xs.clone(), xr.clone()
-        st.step(r_s, xs)
-        rs.step(r_r, xr)
+        st.step(r_s, xs, record=rec_s)
+        rs.step(r_r, xr, record=rec_r)
         torch.cuda.synchronize()
         assert int(st.workspace[:4].view(torch.int32).item()) == 0, "device error flags (streamed)"
         assert torch.equal(st.topk_idx, rs.topk_idx), t
         assert torch.equal(st.topk_w, rs.topk_w), t
         assert torch.equal(r_s, r_r) and torch.equal(xs, xr), t
+        assert torch.equal(rec_s, rec_r), t
         assert bool(torch.isfinite(xs).all())
+        _check(refs, st, rec_s, stats)
+    assert stats["layers"] == layers * tokens
     return st, rs
 
 
 @pytest.mark.parametrize("name,bits", [("tiny", 4), ("tiny", 2)])
 def test_streamed_equals_resident_tiny(name, bits):
-    cfg = seedgen.CONFIGS[name].replace(bits=bits, layers=6, seed=0x5EED0E10 + bits)
+    cfg = _g(seedgen.CONFIGS[name].replace(bits=bits, layers=6, seed=0x5EED0E10 + bits))
     print(f"[gpu case] streamed tiny bits={bits}", flush=True)
     run_pair(cfg, 6, 4)
 
 
 def test_streamed_equals_resident_hidden4096():
-    cfg = seedgen.CONFIGS["layer"].replace(E=24, layers=5, seed=0x5EED0E20)
+    cfg = _g(seedgen.CONFIGS["layer"].replace(E=24, layers=5, seed=0x5EED0E20))
     print("[gpu case] streamed hidden-4096", flush=True)
     st, _ = run_pair(cfg, 5, 3)
     # the selections really vary across layers, so the slots are exercised
@@ -77,13 +103,13 @@ def test_streamed_equals_resident_hidden4096():
 
 
 def test_streamed_aliased_arena():
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=5, seed=0x5EED0E30)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(layers=5, seed=0x5EED0E30))
     print("[gpu case] streamed aliased arena", flush=True)
     run_pair(cfg, 5, 3, arena_blobs=23)
 
 
 def test_streamed_no_shared():
-    cfg = seedgen.CONFIGS["tiny"].replace(n_shared=0, layers=4, seed=0x5EED0E40)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(n_shared=0, layers=4, seed=0x5EED0E40))
     print("[gpu case] streamed without shared expert", flush=True)
     run_pair(cfg, 4, 3)
 
@@ -92,7 +118,7 @@ def test_streamed_matches_oracle_first_layer():
     """Layer 0 of the streamed stack against the oracle (the later layers
     are covered by bitwise equality with the resident stack, whose
     per-layer outputs the resident stack tests check)."""
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=1, seed=0x5EED0E50)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(layers=1, seed=0x5EED0E50))
     print("[gpu case] streamed layer 0 vs oracle", flush=True)
     st = W.build_streamed(cfg, layers=1)
     x0 = seedgen.activation(cfg, 0)
@@ -111,10 +137,11 @@ def test_hybrid_residency_equals_resident(pattern):
     stream.  Output, selections and weights equal the resident stack's bit
     for bit, whichever layers stream (first streamed layer after resident
     ones, resident runs in the middle and at the end, none streamed)."""
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=len(pattern), seed=0x5EED0E60)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(layers=len(pattern), seed=0x5EED0E60))
     print(f"[gpu case] hybrid residency {pattern}", flush=True)
     st = W.build_streamed(cfg, layers=len(pattern), arena_blobs=29)
     rs = W.resident_twin(st)
+    refs, rec, stats = _refs(cfg, st), _rec(st), {}
     for l, c in enumerate(pattern):
         if c == "R":
             st.set_resident(l, rs.arena.data_ptr() + l * st.E * st.bb, rs.shared.data_ptr() + l * st.bb)
@@ -123,13 +150,15 @@ def test_hybrid_residency_equals_resident(pattern):
     xs, xr = v.clone(), v.clone()
     for t in range(3):
         r_s, r_r = xs.clone(), xr.clone()
-        st.step(r_s, xs)
+        st.step(r_s, xs, record=rec)
         rs.step(r_r, xr)
         torch.cuda.synchronize()
         assert int(st.workspace[:4].view(torch.int32).item()) == 0
         assert torch.equal(st.topk_idx, rs.topk_idx), t
         assert torch.equal(st.topk_w, rs.topk_w), t
         assert torch.equal(r_s, r_r) and torch.equal(xs, xr), t
+        _check(refs, st, rec, stats)
+    assert stats["layers"] == 3 * len(pattern)
     # and back to fully streamed
     for l in range(len(pattern)):
         st.set_resident(l, None)
@@ -175,10 +204,11 @@ def test_expert_cache_equals_resident(n_slots, pattern, speculate, bits):
     streamed layer's shared blob, then (speculate) the previous token's
     selection of that layer as guesses.  Tokens repeat, so a cache that
     holds every blob serves the repeats entirely from HBM."""
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=len(pattern), bits=bits, seed=0x5EED0E70 + bits)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(layers=len(pattern), bits=bits, seed=0x5EED0E70 + bits))
     print(f"[gpu case] expert cache slots={n_slots} {pattern} speculate={speculate} bits={bits}", flush=True)
     st = W.build_streamed(cfg, layers=len(pattern), arena_blobs=31)
     rs = W.resident_twin(st)
+    refs, rec, stats = _refs(cfg, st), _rec(st), {}
     for l, c in enumerate(pattern):
         if c == "R":
             st.set_resident(l, rs.arena.data_ptr() + l * st.E * st.bb, rs.shared.data_ptr() + l * st.bb)
@@ -188,12 +218,13 @@ def test_expert_cache_equals_resident(n_slots, pattern, speculate, bits):
     for t, v0 in enumerate(inputs):
         v = torch.from_numpy(v0).cuda().view(1, -1)
         r_s, x_s, r_r, x_r = v.clone(), v.clone(), v.clone(), v.clone()
-        st.step(r_s, x_s)
+        st.step(r_s, x_s, record=rec)
         rs.step(r_r, x_r)
         torch.cuda.synchronize()
         assert int(st.workspace[:4].view(torch.int32).item()) == 0
         assert torch.equal(st.topk_idx, rs.topk_idx), t
         assert torch.equal(r_s, r_r) and torch.equal(x_s, x_r), t
+        _check(refs, st, rec, stats)
         sel = st.topk_idx.cpu().numpy()
         streamed = [l for l, c in enumerate(pattern) if c == "S"]
         LE = len(pattern) * cfg.E
@@ -222,21 +253,23 @@ def test_zero_copy_equals_resident(arena_blobs, bits):
     host wait).  Outputs and selections equal the resident stack's holding
     the same bytes, bit for bit, with a full and an aliased arena (32 blobs =
     two layers' experts)."""
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=5, bits=bits, seed=0x5EED0E80 + bits)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(layers=5, bits=bits, seed=0x5EED0E80 + bits))
     print(f"[gpu case] zero-copy arena_blobs={arena_blobs} bits={bits}", flush=True)
     st = W.build_streamed(cfg, layers=5, arena_blobs=arena_blobs)
     rs = W.resident_twin(st)
+    refs, rec, stats = _refs(cfg, st), _rec(st), {}
     v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
     xz, xr = v.clone(), v.clone()
     for t in range(3):
         r_z, r_r = xz.clone(), xr.clone()
-        st.step_zero_copy(r_z, xz)
+        st.step_zero_copy(r_z, xz, record=rec)
         rs.step(r_r, xr)
         torch.cuda.synchronize()
         assert int(st.workspace[:4].view(torch.int32).item()) == 0
         assert torch.equal(st.topk_idx, rs.topk_idx), t
         assert torch.equal(st.topk_w, rs.topk_w), t
         assert torch.equal(r_z, r_r) and torch.equal(xz, xr), t
+        _check(refs, st, rec, stats)
     # layers 0 and 1 from HBM (the twin's arena), the rest from host memory, one launch
     zh = st.zero_copy_hybrid_descs(2, lambda l: rs.arena.data_ptr() + l * st.E * st.bb,
                                    lambda l: rs.shared.data_ptr() + l * st.bb)
@@ -263,10 +296,11 @@ def test_address_tables_equal_resident(arena_blobs, n_slots, bits):
     token).  Outputs equal the resident stack's bit for bit; one layer
     through moe_layer_step in the same mode does too."""
     import expert_weight_streaming_amd as ews
-    cfg = seedgen.CONFIGS["tiny"].replace(layers=4, bits=bits, seed=0x5EED0E90 + bits)
+    cfg = _g(seedgen.CONFIGS["tiny"].replace(layers=4, bits=bits, seed=0x5EED0E90 + bits))
     print(f"[gpu case] address tables arena={arena_blobs} slots={n_slots} bits={bits}", flush=True)
     st = W.build_streamed(cfg, layers=4, arena_blobs=arena_blobs)
     rs = W.resident_twin(st)
+    refs, rec, stats = _refs(cfg, st), _rec(st), {}
     hot = [(l, e) for l in range(4) for e in range(cfg.E) if (l + e) % 3 == 0]
     placed = st.place_experts(n_slots, hot)
     assert len(placed) == min(n_slots, len(hot))
@@ -274,12 +308,13 @@ def test_address_tables_equal_resident(arena_blobs, n_slots, bits):
     xp, xr = v.clone(), v.clone()
     for t in range(3):
         r_p, r_r = xp.clone(), xr.clone()
-        st.step_placed(r_p, xp)
+        st.step_placed(r_p, xp, record=rec)
         rs.step(r_r, xr)
         torch.cuda.synchronize()
         assert int(st.workspace[:4].view(torch.int32).item()) == 0
         assert torch.equal(st.topk_idx, rs.topk_idx), t
         assert torch.equal(r_p, r_r) and torch.equal(xp, xr), t
+        _check(refs, st, rec, stats)
     r_p, r_r, x_p, x_r = v.clone(), v.clone(), v.clone(), v.clone()
     ews.moe_layer_step(st._table_descs[0], r_p, x_p, 1, st.topk_idx[0], st.topk_w[0], st.workspace)
     rs.layer_step(0, r_r, x_r)
@@ -291,19 +326,21 @@ def test_zero_copy_and_tables_hidden4096():
     """The hidden-4096 shape (the 60-layer stack's kernel instantiation):
     zero-copy and address-table tokens equal the resident stack bit for
     bit."""
-    cfg = seedgen.CONFIGS["layer"].replace(E=24, layers=3, seed=0x5EED0EA0)
+    cfg = _g(seedgen.CONFIGS["layer"].replace(E=24, layers=3, seed=0x5EED0EA0))
     print("[gpu case] zero-copy and tables hidden-4096", flush=True)
     st = W.build_streamed(cfg, layers=3)
     rs = W.resident_twin(st)
+    refs, rec, stats = _refs(cfg, st), _rec(st), {}
     st.place_experts(20, [(l, e) for l in range(3) for e in range(0, cfg.E, 3)])
     v = torch.from_numpy(seedgen.activation(cfg, 0)).cuda().view(1, -1)
     for step in (st.step_zero_copy, st.step_placed):
         xs, xr = v.clone(), v.clone()
         for t in range(2):
             r_s, r_r = xs.clone(), xr.clone()
-            step(r_s, xs)
+            step(r_s, xs, record=rec)
             rs.step(r_r, xr)
             torch.cuda.synchronize()
             assert int(st.workspace[:4].view(torch.int32).item()) == 0
             assert torch.equal(st.topk_idx, rs.topk_idx), (step.__name__, t)
             assert torch.equal(r_s, r_r) and torch.equal(xs, xr), (step.__name__, t)
+            _check(refs, st, rec, stats)

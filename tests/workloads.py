@@ -25,6 +25,7 @@ def build_stack(cfg, layers=None, T=1):
         if cfg.n_shared:
             seedgen.dev_blobs(cfg, l, seedgen.SHARED_ID, 1, st.shared_ptr(l), s)
         st.router[l].copy_(torch.from_numpy(seedgen.router(cfg, l)))
+        st.gamma[l].copy_(torch.from_numpy(seedgen.gamma(cfg, l)))
     torch.cuda.synchronize()
     return st
 
@@ -52,16 +53,24 @@ class LayerRef:
     """Oracle evaluation of one layer of a config, blobs regenerated on the
     host and cached."""
 
-    def __init__(self, cfg, layer, shared=True):
+    def __init__(self, cfg, layer, shared=True, arena_blobs=None):
+        """arena_blobs: the host arena of a streamed stack holds that many
+        blobs and expert (layer, e) reads blob (layer*E + e) mod arena_blobs,
+        which holds the seeded blob of (p // E, p % E)."""
         self.cfg, self.layer = cfg, layer
         self.Wr = seedgen.router(cfg, layer)
-        self.gamma = seedgen.gamma(cfg)
+        self.gamma = seedgen.gamma(cfg, layer)
+        self.P = arena_blobs
         self._blobs = {}
         self.shared = seedgen.blob(cfg, layer, seedgen.SHARED_ID) if (shared and cfg.n_shared) else None
 
     def blob(self, e):
         if e not in self._blobs:
-            self._blobs[e] = seedgen.blob(self.cfg, self.layer, e)
+            if self.P is None:
+                self._blobs[e] = seedgen.blob(self.cfg, self.layer, e)
+            else:
+                p = (self.layer * self.cfg.E + e) % self.P
+                self._blobs[e] = seedgen.blob(self.cfg, p // self.cfg.E, p % self.cfg.E)
         return self._blobs[e]
 
     def run(self, r, x, forced_sel=None):
@@ -92,6 +101,19 @@ def check_layer(ref: LayerRef, r_in, x_in, gpu_sel, gpu_w, gpu_r, gpu_x, stats=N
     return res
 
 
+def check_record(refs, rec, sel, w, stats=None):
+    """Every layer of a recorded chain against the oracle, each on the
+    (resid, x) the GPU recorded entering it (rec [L+1][2][1][D] or
+    [L+1][2][D]; sel, w [L][1][K] or [L][K])."""
+    R = np.asarray(rec, np.float32).reshape(len(refs) + 1, 2, -1)
+    sel = np.asarray(sel).reshape(len(refs), -1)
+    w = np.asarray(w).reshape(len(refs), -1)
+    stats = {} if stats is None else stats
+    for l, ref in enumerate(refs):
+        check_layer(ref, R[l, 0], R[l, 1], sel[l], w[l], R[l + 1, 0], R[l + 1, 1], stats)
+    return stats
+
+
 def build_streamed(cfg, layers=None, arena_blobs=None):
     """A StreamedStack whose host arena holds the seeded blobs: host blob p
     is expert (p // E, p % E); expert (l, e) streams host blob
@@ -112,6 +134,7 @@ def build_streamed(cfg, layers=None, arena_blobs=None):
             seedgen.dev_blobs(cfg, l, seedgen.SHARED_ID, 1, tmp.data_ptr(), s)
             st.host_shared_blob(l).copy_(tmp[:st.bb])
         st.router[l].copy_(torch.from_numpy(seedgen.router(cfg, l)))
+        st.gamma[l].copy_(torch.from_numpy(seedgen.gamma(cfg, l)))
     torch.cuda.synchronize()
     return st
 

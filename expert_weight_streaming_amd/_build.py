@@ -12,6 +12,7 @@ OBJ_DIR = os.path.join(HERE, "_obj")
 UNITS = [
     ("moe_abi.hip", [], "moe_abi.o"),
     ("moe_kernels.hip", [], "moe_kernels.o"),
+    ("moe_gemv.hip", [], "moe_gemv.o"),
     # MFMA results in VGPRs (the AGPR form costs a copy per result register)
     ("moe_batch.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "moe_batch.o"),
     ("moe_stack.hip", ["-DMOE_STACK_BITS=4"], "moe_stack4.o"),

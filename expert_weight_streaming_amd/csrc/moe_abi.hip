@@ -482,6 +482,31 @@ int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid,
                          (hipStream_t)stream);
 }
 
+int moe_expert_gemv(const moe_layer_desc *desc, const float *x, int32_t first, int32_t count, float *h, float *y,
+                    void *stream)
+{
+    int rc = check_desc(desc, 1);
+    if (rc) return rc;
+    if (!desc->experts || desc->expert_addr)
+        return fail(MOE_EINVAL, "moe_expert_gemv needs a resident layer (experts in device-visible memory)");
+    if (first < 0 || count < 1 || (int64_t)first + count > desc->n_experts)
+        return fail(MOE_EINVAL, "expert range [%d, %d + %d) outside [0, %d)", first, first, count, desc->n_experts);
+    if ((rc = check_ptr(x, "x")) || (rc = check_ptr(h, "h")) || (rc = check_ptr(y, "y"))) return rc;
+    moe::GemvArgs a;
+    a.experts = desc->experts;
+    a.blob_bytes = desc->blob_bytes;
+    a.first = first;
+    a.count = count;
+    a.x = x;
+    a.h = h;
+    a.y = y;
+    a.D = desc->hidden;
+    a.I = desc->inter;
+    hipError_t e = moe::launch_expert_gemv(a, desc->bits, (hipStream_t)stream, nullptr);
+    if (e == hipErrorNotSupported) return fail(MOE_EUNSUPPORTED, "no expert GEMV plan for this shape");
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert GEMV launch");
+}
+
 int moe_layer_plan(const moe_layer_desc *desc, int32_t n_tokens, int32_t *out)
 {
     int rc = check_desc(desc, n_tokens);

@@ -144,6 +144,17 @@ struct BatchArgs {
     int32_t mode;            // 0: yout = combine; 1: residual + RMSNorm
 };
 
+// The expert GEMVs of a range of resident experts (moe_gemv.hip).
+struct GemvArgs {
+    const uint8_t *experts;  // resident arena, blob_bytes apart
+    uint64_t blob_bytes;
+    int32_t first, count;    // experts first .. first + count - 1
+    const float *x;          // [D]
+    float *h;                // [count][I]
+    float *y;                // [count][D]
+    int32_t D, I;
+};
+
 // Down-projection lane split: LPR lanes per row (a power of two <= 64),
 // cpl 16-byte chunks per lane.
 struct DownShape {
@@ -156,6 +167,11 @@ hipError_t launch_batch_route(const BatchArgs &a, int do_topk, int bits, hipStre
 hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s);
 hipError_t launch_gate_up(const GateUpArgs &a, int bits, hipStream_t s);
 hipError_t launch_down(const DownArgs &a, int bits, hipStream_t s);
+
+struct LayerPlan;
+// hipErrorNotSupported (nothing launched) for a shape without a plan; p
+// (optional) receives the launch shape.
+hipError_t launch_expert_gemv(const GemvArgs &a, int bits, hipStream_t s, LayerPlan *p);
 
 // Launch plan of the persistent stack kernel for a shape (nothing
 // launched): grid 0 when the shape takes the three-launch path.

@@ -217,6 +217,24 @@ int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid,
                    float *topk_w, float *record, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * The dequantised expert GEMVs alone, for a range of a resident layer's
+ * experts and one activation vector: the matrix-vector kernel the pages
+ * measure against the memory bandwidth (hakusoku.com, 「Apple Siliconにおける
+ * メモリ制約」), in the dequant form w = q*scale + bias.  For n < count and
+ * expert e = first + n:
+ *   h[n][i] = silu(sum_j Wg_e[i][j] x[j]) * sum_j Wu_e[i][j] x[j]
+ *   y[n][o] = sum_i Wd_e[o][i] h[n][i]
+ * No routing, no weighting, no residual.  One launch; a workgroup runs whole
+ * experts (gate/up, then down from h kept on chip), so every byte of the
+ * range's blobs is read once.
+ * desc: resident (experts != NULL, no address table); 0 <= first, 1 <=
+ * count, first + count <= n_experts (MOE_EINVAL otherwise).  x: [D]; h:
+ * [count][I]; y: [count][D]; all 16-byte aligned device memory.
+ */
+int moe_expert_gemv(const moe_layer_desc *desc, const float *x, int32_t first, int32_t count, float *h, float *y,
+                    void *stream);
+
+/*
  * How moe_layer_step / moe_stack_step will run this shape on the current
  * device (queries the device, enqueues nothing).  out[7] (host) receives:
  * fused (1 when a token's layers run as one persistent launch with

@@ -217,3 +217,21 @@ def test_host_alloc_rejects_bad_arguments():
     assert L.moe_host_alloc(0, ctypes.byref(p)) == ews.MOE_EINVAL
     assert L.moe_host_alloc(16, None) == ews.MOE_EINVAL
     assert L.moe_host_free(None) == ews.MOE_OK
+
+
+def test_expert_gemv_validation():
+    """moe_expert_gemv checks its range, its layer mode and its buffers before
+    enqueueing anything."""
+    L = ews.lib()
+    d = _desc()
+    ok = dict(x=1 << 20, h=1 << 21, y=1 << 22)
+    call = lambda desc, first, count, x=ok["x"], h=ok["h"], y=ok["y"]: L.moe_expert_gemv(
+        ctypes.byref(desc), x, first, count, h, y, None)
+    assert call(d, -1, 2) == ews.MOE_EINVAL
+    assert call(d, 0, 0) == ews.MOE_EINVAL
+    assert call(d, 10, 7) == ews.MOE_EINVAL
+    assert call(d, 0, 2, x=None) == ews.MOE_EINVAL
+    assert call(d, 0, 2, h=(1 << 21) + 4) == ews.MOE_EINVAL
+    assert call(_desc(experts=None, slab=1 << 23), 0, 2) == ews.MOE_EINVAL
+    assert call(_desc(bits=3), 0, 2) == ews.MOE_EINVAL
+

@@ -93,7 +93,7 @@ def check_layer(ref: LayerRef, r_in, x_in, gpu_sel, gpu_w, gpu_r, gpu_x, stats=N
             stats["near_ties"] = stats.get("near_ties", 0) + 1
         res = ref.run(r_in, x_in, forced_sel=np.array(gsel, np.int32))
     w_ref = dict(zip((int(e) for e in res["sel"]), res["w"]))
-    assert_close([gpu_w[k] for k in range(len(gsel))], [w_ref[e] for e in gsel], "routing weights", rel=1e-5)
+    assert_close([gpu_w[k] for k in range(len(gsel))], [w_ref[e] for e in gsel], "routing weights")
     assert_close(gpu_r, res["r"], "residual")
     assert_close(gpu_x, res["x"], "normalised output")
     if stats is not None:

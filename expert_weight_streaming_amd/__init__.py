@@ -49,7 +49,7 @@ class Streamer(ctypes.Structure):
 
 
 EXPORTS = ["moe_blob_bytes", "moe_workspace_bytes", "moe_workspace_state_bytes", "moe_strerror", "moe_last_error", "moe_route",
-           "moe_expert_forward", "moe_layer_step", "moe_stack_step", "moe_layer_plan", "moe_expert_gemv", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
+           "moe_expert_forward", "moe_layer_step", "moe_stack_step", "moe_stack_step_noalloc", "moe_layer_plan", "moe_expert_gemv", "moe_workspace_grouping", "moe_stream_prefetch", "moe_stream_token",
            "moe_host_alloc", "moe_host_free", "moe_expert_cache_meta_bytes", "moe_expert_cache_reset"]
 
 _lib = None
@@ -82,6 +82,8 @@ def lib():
         L.moe_stack_step.argtypes = [ctypes.POINTER(LayerDesc), i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_gemv.restype = ctypes.c_int
         L.moe_expert_gemv.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, i32, vp, vp, vp]
+        L.moe_stack_step_noalloc.restype = ctypes.c_int
+        L.moe_stack_step_noalloc.argtypes = [ctypes.POINTER(LayerDesc), i32, vp, vp, vp, vp, vp, vp, vp]
         L.moe_layer_plan.restype = ctypes.c_int
         L.moe_layer_plan.argtypes = [ctypes.POINTER(LayerDesc), i32, vp]
         L.moe_workspace_grouping.restype = ctypes.c_int
@@ -179,6 +181,14 @@ def moe_stack_step(descs, resid, x, topk_idx, topk_w, workspace, record=None, st
 
 def moe_expert_gemv(desc, x, first: int, count: int, h, y, stream=None) -> None:
     _check(lib().moe_expert_gemv(ctypes.byref(desc), _ptr(x), first, count, _ptr(h), _ptr(y), _stream(stream)))
+
+
+def moe_stack_step_noalloc(descs, resid, x, topk_idx, topk_w, record=None, flags=None, stream=None) -> None:
+    """moe_stack_step on the library's own scratch (no workspace); descs: a
+    ctypes array of LayerDesc; flags: None or a device int32/uint32 tensor of
+    one element receiving the device error bits."""
+    _check(lib().moe_stack_step_noalloc(descs, len(descs), _ptr(resid), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                                        _ptr(record), _ptr(flags), _stream(stream)))
 
 
 def moe_layer_plan(desc, n_tokens: int = 1) -> dict:

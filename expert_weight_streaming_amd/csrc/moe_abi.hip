@@ -4,7 +4,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
+
+// The workspace of moe_stack_step_noalloc: one array per device in the
+// library's code object, held until the process ends.  Host code uses only
+// the per-device addresses that hipGetSymbolAddress returns for it.
+static __device__ __align__(256) uint8_t scratch[1u << 20];
 
 namespace {
 
@@ -179,14 +186,15 @@ int enqueue_route(const moe_layer_desc *d, const float *x, int32_t *idx, float *
 // Gate/up then down + combine.  y != NULL: y = combine (no residual).
 // y == NULL: resid += combine, xout = RMSNorm(resid) * gamma.
 int enqueue_forward(const moe_layer_desc *d, const float *x, const int32_t *idx, const float *w, float *y,
-                    float *resid, float *xout, uint8_t *ws, const moe::WsLayout &L, hipStream_t s)
+                    float *resid, float *xout, uint8_t *ws, const moe::WsLayout &L, hipStream_t s,
+                    uint32_t *flags = nullptr)
 {
     moe::GateUpArgs g;
     g.src = blob_src(d);
     g.topk_idx = idx;
     g.x = x;
     g.h = reinterpret_cast<float *>(ws + L.h);
-    g.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    g.flags = flags ? flags : reinterpret_cast<uint32_t *>(ws + L.flags);
     g.D = d->hidden;
     g.I = d->inter;
     g.blocks_per_slot = moe::gate_up_blocks_per_slot(d->inter, d->top_k + d->n_shared);
@@ -240,7 +248,7 @@ hipError_t stack_plan_or_launch(const moe::StackArgs *a, const moe_layer_desc *d
 // three launches per layer (route, gate/up, down with residual and norm).
 // record (optional): [n+1][2][D] (r, x) entering every layer and the output.
 int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, int32_t *idx, float *w, float *record,
-                  uint8_t *ws, const moe::WsLayout &L, hipStream_t s)
+                  uint8_t *ws, const moe::WsLayout &L, hipStream_t s, uint32_t *flags = nullptr)
 {
     const moe_layer_desc *d = &ds[0];
     const int D = d->hidden, K = d->top_k;
@@ -272,7 +280,7 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
         a.tss = reinterpret_cast<uint64_t *>(ws + L.tss);
         a.hdr = reinterpret_cast<uint32_t *>(ws + L.hdr);
         a.slots = reinterpret_cast<uint32_t *>(ws + L.slots);
-        a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+        a.flags = flags ? flags : reinterpret_cast<uint32_t *>(ws + L.flags);
         a.blob_bytes = d->blob_bytes;
         a.n_layers = cnt;
         a.D = D;
@@ -300,7 +308,7 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
             const bool slab = !dj->experts && !dj->expert_addr;
             int rc = slab ? MOE_OK : enqueue_route(dj, x, ij, wj, nullptr, ws, L, s);
             if (rc) return rc;
-            if ((rc = enqueue_forward(dj, x, ij, wj, nullptr, resid, x, ws, L, s))) return rc;
+            if ((rc = enqueue_forward(dj, x, ij, wj, nullptr, resid, x, ws, L, s, flags))) return rc;
         }
         if (record) {
             float *rn = record + (size_t)(l0 + cnt) * 2 * D;
@@ -455,8 +463,13 @@ int moe_layer_step(const moe_layer_desc *desc, float *resid, float *x, int32_t n
     return enqueue_stack(desc, 1, resid, x, topk_idx, topk_w, nullptr, (uint8_t *)workspace, L, (hipStream_t)stream);
 }
 
-int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
-                   float *topk_w, float *record, void *workspace, size_t ws_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// moe_stack_step's checks of everything but the workspace.
+int check_stack(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
+                float *topk_w, float *record)
 {
     if (!layers || n_layers < 1) return fail(MOE_EINVAL, "no layers");
     int rc = check_desc(&layers[0], 1);
@@ -476,8 +489,78 @@ int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid,
     const size_t span = (size_t)d->hidden * 4;
     if ((const uint8_t *)resid < (const uint8_t *)x + span && (const uint8_t *)x < (const uint8_t *)resid + span)
         return fail(MOE_EINVAL, "resid and x overlap");
-    if ((rc = check_ws(d, 1, workspace, ws_bytes))) return rc;
-    const moe::WsLayout L = layout(d, 1);
+    return MOE_OK;
+}
+
+// Per-device address of `scratch` (hipGetSymbolAddress with the device
+// current) and whether it has been cleared by an eager launch.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[kMaxDevices];
+bool g_scratch_clear[kMaxDevices];
+
+__global__ void k_zero16(uint4 *p, uint32_t n16)
+{
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_stack_step_noalloc(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
+                           float *topk_w, float *record, uint32_t *flags, void *stream)
+{
+    int rc = check_stack(layers, n_layers, resid, x, topk_idx, topk_w, record);
+    if (rc) return rc;
+    if (flags && ((uintptr_t)flags & 3u)) return fail(MOE_EINVAL, "flags not 4-byte aligned");
+    const moe::WsLayout L = layout(&layers[0], 1);
+    if (L.total > sizeof(scratch))
+        return fail(MOE_EINVAL, "this shape needs %zu bytes of workspace, more than the %zu of the library's scratch",
+                    L.total, sizeof(scratch));
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "current device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device %d beyond the %d the library serves", dev, kMaxDevices);
+    uint8_t *ws = nullptr;
+    bool clear = false;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            void *p = nullptr;
+            if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return hip_fail(e, "scratch address");
+            g_scratch_ptr[dev] = static_cast<uint8_t *>(p);
+        }
+        ws = g_scratch_ptr[dev];
+        clear = !g_scratch_clear[dev];
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (clear) {
+        // the epochs and exchange words must start at zero: a fill kernel
+        // ahead of the step (also when the stream is being captured, so that
+        // a graph clears it on each replay); once an eager launch has
+        // cleared it, the state carries over from call to call
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(s, &cap)) != hipSuccess) return hip_fail(e, "capture status");
+        hipLaunchKernelGGL(k_zero16, dim3(256), dim3(256), 0, s, reinterpret_cast<uint4 *>(ws),
+                           (uint32_t)(sizeof(scratch) / 16));
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "scratch clear");
+        if (cap == hipStreamCaptureStatusNone) {
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            g_scratch_clear[dev] = true;
+        }
+    }
+    return enqueue_stack(layers, n_layers, resid, x, topk_idx, topk_w, record, ws, L, s, flags);
+}
+
+int moe_stack_step(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
+                   float *topk_w, float *record, void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_stack(layers, n_layers, resid, x, topk_idx, topk_w, record);
+    if (rc) return rc;
+    if ((rc = check_ws(&layers[0], 1, workspace, ws_bytes))) return rc;
+    const moe::WsLayout L = layout(&layers[0], 1);
     return enqueue_stack(layers, n_layers, resid, x, topk_idx, topk_w, record, (uint8_t *)workspace, L,
                          (hipStream_t)stream);
 }

@@ -235,6 +235,25 @@ int moe_expert_gemv(const moe_layer_desc *desc, const float *x, int32_t first, i
                     void *stream);
 
 /*
+ * moe_stack_step without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  The library's own scratch serves as the
+ * workspace: a 1 MiB device array per device, in the library's code object,
+ * held until the process ends (every valid one-token shape fits; a shape
+ * that does not returns MOE_EINVAL).  It is cleared before its first use on
+ * a device and then keeps the state one call hands to the next, exactly as
+ * a caller's workspace does.  Every call on a device shares that device's
+ * array: calls that overlap on one device (on two streams, or from two
+ * threads without ordering) race and their results are undefined; order
+ * them on one stream.  The call allocates and frees nothing.
+ * Arguments as moe_stack_step; flags: NULL or a device uint32 (4-byte
+ * aligned, zeroed by the caller) into which the call's kernels OR their
+ * MOE_DEVERR_* bits (with NULL they go to the scratch, unseen).
+ */
+int moe_stack_step_noalloc(const moe_layer_desc *layers, int32_t n_layers, float *resid, float *x, int32_t *topk_idx,
+                           float *topk_w, float *record, uint32_t *flags, void *stream);
+
+/*
  * How moe_layer_step / moe_stack_step will run this shape on the current
  * device (queries the device, enqueues nothing).  out[7] (host) receives:
  * fused (1 when a token's layers run as one persistent launch with

@@ -235,3 +235,19 @@ def test_expert_gemv_validation():
     assert call(_desc(experts=None, slab=1 << 23), 0, 2) == ews.MOE_EINVAL
     assert call(_desc(bits=3), 0, 2) == ews.MOE_EINVAL
 
+
+def test_noalloc_scratch_holds_every_one_token_shape():
+    """The library's scratch (1 MiB per device) holds the one-token workspace
+    of the largest valid shape; bad arguments are refused before any device
+    work."""
+    d = _desc(hidden=8192, n_experts=4096, top_k=8, inter=4096)
+    d.blob_bytes = ews.moe_blob_bytes(8192, 4096, 4, 64)
+    assert 0 < ews.moe_workspace_bytes(d, 1) <= 1 << 20
+    L = ews.lib()
+    descs = (ews.LayerDesc * 1)(_desc())
+    assert L.moe_stack_step_noalloc(None, 1, 1 << 20, 1 << 21, 1 << 22, 1 << 23, None, None, None) == ews.MOE_EINVAL
+    assert L.moe_stack_step_noalloc(descs, 0, 1 << 20, 1 << 21, 1 << 22, 1 << 23, None, None, None) == ews.MOE_EINVAL
+    assert L.moe_stack_step_noalloc(descs, 1, 1 << 20, 1 << 20, 1 << 22, 1 << 23, None, None, None) == ews.MOE_EINVAL
+    assert L.moe_stack_step_noalloc(descs, 1, 1 << 20, 1 << 21, 1 << 22, 1 << 23, None, (1 << 24) + 2,
+                                    None) == ews.MOE_EINVAL
+

@@ -370,6 +370,21 @@ __device__ __forceinline__ uint4 tag_load2(const uint64_t *base, int i)
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Byte offset past the num_records (0x7FFFFFFF) of the tag buffers' resource
+// for every dword of a load issued there: such a buffer load is out of
+// range, returns zeros and makes no memory access.
+constexpr uint32_t kNoAccess = 0x80000000u;
+
+// tag_load2 for a lane that still needs the words; a lane that has them
+// already issues an out-of-range buffer load (no memory access, zeros).
+__device__ __forceinline__ uint4 tag_load2_if(const uint64_t *base, int i, bool need)
+{
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(base), (short)0, 0x7FFFFFFF,
+                                                                 0x00020000);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, need ? (uint32_t)i * 8u : kNoAccess, 0, 16 /* sc1: agent scope */);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // One wave: dot of router row `row` (D fp32) with x; x may live in LDS.
 // Returns the full sum in every lane.  Rows of up to 4096 are fetched with
 // every load in flight before the first FMA.

@@ -11,8 +11,11 @@
 // applied, h kept in LDS), then h's digit table, then the down rows; so h
 // never leaves the chip and every byte of the range's blobs is read once.
 // Inside an expert, wave w takes row units w, w + 8, ..., so that the eight
-// waves read neighbouring rows at any time, and each wave has the next unit's
-// loads in flight while it computes the current one.
+// waves read neighbouring rows at any time.  A wave holds one unit (one
+// gate/up row pair, or 8 to 16 down rows) at a time, so that the kernel fits
+// 128 registers and four waves run per SIMD: while one computes, the loads
+// of the others are in flight (measured faster than two units in flight per
+// wave at two waves per SIMD).
 #include "moe_device.h"
 
 namespace moe {
@@ -63,11 +66,80 @@ __device__ __forceinline__ void digit_table(const float *v, int n, int *dig, flo
     }
 }
 
-template <int BITS, int GCPL, int R, int LPR, int DCPL>
-__global__ void __launch_bounds__(NT) k_expert_gemv(GemvArgs a)
+// S down row groups of one wave unit (RPU = 64/LPR rows each, rows o0 +
+// s*RPU + lane/LPR), loaded together.
+template <int BITS, int DCPL, int S>
+struct DnUnit {
+    DnRegs<BITS, DCPL> d[S];
+};
+
+template <int BITS, int LPR, int DCPL, int S>
+__device__ __forceinline__ void dn_unit_load(DnUnit<BITS, DCPL, S> &u, const uint8_t *blob, int D, int I, int o0,
+                                             int lane)
+{
+    constexpr int RPU = 64 / LPR;
+#pragma unroll
+    for (int s = 0; s < S; ++s) dn_load<BITS, LPR, DCPL>(u.d[s], blob, D, I, o0 + s * RPU, lane);
+}
+
+// The unit's rows against h's digit table (LDS), each chunk's digits read
+// once for all S groups; row sums in rows o0 + s*RPU + lane/LPR.
+template <int BITS, int LPR, int DCPL, int S>
+__device__ __forceinline__ void dn_unit_finish(const DnUnit<BITS, DCPL, S> &u, const int *hdig, const float *hcsum,
+                                               const float *hcinv, int I, int D, int o0, int lane, float *yn)
 {
     using C = Codes<BITS>;
-    constexpr int RPU = 64 / LPR;  // down rows per wave unit
+    constexpr int RPU = 64 / LPR;
+    const int nchunks = I * BITS / 128;
+    const int lc = lane % LPR;
+    float t[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) t[s] = 0.f;
+#pragma unroll
+    for (int m = 0; m < DCPL; ++m) {
+        const int c = lc + LPR * m;
+        if (c < nchunks) {
+            int dg[C::DW];
+            const int4 *src = reinterpret_cast<const int4 *>(hdig + c * C::DW);
+#pragma unroll
+            for (int t4 = 0; t4 < C::DW / 4; ++t4) {
+                const int4 v = src[t4];
+                dg[4 * t4] = v.x;
+                dg[4 * t4 + 1] = v.y;
+                dg[4 * t4 + 2] = v.z;
+                dg[4 * t4 + 3] = v.w;
+            }
+            const float cs = hcsum[c], ci = hcinv[c];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const float qh = qdot<BITS>(u.d[s].q[m], dg);
+                t[s] = fmaf(bf16_lo(u.d[s].sb[m]) * ci, qh, t[s]);
+                t[s] = fmaf(bf16_hi(u.d[s].sb[m]), cs, t[s]);
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float r = group_sum<LPR>(t[s]);
+        const int o = o0 + s * RPU + lane / LPR;
+        if (lane % LPR == 0 && o < D) yn[o] = r;
+    }
+}
+
+// Waves per SIMD the compiler must leave room for: four (at most 128
+// registers), or one for gate/up rows of more than 2 KB, whose registers do
+// not fit that.
+template <int BITS, int GCPL>
+constexpr int gemv_waves() { return GCPL >= 4 || (BITS == 2 && GCPL >= 2) ? 1 : 4; }
+
+template <int BITS, int GCPL, int R, int LPR, int DCPL>
+__global__ void __launch_bounds__(NT, (gemv_waves<BITS, GCPL>())) k_expert_gemv(GemvArgs a)
+{
+    constexpr int RPU = 64 / LPR;  // down rows per row group
+    // row groups per down unit: up to 16 rows, at most 4 chunks per lane
+    constexpr int S0 = 16 / RPU > 0 ? 16 / RPU : 1;
+    constexpr int S = S0 * DCPL > 4 ? 4 / DCPL : S0;
+    constexpr int RPD = RPU * S;   // rows per down unit
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -85,56 +157,38 @@ __global__ void __launch_bounds__(NT) k_expert_gemv(GemvArgs a)
     lds_barrier();
 
     const int ngu = (I + R - 1) / R;          // gate/up units of an expert
-    const int ndn = (D + RPU - 1) / RPU;      // down units
+    const int ndn = (D + RPD - 1) / RPD;      // down units
     for (int n = blockIdx.x; n < a.count; n += gridDim.x) {
         const uint8_t *blob = a.experts + (uint64_t)(a.first + n) * a.blob_bytes;
         float *hn = a.h + (size_t)n * I;
         float *yn = a.y + (size_t)n * D;
-        // gate/up rows, two units in flight per wave
-        {
-            GuRegs<BITS, GCPL, R> g0, g1;
-            auto finish = [&](const GuRegs<BITS, GCPL, R> &g, int u) {
-                float hv[R];
-                gu_finish_c<BITS, GCPL, R>(g, dig, csum, cinv, D, lane, hv);
-                if (lane == 0) {
+        // gate/up rows
+        for (int u = wave; u < ngu; u += NW) {
+            GuRegs<BITS, GCPL, R> g;
+            gu_load<BITS, GCPL, R>(g, blob, D, I, u * R, lane);
+            float hv[R];
+            gu_finish_c<BITS, GCPL, R>(g, dig, csum, cinv, D, lane, hv);
+            if (lane == 0) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const int i = u * R + r;
-                        if (i < I) {
-                            hs[i] = hv[r];
-                            hn[i] = hv[r];
-                        }
+                for (int r = 0; r < R; ++r) {
+                    const int i = u * R + r;
+                    if (i < I) {
+                        hs[i] = hv[r];
+                        hn[i] = hv[r];
                     }
                 }
-            };
-            int u = wave;
-            if (u < ngu) gu_load<BITS, GCPL, R>(g0, blob, D, I, u * R, lane);
-            for (; u < ngu; u += 2 * NW) {
-                if (u + NW < ngu) gu_load<BITS, GCPL, R>(g1, blob, D, I, (u + NW) * R, lane);
-                finish(g0, u);
-                if (u + 2 * NW < ngu) gu_load<BITS, GCPL, R>(g0, blob, D, I, (u + 2 * NW) * R, lane);
-                if (u + NW < ngu) finish(g1, u + NW);
             }
         }
         // the first down unit is requested before h is complete
-        DnRegs<BITS, DCPL> d0, d1;
-        int u = wave;
-        if (u < ndn) dn_load<BITS, LPR, DCPL>(d0, blob, D, I, u * RPU, lane);
+        DnUnit<BITS, DCPL, S> d;
+        if (wave < ndn) dn_unit_load<BITS, LPR, DCPL, S>(d, blob, D, I, wave * RPD, lane);
         lds_barrier();
         digit_table<BITS>(hs, I, hdig, hcsum, hcinv);
         lds_barrier();
-        auto finish_dn = [&](const DnRegs<BITS, DCPL> &d, int uu) {
-            const float t = group_sum<LPR>(dn_part_c<BITS, LPR, DCPL>(d, hdig, hcsum, hcinv, I, lane));
-            const int o = uu * RPU + lane / LPR;
-            if (lane % LPR == 0 && o < D) yn[o] = t;
-        };
-        for (; u < ndn; u += 2 * NW) {
-            if (u + NW < ndn) dn_load<BITS, LPR, DCPL>(d1, blob, D, I, (u + NW) * RPU, lane);
-            finish_dn(d0, u);
-            if (u + 2 * NW < ndn) dn_load<BITS, LPR, DCPL>(d0, blob, D, I, (u + 2 * NW) * RPU, lane);
-            if (u + NW < ndn) finish_dn(d1, u + NW);
+        for (int u = wave; u < ndn; u += NW) {
+            if (u > wave) dn_unit_load<BITS, LPR, DCPL, S>(d, blob, D, I, u * RPD, lane);
+            dn_unit_finish<BITS, LPR, DCPL, S>(d, hdig, hcsum, hcinv, I, D, u * RPD, lane, yn);
         }
-        (void)C::CODES;
     }
 }
 
@@ -209,7 +263,7 @@ hipError_t gemv_bits(const GemvArgs &a, hipStream_t s, LayerPlan *p)
 {
     const int nch = a.D * BITS / 128;  // 16-byte chunks of a gate/up row
     if (nch <= 64) return gemv_dn<BITS, 1, 2>(a, s, p);
-    if (nch <= 128) return gemv_dn<BITS, 2, 2>(a, s, p);
+    if (nch <= 128) return gemv_dn<BITS, 2, 1>(a, s, p);
     if constexpr (BITS == 4) return gemv_dn<BITS, 4, 1>(a, s, p);
     return hipErrorNotSupported;
 }

@@ -149,30 +149,44 @@ template <int NV>
 __device__ __forceinline__ float poll_residual(KArgs A, int q0, int D, int NB, uint32_t tag, bool with_ss, float4 (&rv)[NV])
 {
     const int tid = threadIdx.x, lane = tid & 63;
-    float t = 0.f;
+    constexpr int SI = kMaxLayerBlocks / 256;
+    uint4 sa[SI], sc[SI], ra[NV], rc[NV];
+    bool ns[SI], nr[NV];
+#pragma unroll
+    for (int i = 0; i < SI; ++i) {
+        ns[i] = with_ss && 256 * i + 4 * lane < NB;
+        sa[i] = sc[i] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        nr[j] = q0 + tid + j * NT < D / 4;
+        ra[j] = rc[j] = make_uint4(0, 0, 0, 0);
+    }
     for (uint32_t spins = 0;;) {
         bool ok = true;
-        t = 0.f;
-        if (with_ss) {
-            for (int i = 0; 256 * i < NB; ++i) {
-                const int p = 256 * i + 4 * lane;
-                const uint4 a = tag_load2(A->tss, p), c = tag_load2(A->tss, p + 2);
-                ok &= (p >= NB || a.y == tag) && (p + 1 >= NB || a.w == tag) && (p + 2 >= NB || c.y == tag) &&
-                      (p + 3 >= NB || c.w == tag);
-                t += p < NB ? __uint_as_float(a.x) : 0.f;
-                t += p + 1 < NB ? __uint_as_float(a.z) : 0.f;
-                t += p + 2 < NB ? __uint_as_float(c.x) : 0.f;
-                t += p + 3 < NB ? __uint_as_float(c.z) : 0.f;
+#pragma unroll
+        for (int i = 0; i < SI; ++i) {
+            const int p = 256 * i + 4 * lane;
+            const uint4 a = tag_load2_if(A->tss, p, ns[i]), c = tag_load2_if(A->tss, p + 2, ns[i]);
+            const bool g = (p >= NB || a.y == tag) && (p + 1 >= NB || a.w == tag) && (p + 2 >= NB || c.y == tag) &&
+                           (p + 3 >= NB || c.w == tag);
+            if (ns[i]) {
+                sa[i] = a;
+                sc[i] = c;
+                ok &= g;
+                ns[i] = !g;
             }
         }
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int q = q0 + tid + j * NT;
-            rv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (q < D / 4) {
-                const uint4 a = tag_load2(A->tres, 4 * q), c = tag_load2(A->tres, 4 * q + 2);
-                ok &= a.y == tag && a.w == tag && c.y == tag && c.w == tag;
-                rv[j] = make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(c.x), __uint_as_float(c.z));
+            const uint4 a = tag_load2_if(A->tres, 4 * q, nr[j]), c = tag_load2_if(A->tres, 4 * q + 2, nr[j]);
+            const bool g = a.y == tag && a.w == tag && c.y == tag && c.w == tag;
+            if (nr[j]) {
+                ra[j] = a;
+                rc[j] = c;
+                ok &= g;
+                nr[j] = !g;
             }
         }
         if (__all(ok)) break;
@@ -182,7 +196,22 @@ __device__ __forceinline__ float poll_residual(KArgs A, int q0, int D, int NB, u
             break;
         }
     }
-    return t;
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < SI; ++i) {
+        const int p = 256 * i + 4 * lane;
+        if (256 * i < NB) {
+            t += p < NB ? __uint_as_float(sa[i].x) : 0.f;
+            t += p + 1 < NB ? __uint_as_float(sa[i].z) : 0.f;
+            t += p + 2 < NB ? __uint_as_float(sc[i].x) : 0.f;
+            t += p + 3 < NB ? __uint_as_float(sc[i].z) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        rv[j] = make_float4(__uint_as_float(ra[j].x), __uint_as_float(ra[j].z), __uint_as_float(rc[j].x),
+                            __uint_as_float(rc[j].z));
+    return with_ss ? t : 0.f;
 }
 
 template <int BITS, int GCPL, int RX, int LPR, int DCPL, int MAXS, bool TBL>
@@ -377,17 +406,24 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             const int n4 = S * I / 4;
             for (int q0 = 0; q0 < n4; q0 += NT * HV) {
                 float4 hv[HV];
+                bool nh[HV];
+#pragma unroll
+                for (int j = 0; j < HV; ++j) {
+                    nh[j] = q0 + tid + j * NT < n4;
+                    hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
                 for (uint32_t spins = 0;;) {
                     bool ok = true;
 #pragma unroll
                     for (int j = 0; j < HV; ++j) {
                         const int q = q0 + tid + j * NT;
-                        hv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-                        if (q < n4) {
-                            const uint4 a = tag_load2(A->th, 4 * q), c = tag_load2(A->th, 4 * q + 2);
-                            ok &= a.y == t_h && a.w == t_h && c.y == t_h && c.w == t_h;
+                        const uint4 a = tag_load2_if(A->th, 4 * q, nh[j]), c = tag_load2_if(A->th, 4 * q + 2, nh[j]);
+                        const bool g = a.y == t_h && a.w == t_h && c.y == t_h && c.w == t_h;
+                        if (nh[j]) {
                             hv[j] = make_float4(__uint_as_float(a.x), __uint_as_float(a.z), __uint_as_float(c.x),
                                                 __uint_as_float(c.z));
+                            ok &= g;
+                            nh[j] = !g;
                         }
                     }
                     if (__all(ok)) break;

@@ -521,7 +521,7 @@ def streamed_bench(cfg, resident, out0, v0, tokens, warmup, arena_gb):
             "expert_cache": cache_out}
 
 
-def gemv_bench(st, cfg, calls=20, warmup=3):
+def gemv_bench(st, cfg, calls=20, warmup=10):
     """moe_expert_gemv over all E experts of one layer per call: one launch,
     each workgroup streaming whole experts (gate/up, SwiGLU, then down from h
     kept on chip), so every byte of the layer's E blobs (3.6 GB at 4-bit) is

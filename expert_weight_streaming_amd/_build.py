@@ -27,21 +27,25 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(force: bool = False, extra=None, jobs: int = 8) -> str:
-    if not force and os.path.exists(SO):
-        return SO
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(force: bool = False, extra=None, jobs: int = 8, out: str = SO) -> str:
+    """Compile every unit and link `out` (default: the library itself;
+    another path with extra defines gives a variant, such as the timeline
+    build)."""
+    if not force and os.path.exists(out):
+        return out
+    obj_dir = OBJ_DIR if out == SO else os.path.join(OBJ_DIR, os.path.splitext(os.path.basename(out))[0])
+    os.makedirs(obj_dir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
     def compile_unit(unit):
         src, defs, obj = unit
-        out = os.path.join(OBJ_DIR, obj)
+        o = os.path.join(obj_dir, obj)
         subprocess.check_call(["hipcc", *HIPCC_FLAGS, *inc, *defs, *(extra or []), "-c",
-                               os.path.join(HERE, "csrc", src), "-o", out])
-        return out
+                               os.path.join(HERE, "csrc", src), "-o", o])
+        return o
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_unit, UNITS))
-    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", SO + ".tmp"])
-    os.replace(SO + ".tmp", SO)
-    return SO
+    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"])
+    os.replace(out + ".tmp", out)
+    return out

@@ -17,6 +17,10 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Timeline builds (-DMOE_STACK_PROBE): where the stack kernel stores its
+// stamps (moe_probe_set); always NULL otherwise.
+uint64_t *g_probe = nullptr;
+
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char *fmt, ...)
 {
@@ -278,6 +282,7 @@ int enqueue_stack(const moe_layer_desc *ds, int32_t n, float *resid, float *x, i
         a.th = reinterpret_cast<uint64_t *>(ws + L.th);
         a.tres = reinterpret_cast<uint64_t *>(ws + L.tres);
         a.tss = reinterpret_cast<uint64_t *>(ws + L.tss);
+        a.probe = g_probe;
         a.hdr = reinterpret_cast<uint32_t *>(ws + L.hdr);
         a.slots = reinterpret_cast<uint32_t *>(ws + L.slots);
         a.flags = flags ? flags : reinterpret_cast<uint32_t *>(ws + L.flags);
@@ -902,6 +907,17 @@ int moe_stream_token(const moe_layer_desc *layers, int32_t n_layers, const moe_s
     }
     return rec(n_layers);
 }
+
+#ifdef MOE_STACK_PROBE
+// Timeline builds only (not part of the C ABI of moe.h): the device buffer
+// of [n_layers][grid][8][kProbePoints] uint64 stamps that the next stack
+// launches fill, or NULL.
+int moe_probe_set(void *buf)
+{
+    g_probe = static_cast<uint64_t *>(buf);
+    return MOE_OK;
+}
+#endif
 
 int moe_host_alloc(size_t bytes, void **out)
 {

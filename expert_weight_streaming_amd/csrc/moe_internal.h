@@ -181,6 +181,7 @@ struct LayerPlan {
 
 // One launch for a whole stack of layers (batch 1), moe_stack.hip.
 constexpr int kMaxStackLayers = 64;
+constexpr int kProbePoints = 16;  // stamps per layer and wave in timeline builds
 constexpr int kStackThreads = 512;
 
 struct StackLayer {
@@ -203,6 +204,8 @@ struct StackArgs {
     uint64_t *th;            // workspace [slots][I]: (h, epoch)
     uint64_t *tres;          // workspace [D]: (residual, epoch)
     uint64_t *tss;           // workspace [kMaxLayerBlocks]: (partial sum of squares, epoch)
+    uint64_t *probe;         // timeline builds (MOE_STACK_PROBE): [n_layers][grid][8 waves][kProbePoints]
+                             // s_memrealtime stamps, or NULL; unused otherwise
     uint32_t *hdr;           // workspace: grid of the last persistent launch (0: none yet)
     uint32_t *slots;         // workspace: per-block epoch reached by the last launch
     uint32_t *flags;
@@ -213,14 +216,16 @@ struct StackArgs {
 
 // Dynamic LDS of the stack kernel (byte offsets, 16-byte aligned).
 struct StackLds {
-    uint32_t xs, rs, dig, csum, xcinv, u, hdig, hcsum, hcinv, misc, total;
+    uint32_t xs, rs, dig, csum, xcinv, u, hdig, hcsum, hcinv, yh, misc, total;
 };
 constexpr int kStackMiscWords = 256;
 // LDS of the stack kernel: x (fp32) and r of the layer, x's digit table
 // with per-chunk sums and steps, a region shared by the router partials
 // (phase A: one per wave and round of router rows) and the combined rows
 // (phase C), h's digit tables with their per-chunk
-// sums and steps, and small scalars (selection, weights, ready flags).
+// sums and steps, the slot partials that helper waves hand to their
+// partners in the down phase, and small scalars (selection, weights, ready
+// flags).
 __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bits)
 {
     const uint32_t codes = 128 / bits, dw = 4 * (8 / bits) * 3;
@@ -241,6 +246,7 @@ __host__ __device__ inline StackLds stack_lds(int D, int E, int I, int S, int bi
     take(l.hdig, hc * dw * 4);
     take(l.hcsum, hc * 4);
     take(l.hcinv, hc * 4);
+    take(l.yh, 4u * 4u * 64u * 4u);  // helper waves' slot partials: [4 waves][4 slots][64 lanes]
     take(l.misc, kStackMiscWords * 4);
     l.total = o;
     return l;

@@ -62,6 +62,20 @@ constexpr int HV = 3;              // h float4 per thread and round
 constexpr int KPL = 8;             // top-K keys per lane: E <= 512
 constexpr uint32_t kTagSpins = 1u << 16;  // polls of an exchange before it is given up (error flag)
 
+// Timeline builds (-DMOE_STACK_PROBE): lane 0 of every wave stores the
+// device's constant-rate clock (s_memrealtime) at fixed points of each
+// layer into args.probe; other builds compile the points away.
+#ifdef MOE_STACK_PROBE
+#define MOE_PROBE(P)                                                                                                   \
+    do {                                                                                                               \
+        if (A->probe && (threadIdx.x & 63) == 0)                                                                       \
+            A->probe[(((size_t)l * gridDim.x + blockIdx.x) * NWB + (threadIdx.x >> 6)) * kProbePoints + (P)] =         \
+                __builtin_amdgcn_s_memrealtime();                                                                      \
+    } while (0)
+#else
+#define MOE_PROBE(P) ((void)0)
+#endif
+
 // Values that the compiler must not keep live across the layer loop: a
 // persistent kernel's loop body would otherwise have every lane-dependent
 // address of every phase hoisted out of it, all live at once.
@@ -96,7 +110,7 @@ __device__ __forceinline__ StackLayer layer_of(KArgs A, int l)
 
 // Per-layer LDS views.
 struct Views {
-    float *xs, *rs, *csum, *xcinv, *u, *hcsum, *hcinv, *misc;
+    float *xs, *rs, *csum, *xcinv, *u, *hcsum, *hcinv, *yh, *misc;
     int *dig, *hdig;
 };
 template <int BITS>
@@ -113,6 +127,7 @@ __device__ __forceinline__ Views views(unsigned char *smem, int D, int E, int I,
     v.hdig = reinterpret_cast<int *>(smem + lo.hdig);
     v.hcsum = reinterpret_cast<float *>(smem + lo.hcsum);
     v.hcinv = reinterpret_cast<float *>(smem + lo.hcinv);
+    v.yh = reinterpret_cast<float *>(smem + lo.yh);
     v.misc = reinterpret_cast<float *>(smem + lo.misc);
     return v;
 }
@@ -274,6 +289,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
         const int cpk = I / C::CODES;                 // h chunks per slot
         const int nd = (D + RPU - 1) / RPU;           // down units
         const uint32_t t_log = base + 3u * l + 1u, t_h = t_log + 1u, t_res = t_log + 2u;
+        MOE_PROBE(0);
 
         // ---- phase A: x_l, r_l and x_l's digit table
         {
@@ -297,6 +313,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                     // the residual rows and sums of squares of layer l-1
                     const float t = poll_residual<XV>(A, q0, D, NB, t_res - 3u, q0 == 0, rv);
                     if (q0 == 0) inv = 1.f / sqrtf(group_sum<64>(t) / (float)D + A->eps);
+                    if (q0 == 0) MOE_PROBE(1);
                 }
 #pragma unroll
                 for (int j = 0; j < XV; ++j) {
@@ -318,6 +335,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 }
             }
         }
+        MOE_PROBE(2);
         lds_barrier();
 
         // router rows: RSL waves per row, RPB rows per block and round, the
@@ -333,6 +351,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 if (lane == 0) v.u[j * NWB + wave] = acc;
             }
         }
+        MOE_PROBE(3);
         lds_barrier();
         for (int t = tid; t < nr * RPB; t += NT) {
             const int j = t / RPB, rr = t - j * RPB;
@@ -344,6 +363,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 tag_store(A->tlog + e, s, t_log);
             }
         }
+        MOE_PROBE(4);
 
         // ---- phase B: wave 0 polls the logits and takes the top-K, each
         // selected index published as soon as it is known; waves 1.. run the
@@ -361,7 +381,11 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 __builtin_amdgcn_wave_barrier();
                 if (lane < K) __hip_atomic_store(rdy + lane, l + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             } else {
+                // the top-K is on every layer's critical path: its wave goes
+                // ahead of the shared gate/up wave on the same SIMD
+                __builtin_amdgcn_s_setprio(3);
                 wave_topk_global<KPL>(A->tlog, t_log, E, K, sel, selw, rdy, l + 1, lane, A->flags);
+                __builtin_amdgcn_s_setprio(0);
                 if (b == 0 && lane < K) {
                     A->topk_idx[l * K + lane] = sel[lane];
                     A->topk_w[l * K + lane] = selw[lane];
@@ -375,6 +399,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 if (lane == 0) tag_store(A->th + (size_t)K * I + u, hv[0], t_h);
             }
         }
+        MOE_PROBE(5);
         {
             const int upe = (I + RX - 1) / RX;
             for (int u = gw; u < K * upe; u += GW) {
@@ -391,13 +416,32 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 }
             }
         }
+        MOE_PROBE(6);
+        // Down units: when at most half the waves have one (wide row units),
+        // wave w and its helper w + NWB/2 share a unit: the partner takes
+        // slots [0, ka), the helper slots [ka, S) and hands its per-lane slot
+        // partials over through LDS, so the partner's slot-order combine is
+        // the same arithmetic as one wave's.
+        static_assert(NWB == 8 && kMaxSlots - (kMaxSlots + 1) / 2 <= 4, "helper partials are [4 waves][4 slots]");
+        // (only units of four or more rows, LPR <= 16, have the split: with
+        // one- and two-row units the plain path measured faster or the
+        // registers did not allow it)
+        constexpr bool kSplit = LPR <= 16;
+        const bool split = kSplit && 2 * nd <= GW;
+        const int half = NWB / 2;
+        const bool helper = split && wave >= half;
+        const int ud = split ? (wave % half) * NB + b : gw;  // this wave's (first) down unit
+        const int ka = (S + 1) / 2;
+        const int k_lo = helper ? ka : 0, k_hi = split && !helper ? ka : S;
         // the down rows of every slot (first round): they stream while the
         // other blocks finish their gate/up rows
         DnRegs<BITS, DCPL> dn[MAXS];
         if (TBL ? !Ly.slab : Ly.experts != nullptr) wait_selected(rdy, K - 1, l + 1, A->flags);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k)
-            dn_load<BITS, LPR, DCPL>(dn[k], (k < S && gw < nd) ? slot_blob<TBL>(A, Ly, sel, k) : nullptr, D, I, gw * RPU, lane);
+            dn_load<BITS, LPR, DCPL>(dn[k], (k >= k_lo && k < k_hi && ud < nd) ? slot_blob<TBL>(A, Ly, sel, k) : nullptr, D,
+                                     I, ud * RPU, lane);
+        MOE_PROBE(7);
 
         // ---- phase C: h of every slot (polled until all of it carries this
         // layer's epoch) as digit tables; then the next layer's router and
@@ -441,8 +485,34 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
                 }
             }
         }
+        MOE_PROBE(8);
         lds_barrier();
+        MOE_PROBE(9);
         // down rows of all slots, combined in slot order into LDS
+        if (kSplit && split) {
+            // the partner's chain over its own slots, the helper's partials
+            // to LDS; then the partner continues the chain with them
+            float c = 0.f;
+#pragma unroll
+            for (int k = 0; k < MAXS; ++k) {
+                if (k < k_lo || k >= k_hi || ud >= nd) continue;
+                const float y = dn_part_c<BITS, LPR, DCPL>(dn[k], v.hdig + k * cpk * C::DW, v.hcsum + k * cpk,
+                                                           v.hcinv + k * cpk, I, lane);
+                if (helper)
+                    v.yh[((wave - half) * 4 + (k - ka)) * 64 + lane] = y;
+                else
+                    c = fmaf(k < K ? selw[k] : 1.f, y, c);
+            }
+            lds_barrier();
+            if (!helper && ud < nd) {
+                const int o = ud * RPU + lane / LPR;
+#pragma unroll
+                for (int k = 0; k < MAXS; ++k)
+                    if (k >= ka && k < S) c = fmaf(k < K ? selw[k] : 1.f, v.yh[(wave * 4 + (k - ka)) * 64 + lane], c);
+                c = group_sum<LPR>(c);
+                if (lane % LPR == 0 && o < D) v.u[o] = c;
+            }
+        } else
         for (int u = gw, j = 0; u < nd; u += GW, ++j) {
             const int o0 = u * RPU, o = o0 + lane / LPR;
             if (j > 0) {
@@ -463,6 +533,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             c = group_sum<LPR>(c);
             if (lane % LPR == 0 && o < D) v.u[o] = c;
         }
+        MOE_PROBE(10);
         lds_barrier();
         // the block's rows (units b + NB*m): r' = r + c, published tagged with
         // the block's sum of squares
@@ -482,6 +553,7 @@ __global__ void __launch_bounds__(NT) k_stack(StackArgs args)
             ssacc = group_sum<64>(ssacc);
             if (lane == 0) tag_store(A->tss + b, ssacc, t_res);
         }
+        MOE_PROBE(11);
         // the block's LDS is rewritten by the next layer
         lds_barrier();
     }

@@ -120,6 +120,23 @@ def summarize(cfg, plan, stamps, ms, skip=2):
         wo = np.median(rel[:, :, 1:, p])
         bmax = rel[:, :, :, p].max(axis=2)
         lines.append(f"| {p}. {label} | {w0:.2f} | {wo:.2f} | {np.median(bmax):.2f} / {np.median(bmax.max(axis=1)):.2f} |")
+    # which workgroups are late: per point, each block's slowest wave against
+    # the median block of the same layer, averaged over layers; by
+    # workgroup id modulo 8 (the dispatcher's round-robin over the XCDs) and
+    # the agreement of the per-block means between two halves of the samples
+    G = rel.shape[1]
+    lines += ["", "Late workgroups: per point, a block's slowest wave minus the median block of the same layer "
+              "(us, mean over layers), by workgroup id mod 8; r: correlation of the per-block means between "
+              "two halves of the layers (near 1: the same blocks are late every layer).", "",
+              "| point | slowest block, median over layers | " + " | ".join(f"id%8={x}" for x in range(8)) + " | r |",
+              "|---|---:|" + "---:|" * 8 + "---:|"]
+    for p in LABELS:
+        bmax = rel[:, :, :, p].max(axis=2)
+        late = bmax - np.median(bmax, axis=1, keepdims=True)
+        mean_late = late.mean(axis=0)
+        by = [mean_late[np.arange(G) % 8 == x].mean() for x in range(8)]
+        r = np.corrcoef(late[::2].mean(axis=0), late[1::2].mean(axis=0))[0, 1]
+        lines.append(f"| {p} | {np.median(late.max(axis=1)):.2f} | " + " | ".join(f"{v:+.2f}" for v in by) + f" | {r:.2f} |")
     return lines
 
 

@@ -203,6 +203,26 @@ __global__ void __launch_bounds__(256) k_topk_b(BatchArgs a, int splits)
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
+    if (E <= 64 * 8) {
+        // the one-token kernels' selection on 32-bit order keys (same
+        // order, ties and weights as below, fewer instructions per round)
+        __shared__ int s_sel[4][kMaxTopK], s_rdy[4][kMaxTopK];
+        __shared__ float s_w[4][kMaxTopK];
+        uint32_t ord[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = lane + 64 * u;
+            ord[u] = e < E ? order_key(__float_as_uint(lg[wave][e])) : 0u;
+        }
+        topk_select<8>(ord, K, s_sel[wave], s_w[wave], s_rdy[wave], 1, lane);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        if (lane < K) {
+            a.topk_idx[(size_t)t * K + lane] = s_sel[wave][lane];
+            a.topk_w[(size_t)t * K + lane] = s_w[wave][lane];
+        }
+        return;
+    }
     uint64_t taken = 0;  // bit j: element lane + 64 j selected
     int idx[kMaxTopK];
     float vals[kMaxTopK], w[kMaxTopK];
@@ -388,7 +408,11 @@ __device__ __forceinline__ int token_of(const BatchArgs &a, const Item &it, int 
 
 // ---------------------------------------------------------------------------
 // Per token: combine in slot order (routed k = 0..K-1, then shared), then
-// (mode 1) residual + RMSNorm; one block per token.
+// (mode 1) residual + RMSNorm; one block per token.  PER rows per thread
+// (D <= 1024 PER), up to NS slots: every slot's rows, the residual rows and
+// gamma are requested before the first sum, so that the block waits for one
+// round trip instead of one per slot.
+template <int PER, int NS>
 __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
 {
     const int t = blockIdx.x, tid = threadIdx.x;
@@ -402,30 +426,40 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
     }
     __syncthreads();
     const bool has_shared = a.src.n_slots > K;
-    constexpr int PER = 8;  // D <= 8192
-    float rv[PER];
-    float ss = 0.f;
-    // the combine of the token's rows first (the outputs never alias y),
-    // summed in slot order, then residual and norm; each slot's rows are
-    // loaded together
+    float yv[NS][PER], rr[PER], gg[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) rv[j] = 0.f;
-    for (int k = 0; k <= K; ++k) {
-        const int pk = k < K ? pos[k] : (has_shared ? a.T * K + t : -1);
-        if (pk < 0) continue;
-        float yv[PER];
+    for (int k = 0; k < NS; ++k) {
+        const int pk = k < K ? pos[k] : (k == K && has_shared ? a.T * K + t : -1);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int o = tid + 1024 * j;
-            yv[j] = o < D ? a.y[(size_t)pk * D + o] : 0.f;
+            yv[k][j] = k <= K && pk >= 0 && o < D ? a.y[(size_t)pk * D + o] : 0.f;
         }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int o = tid + 1024 * j;
+        rr[j] = a.mode != 0 && o < D ? a.resid[(size_t)t * D + o] : 0.f;
+        gg[j] = a.mode != 0 && o < D ? a.gamma[o] : 0.f;
+    }
+    float rv[PER];
+    float ss = 0.f;
+    // the combine of the token's rows first (the outputs never alias y),
+    // summed in slot order, then residual and norm
+#pragma unroll
+    for (int j = 0; j < PER; ++j) rv[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        if (k > K) continue;
+        const int pk = k < K ? pos[k] : (has_shared ? a.T * K + t : -1);
+        if (pk < 0) continue;
         if (k < K) {
             const float wk = wts[k];
 #pragma unroll
-            for (int j = 0; j < PER; ++j) rv[j] += wk * yv[j];
+            for (int j = 0; j < PER; ++j) rv[j] += wk * yv[k][j];
         } else {
 #pragma unroll
-            for (int j = 0; j < PER; ++j) rv[j] += yv[j];
+            for (int j = 0; j < PER; ++j) rv[j] += yv[k][j];
         }
     }
 #pragma unroll
@@ -435,7 +469,7 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
         if (a.mode == 0) {
             a.yout[(size_t)t * D + o] = rv[j];
         } else {
-            const float r = a.resid[(size_t)t * D + o] + rv[j];
+            const float r = rr[j] + rv[j];
             rv[j] = r;
             ss += r * r;
         }
@@ -456,7 +490,7 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int o = tid + 1024 * j;
-        if (o < D) a.xout[(size_t)t * D + o] = rv[j] * inv * a.gamma[o];
+        if (o < D) a.xout[(size_t)t * D + o] = rv[j] * inv * gg[j];
     }
 }
 
@@ -823,7 +857,14 @@ hipError_t launch_batch_experts(const BatchArgs &a, int bits, hipStream_t s)
         hipError_t e = bits == 4 ? batch_bits<4>(a, stage, s) : batch_bits<2>(a, stage, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_combine_b, dim3(a.T), dim3(1024), 0, s, a);
+    // rows per thread and slots of the combine
+    const int ns = a.K + (a.src.n_slots > a.K ? 1 : 0);
+    if (a.D <= 4096 && ns <= 5)
+        hipLaunchKernelGGL((k_combine_b<4, 5>), dim3(a.T), dim3(1024), 0, s, a);
+    else if (a.D <= 4096)
+        hipLaunchKernelGGL((k_combine_b<4, kMaxSlots>), dim3(a.T), dim3(1024), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_combine_b<8, kMaxSlots>), dim3(a.T), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 

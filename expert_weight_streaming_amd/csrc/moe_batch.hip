@@ -25,6 +25,8 @@
 //                  shared expert's y, then (layer mode) residual + RMSNorm
 //
 // Every step is deterministic (no float atomics, fixed summation orders).
+#include <type_traits>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -507,15 +509,23 @@ __global__ void __launch_bounds__(1024) k_combine_b(BatchArgs a)
 // stage's codes, scale words, digit words, group sums and steps with
 // coalesced 16-byte loads into registers while it computes the previous
 // stage from LDS.  One v_mfma_i32_16x16x64_i8 per (plane, matrix, scale group) takes
-// the vectors' digit words of the plane as A (vector l % 16, K-slice l / 16)
-// and the group's masked codes as B (row l % 16), so C arrives as vectors
-// 4 (l / 16) + r, row l % 16 and a lane needs only its own row's scale and
-// bias word.  The three plane sums are exact int32; the group's bf16 scale
-// times the vector's step 2^-k for the group multiplies their fp32
-// combination, and the group's bias the vector's sum over the group.
+// the vectors' digit words of the plane as A (A-row l % 16, K-slice l / 16)
+// and the group's masked codes as B (row l % 16), so a lane's C values are
+// its own row's and it needs only that row's scale and bias word.  Vector
+// slot t sits at A-row 4 (t % 4) + t / 4, so lane group l / 16 holds vectors
+// l / 16 + 4 r: a tile of n vectors uses r < ceil(n / 4) only, and the
+// epilogue, compiled for each such count, skips the rest.  The three plane
+// sums are exact int32; the group's bf16 scale times the vector's step 2^-k
+// for the group multiplies their fp32 combination, and the group's bias the
+// vector's sum over the group.
 // MODE 0 leaves h as digit words (a unit's 64 rows are one scale group of
 // h), so the down rows read them as the gate/up rows read x's.
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+// The MFMA A-row (and so C row) of a tile's vector slot t: 4 (t % 4) + t / 4.
+// C row 4 h + r of lane group h is vector h + 4 r, so the first n vectors of
+// a tile occupy the first ceil(n / 4) of a lane's four outputs.
+__device__ __forceinline__ int arow(int t) { return 4 * (t & 3) + (t >> 2); }
 
 template <int BITS, int SG>
 struct MmShape {
@@ -607,6 +617,10 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
         const int wk = a.mwork[u / rgroups];
         const Item it = item_of(a, wk >> 2, nact);
         const int j0 = (wk & 3) * 16, row0 = (u % rgroups) * UR;
+        // C rows 4 h + r hold vectors h + 4 r: a tile of n vectors fills
+        // r = 0 .. ceil(n / 4) - 1, and the epilogue skips the other r
+        const int nv = it.n - j0 < 16 ? it.n - j0 : 16;
+        const int nr = __builtin_amdgcn_readfirstlane((nv + 3) >> 2);
         __syncthreads();  // the previous unit's readers of LDS are done
         if (tid < 16) {
             const int j = j0 + tid;
@@ -680,15 +694,15 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
             for (int c = 0; c < DQ; ++c) {
                 const int f = tid + 256 * c, t = f / (SG * kGroupWords / 4);
                 const int rem = f - t * (SG * kGroupWords / 4);
-                *reinterpret_cast<v4i *>(&s_dig[t][4 * rem]) = rd[c];
+                *reinterpret_cast<v4i *>(&s_dig[arow(t)][4 * rem]) = rd[c];
             }
             // group sums of groups past ng are zero: the bias products take
             // a stage's groups four at a time
             if (tid < 16 * SG) {
                 const int t = tid / SG, gl = tid - t * SG;
                 const bool ok = s_vec[t] >= 0 && g0 + gl < ng;
-                s_gs[gl][t] = ok ? rg : 0.f;
-                s_inv[gl][t] = ok ? ri : 0.f;
+                s_gs[gl][arow(t)] = ok ? rg : 0.f;
+                s_inv[gl][arow(t)] = ok ? ri : 0.f;
             }
         };
         float acs[M][WT][4];
@@ -709,7 +723,8 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
             const int g0 = st * SG;
             if (st + 1 < nst) load(g0 + SG);  // in flight while this stage is computed
             const int gn = ng - g0 < SG ? ng - g0 : SG;
-            auto group = [&](int gl) {
+            auto group = [&](int gl, auto NRc) {
+                constexpr int NR = decltype(NRc)::value;
                 v4i da[3];
 #pragma unroll
                 for (int p = 0; p < 3; ++p) da[p] = digits_of<BITS>(&s_dig[r16][0], gl, h, p);
@@ -727,7 +742,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                         const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[1], bq, z, 0, 0, 0);
                         const v4i c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[2], bq, z, 0, 0, 0);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
+                        for (int r = 0; r < NR; ++r) {
                             float ps;
                             if constexpr (BITS == 2) {
                                 // |c0 + 256 c1 + 65536 c2| < 3 * 64 * 2^22 < 2^31: exact in
@@ -742,14 +757,22 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                         }
                     }
             };
-            if (BITS == 2 && gn == SG) {
-                // a whole stage: unrolled, so that one group's LDS reads and
-                // matrix-core work overlap the previous group's (at 4-bit the
-                // unrolled gate/up kernel would need more than 256 VGPRs)
+            auto stage = [&](auto NRc) {
+                if (BITS == 2 && gn == SG) {
+                    // a whole stage: unrolled, so that one group's LDS reads and
+                    // matrix-core work overlap the previous group's (at 4-bit the
+                    // unrolled gate/up kernel would need more than 256 VGPRs)
 #pragma unroll
-                for (int gl = 0; gl < SG; ++gl) group(gl);
-            } else {
-                for (int gl = 0; gl < gn; ++gl) group(gl);
+                    for (int gl = 0; gl < SG; ++gl) group(gl, NRc);
+                } else {
+                    for (int gl = 0; gl < gn; ++gl) group(gl, NRc);
+                }
+            };
+            switch (nr) {
+            case 1: stage(std::integral_constant<int, 1>{}); break;
+            case 2: stage(std::integral_constant<int, 2>{}); break;
+            case 3: stage(std::integral_constant<int, 3>{}); break;
+            default: stage(std::integral_constant<int, 4>{}); break;
             }
             // the stage's bias terms, four groups per v_mfma_f32_16x16x4f32:
             // A = group sums (vector l % 16, group l / 16), B = the rows' bias
@@ -785,7 +808,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
             if (s_vec[t] >= 0) {
                 float v[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = s_h[t][group_value<BITS>(r16, j)];
+                for (int j = 0; j < 4; ++j) v[j] = s_h[arow(t)][group_value<BITS>(r16, j)];
                 const size_t pg = ((size_t)it.pos0 + j0 + t) * (I / kGroup) + row0 / kGroup;
                 group_digits<BITS>(v, r16, a.hdig + pg * kGroupWords, a.hcsum + pg, a.hinv + pg);
             }
@@ -795,7 +818,7 @@ __global__ void __launch_bounds__(256) k_expert_mm(BatchArgs a)
                 const int row = row0 + wrow0 + 16 * wt;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * h + r;
+                    const int t = h + 4 * r;
                     if (s_vec[t] < 0 || row >= rows) continue;
                     a.y[((size_t)it.pos0 + j0 + t) * D + row] = acs[0][wt][r] + acb[0][wt][r];
                 }

@@ -142,7 +142,7 @@ __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
 }
 
 // sum over one chunk of code * x_int, from the chunk's digit words; exact
-// in int32 per plane, combined in fp32.
+// in int32, rounded to fp32 once.
 template <int BITS>
 __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
 {
@@ -159,7 +159,12 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
             a1 = __builtin_amdgcn_sdot4(m, d[C::PW], a1, false);
             a2 = __builtin_amdgcn_sdot4(m, d[2 * C::PW], a2, false);
         }
-    return fmaf((float)a2, 65536.f, fmaf((float)a1, 256.f, (float)a0));
+    // |a0|, |a1| <= CODES (2^BITS - 1) 128 and |a2| <= CODES (2^BITS - 1) 64
+    // (digit bounds above), so every partial sum of a0 + 256 a1 + 65536 a2
+    // stays below 2.03e9 < 2^31 at 4-bit (8.1e8 at 2-bit): the chunk's sum
+    // of code * xi exactly, rounded once (the same value as
+    // fma(a2, 65536, a0 + 256 a1) in fp32)
+    return (float)(a2 * 65536 + a1 * 256 + a0);
 }
 
 // Digit table of one chunk built in registers, with a fixed-point step of

@@ -11,11 +11,13 @@
 // applied, h kept in LDS), then h's digit table, then the down rows; so h
 // never leaves the chip and every byte of the range's blobs is read once.
 // Inside an expert, wave w takes row units w, w + 8, ..., so that the eight
-// waves read neighbouring rows at any time.  A wave holds one unit (one
-// gate/up row pair, or 8 to 16 down rows) at a time, so that the kernel fits
-// 128 registers and four waves run per SIMD: while one computes, the loads
-// of the others are in flight (measured faster than two units in flight per
-// wave at two waves per SIMD).
+// waves read neighbouring rows at any time.  A wave's registers hold one
+// unit (one gate/up row pair, or 8 to 16 down rows), so that the kernel fits
+// 128 registers and four waves run per SIMD.  At the pages' layer shape
+// (k_expert_gemv_st) the next unit streams into an LDS stage while the
+// current one is computed, and h and y leave the chip in one coalesced pass
+// per expert; other shapes take k_expert_gemv, whose units are loaded
+// straight into registers.
 #include "moe_device.h"
 
 namespace moe {
@@ -192,19 +194,217 @@ __global__ void __launch_bounds__(NT, (gemv_waves<BITS, GCPL>())) k_expert_gemv(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same GEMVs with the next unit's weights in flight while a wave
+// computes.  A wave's registers hold one unit (the 128-register budget of
+// four waves per SIMD leaves no room for a second), so the next unit is
+// requested straight into LDS (buffer loads with the LDS destination: no
+// registers, no waiting at issue): per wave one stage of up to four
+// 16-byte chunks and four scale/bias words per lane.  The unit in the stage
+// is copied into registers (vmcnt(0) first: only the stage's loads and the
+// h stores are outstanding then), the stage is refilled with the unit
+// after, and the copied unit is computed while that refill streams.  The
+// tables live in fixed-size LDS arrays, distinct objects from the stage, so
+// that the compiler sees that the tables' reads do not depend on the stage's
+// loads and puts no wait for them in front of the arithmetic.  Capacity:
+// D <= 4096, I <= 1024 (the pages' layer shape; others take k_expert_gemv).
+constexpr int kStDmax = 4096, kStImax = 1024, kStSlots = 4;
+
+#define MOE_LDSP(p) ((__attribute__((address_space(3))) void *)(p))
+
+// wait for every outstanding vector-memory operation of the wave (gfx9
+// s_waitcnt: vmcnt 0, expcnt and lgkmcnt left open)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait for every outstanding LDS operation of the wave (vmcnt left open)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int BITS>
+struct StLds {
+    using C = Codes<BITS>;
+    static constexpr int XCH = kStDmax * BITS / 128, HCH = kStImax * BITS / 128;
+    int dig[XCH * C::DW];
+    float csum[XCH], cinv[XCH];
+    float h[kStImax];
+    float y[kStDmax];
+    int hdig[HCH * C::DW];
+    float hcsum[HCH], hcinv[HCH];
+};
+
+// gate/up unit (rows i0 .. i0+R-1) -> stage: slot (m*R + r)*2 + mat
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void gu_stage(__amdgpu_buffer_rsrc_t rs, uint4 (*sq)[64], uint32_t (*ssb)[64], int D, int I,
+                                         int i0, int lane)
+{
+    using C = Codes<BITS>;
+    static_assert(CPL * R * 2 <= kStSlots, "stage slots");
+    const int nchunks = D * BITS / 128;
+    const uint32_t mat_q = (uint32_t)I * D * BITS / 8, row_q = (uint32_t)D * BITS / 8;
+    const uint32_t sb0 = 3 * mat_q, mat_sb = (uint32_t)I * (D / kGroup) * 4, row_sb = (uint32_t)(D / kGroup) * 4;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lane + 64 * m;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = i0 + r;
+            if (i >= I || c >= nchunks) continue;
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                const int slot = (m * R + r) * 2 + mat;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&sq[slot][0]), 16, (uint32_t)c * 16,
+                                                         mat * mat_q + (uint32_t)i * row_q, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&ssb[slot][0]), 4,
+                                                         (uint32_t)(c * C::CODES / kGroup) * 4,
+                                                         sb0 + mat * mat_sb + (uint32_t)i * row_sb, 0, 0);
+            }
+        }
+    }
+}
+
+template <int BITS, int CPL, int R>
+__device__ __forceinline__ void gu_unstage(GuRegs<BITS, CPL, R> &g, const uint4 (*sq)[64], const uint32_t (*ssb)[64],
+                                           int D, int I, int i0, int lane)
+{
+    const int nchunks = D * BITS / 128;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = lane + 64 * m;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool ok = i0 + r < I && c < nchunks;
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                const int slot = (m * R + r) * 2 + mat;
+                g.q[m][r][mat] = ok ? sq[slot][lane] : make_uint4(0, 0, 0, 0);
+                g.sb[m][r][mat] = ok ? ssb[slot][lane] : 0u;
+            }
+        }
+    }
+}
+
+// down unit (S row groups of RPU rows from o0) -> stage: slot s*DCPL + m
+template <int BITS, int LPR, int DCPL, int S>
+__device__ __forceinline__ void dn_stage(__amdgpu_buffer_rsrc_t rs, uint4 (*sq)[64], uint32_t (*ssb)[64], int D, int I,
+                                         int o0, int lane)
+{
+    using C = Codes<BITS>;
+    constexpr int RPU = 64 / LPR;
+    static_assert(S * DCPL <= kStSlots, "stage slots");
+    const int nchunks = I * BITS / 128, lc = lane % LPR;
+    const uint32_t mat_q = (uint32_t)I * D * BITS / 8, row_q = (uint32_t)I * BITS / 8;
+    const uint32_t sbd = 3 * mat_q + 2 * ((uint32_t)D * (I / kGroup) * 4), row_sb = (uint32_t)(I / kGroup) * 4;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int os = o0 + s * RPU;
+        const int o = os + lane / LPR;
+#pragma unroll
+        for (int m = 0; m < DCPL; ++m) {
+            const int c = lc + LPR * m;
+            if (o >= D || c >= nchunks) continue;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&sq[s * DCPL + m][0]), 16,
+                                                     (uint32_t)(lane / LPR) * row_q + (uint32_t)c * 16,
+                                                     2 * mat_q + (uint32_t)os * row_q, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&ssb[s * DCPL + m][0]), 4,
+                                                     (uint32_t)(lane / LPR) * row_sb + (uint32_t)(c * C::CODES / kGroup) * 4,
+                                                     sbd + (uint32_t)os * row_sb, 0, 0);
+        }
+    }
+}
+
+template <int BITS, int LPR, int DCPL, int S>
+__device__ __forceinline__ void dn_unstage(DnUnit<BITS, DCPL, S> &u, const uint4 (*sq)[64], const uint32_t (*ssb)[64],
+                                           int D, int I, int o0, int lane)
+{
+    constexpr int RPU = 64 / LPR;
+    const int nchunks = I * BITS / 128, lc = lane % LPR;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int o = o0 + s * RPU + lane / LPR;
+#pragma unroll
+        for (int m = 0; m < DCPL; ++m) {
+            const bool ok = o < D && lc + LPR * m < nchunks;
+            u.d[s].q[m] = ok ? sq[s * DCPL + m][lane] : make_uint4(0, 0, 0, 0);
+            u.d[s].sb[m] = ok ? ssb[s * DCPL + m][lane] : 0u;
+        }
+    }
+}
+
+template <int BITS, int GCPL, int R, int LPR, int DCPL>
+__global__ void __launch_bounds__(NT, 4) k_expert_gemv_st(GemvArgs a)
+{
+    constexpr int RPU = 64 / LPR;
+    constexpr int S0 = 16 / RPU > 0 ? 16 / RPU : 1;
+    constexpr int S = S0 * DCPL > 4 ? 4 / DCPL : S0;
+    constexpr int RPD = RPU * S;
+    __shared__ __align__(16) StLds<BITS> t;
+    __shared__ __align__(16) uint4 s_q[NW][kStSlots][64];
+    __shared__ __align__(16) uint32_t s_sb[NW][kStSlots][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int D = a.D, I = a.I;
+    uint4 (*sq)[64] = s_q[wave];
+    uint32_t (*ssb)[64] = s_sb[wave];
+
+    digit_table<BITS>(a.x, D, t.dig, t.csum, t.cinv);
+    lds_barrier();
+
+    const int ngu = (I + R - 1) / R;
+    const int ndn = (D + RPD - 1) / RPD;
+    for (int n = blockIdx.x; n < a.count; n += gridDim.x) {
+        const uint8_t *blob = a.experts + (uint64_t)(a.first + n) * a.blob_bytes;
+        const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob);
+        float *hn = a.h + (size_t)n * I;
+        float *yn = a.y + (size_t)n * D;
+        if (wave < ngu) gu_stage<BITS, GCPL, R>(rs, sq, ssb, D, I, wave * R, lane);
+        for (int u = wave; u < ngu; u += NW) {
+            GuRegs<BITS, GCPL, R> g;
+            wait_vm0();
+            gu_unstage<BITS, GCPL, R>(g, sq, ssb, D, I, u * R, lane);
+            wait_lgkm0();
+            if (u + NW < ngu) gu_stage<BITS, GCPL, R>(rs, sq, ssb, D, I, (u + NW) * R, lane);
+            float hv[R];
+            gu_finish_c<BITS, GCPL, R>(g, t.dig, t.csum, t.cinv, D, lane, hv);
+            if (lane == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int i = u * R + r;
+                    if (i < I) t.h[i] = hv[r];
+                }
+            }
+        }
+        // the first down unit streams while h is completed and converted
+        if (wave < ndn) dn_stage<BITS, LPR, DCPL, S>(rs, sq, ssb, D, I, wave * RPD, lane);
+        lds_barrier();
+        digit_table<BITS>(t.h, I, t.hdig, t.hcsum, t.hcinv);
+        for (int i = threadIdx.x; i < I; i += NT) hn[i] = t.h[i];
+        lds_barrier();
+        for (int u = wave; u < ndn; u += NW) {
+            DnUnit<BITS, DCPL, S> d;
+            wait_vm0();
+            dn_unstage<BITS, LPR, DCPL, S>(d, sq, ssb, D, I, u * RPD, lane);
+            wait_lgkm0();
+            if (u + NW < ndn) dn_stage<BITS, LPR, DCPL, S>(rs, sq, ssb, D, I, (u + NW) * RPD, lane);
+            dn_unit_finish<BITS, LPR, DCPL, S>(d, t.hdig, t.hcsum, t.hcinv, I, D, u * RPD, lane, t.y);
+        }
+        // y leaves in one coalesced pass (no stores between a wave's stage
+        // refills, whose wait would also wait for them)
+        lds_barrier();
+        for (int o = threadIdx.x; o < D; o += NT) yn[o] = t.y[o];
+    }
+}
+
 struct GemvPlanCache {
     int ready = 0, n_cu = 0, per_cu = 0, vgprs = 0, scratch = 0;
 };
 
-template <int BITS, int GCPL, int R, int LPR, int DCPL>
-hipError_t gemv_launch(const GemvArgs &a, hipStream_t s, LayerPlan *p)
+// One kernel instantiation's launch: its attributes are read once per
+// device; the grid fills every CU at the occupancy this shape's LDS allows.
+template <typename Kern>
+hipError_t gemv_run(Kern kern, GemvPlanCache *cache, uint32_t lds_bytes, const GemvArgs &a, hipStream_t s,
+                    LayerPlan *p)
 {
-    auto kern = k_expert_gemv<BITS, GCPL, R, LPR, DCPL>;
-    static GemvPlanCache cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    const GemvLds lo = gemv_lds(a.D, a.I, BITS);
     GemvPlanCache c = dev < 64 ? cache[dev] : GemvPlanCache{};
     if (!c.ready) {
         hipFuncAttributes attr;
@@ -212,14 +412,14 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s, LayerPlan *p)
         c.vgprs = attr.numRegs;
         c.scratch = (int)attr.localSizeBytes;
         if ((e = hipDeviceGetAttribute(&c.n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                160 * 1024) != hipSuccess)
+        if (lds_bytes > 0 && hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             (void)hipGetLastError();
         c.ready = 1;
     }
     // occupancy depends on this shape's LDS
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&c.per_cu, reinterpret_cast<const void *>(kern), NT,
-                                                          lo.total)) != hipSuccess)
+                                                          lds_bytes)) != hipSuccess)
         return e;
     if (dev < 64) cache[dev] = c;
     // instantiations that spill to scratch memory are not run
@@ -234,8 +434,26 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s, LayerPlan *p)
         p->vgprs = c.vgprs;
         p->scratch = c.scratch;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lo.total, s, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds_bytes, s, a);
     return hipGetLastError();
+}
+
+template <int BITS, int GCPL, int R, int LPR, int DCPL>
+hipError_t gemv_launch(const GemvArgs &a, hipStream_t s, LayerPlan *p)
+{
+    constexpr int RPU = 64 / LPR;
+    constexpr int S0 = 16 / RPU > 0 ? 16 / RPU : 1;
+    constexpr int S = S0 * DCPL > 4 ? 4 / DCPL : S0;
+    // the staged kernel where its fixed tables hold the shape and a unit
+    // fits its stage
+    if constexpr (GCPL * R * 2 <= kStSlots && S * DCPL <= kStSlots && gemv_waves<BITS, GCPL>() == 4) {
+        if (a.D <= kStDmax && a.I <= kStImax) {
+            static GemvPlanCache cache[64];
+            return gemv_run(k_expert_gemv_st<BITS, GCPL, R, LPR, DCPL>, cache, 0u, a, s, p);
+        }
+    }
+    static GemvPlanCache cache[64];
+    return gemv_run(k_expert_gemv<BITS, GCPL, R, LPR, DCPL>, cache, gemv_lds(a.D, a.I, BITS).total, a, s, p);
 }
 
 template <int BITS, int GCPL, int R>

@@ -235,7 +235,6 @@ template <int BITS, int CPL, int R>
 __device__ __forceinline__ void gu_stage(__amdgpu_buffer_rsrc_t rs, uint4 (*sq)[64], uint32_t (*ssb)[64], int D, int I,
                                          int i0, int lane)
 {
-    using C = Codes<BITS>;
     static_assert(CPL * R * 2 <= kStSlots, "stage slots");
     const int nchunks = D * BITS / 128;
     const uint32_t mat_q = (uint32_t)I * D * BITS / 8, row_q = (uint32_t)D * BITS / 8;
@@ -248,15 +247,21 @@ __device__ __forceinline__ void gu_stage(__amdgpu_buffer_rsrc_t rs, uint4 (*sq)[
             const int i = i0 + r;
             if (i >= I || c >= nchunks) continue;
 #pragma unroll
-            for (int mat = 0; mat < 2; ++mat) {
-                const int slot = (m * R + r) * 2 + mat;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&sq[slot][0]), 16, (uint32_t)c * 16,
-                                                         mat * mat_q + (uint32_t)i * row_q, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&ssb[slot][0]), 4,
-                                                         (uint32_t)(c * C::CODES / kGroup) * 4,
-                                                         sb0 + mat * mat_sb + (uint32_t)i * row_sb, 0, 0);
-            }
+            for (int mat = 0; mat < 2; ++mat)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&sq[(m * R + r) * 2 + mat][0]), 16,
+                                                         (uint32_t)c * 16, mat * mat_q + (uint32_t)i * row_q, 0, 0);
         }
+    }
+    // a row's scale/bias words (D/64 <= 64 of them), word l in lane l, in
+    // slot r*2 + mat
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = i0 + r;
+        if (i >= I || lane >= D / kGroup) continue;
+#pragma unroll
+        for (int mat = 0; mat < 2; ++mat)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&ssb[r * 2 + mat][0]), 4, (uint32_t)lane * 4,
+                                                     sb0 + mat * mat_sb + (uint32_t)i * row_sb, 0, 0);
     }
 }
 
@@ -265,6 +270,7 @@ __device__ __forceinline__ void gu_unstage(GuRegs<BITS, CPL, R> &g, const uint4 
                                            int D, int I, int i0, int lane)
 {
     const int nchunks = D * BITS / 128;
+    using C = Codes<BITS>;
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
         const int c = lane + 64 * m;
@@ -273,9 +279,8 @@ __device__ __forceinline__ void gu_unstage(GuRegs<BITS, CPL, R> &g, const uint4 
             const bool ok = i0 + r < I && c < nchunks;
 #pragma unroll
             for (int mat = 0; mat < 2; ++mat) {
-                const int slot = (m * R + r) * 2 + mat;
-                g.q[m][r][mat] = ok ? sq[slot][lane] : make_uint4(0, 0, 0, 0);
-                g.sb[m][r][mat] = ok ? ssb[slot][lane] : 0u;
+                g.q[m][r][mat] = ok ? sq[(m * R + r) * 2 + mat][lane] : make_uint4(0, 0, 0, 0);
+                g.sb[m][r][mat] = ok ? ssb[r * 2 + mat][c * C::CODES / kGroup] : 0u;
             }
         }
     }
@@ -286,7 +291,6 @@ template <int BITS, int LPR, int DCPL, int S>
 __device__ __forceinline__ void dn_stage(__amdgpu_buffer_rsrc_t rs, uint4 (*sq)[64], uint32_t (*ssb)[64], int D, int I,
                                          int o0, int lane)
 {
-    using C = Codes<BITS>;
     constexpr int RPU = 64 / LPR;
     static_assert(S * DCPL <= kStSlots, "stage slots");
     const int nchunks = I * BITS / 128, lc = lane % LPR;
@@ -303,10 +307,19 @@ __device__ __forceinline__ void dn_stage(__amdgpu_buffer_rsrc_t rs, uint4 (*sq)[
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&sq[s * DCPL + m][0]), 16,
                                                      (uint32_t)(lane / LPR) * row_q + (uint32_t)c * 16,
                                                      2 * mat_q + (uint32_t)os * row_q, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&ssb[s * DCPL + m][0]), 4,
-                                                     (uint32_t)(lane / LPR) * row_sb + (uint32_t)(c * C::CODES / kGroup) * 4,
-                                                     sbd + (uint32_t)os * row_sb, 0, 0);
         }
+    }
+    // the scale/bias words of the unit's rows (contiguous in the blob, I/64
+    // per row, at most 64 * S * DCPL): word w in lane w % 64 of slot w / 64;
+    // words of rows past D are not requested
+    const int rows = D - o0 < RPU * S ? D - o0 : RPU * S;
+    const int nw = rows * (I / kGroup);
+#pragma unroll
+    for (int q = 0; q < S * DCPL; ++q) {
+        if (64 * q >= nw) break;
+        if (64 * q + lane < nw)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MOE_LDSP(&ssb[q][0]), 4, (uint32_t)(64 * q + lane) * 4,
+                                                     sbd + (uint32_t)o0 * row_sb, 0, 0);
     }
 }
 
@@ -316,14 +329,17 @@ __device__ __forceinline__ void dn_unstage(DnUnit<BITS, DCPL, S> &u, const uint4
 {
     constexpr int RPU = 64 / LPR;
     const int nchunks = I * BITS / 128, lc = lane % LPR;
+    using C = Codes<BITS>;
+    const int *sbw = reinterpret_cast<const int *>(ssb);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int o = o0 + s * RPU + lane / LPR;
 #pragma unroll
         for (int m = 0; m < DCPL; ++m) {
-            const bool ok = o < D && lc + LPR * m < nchunks;
+            const int c = lc + LPR * m;
+            const bool ok = o < D && c < nchunks;
             u.d[s].q[m] = ok ? sq[s * DCPL + m][lane] : make_uint4(0, 0, 0, 0);
-            u.d[s].sb[m] = ok ? ssb[s * DCPL + m][lane] : 0u;
+            u.d[s].sb[m] = ok ? (uint32_t)sbw[(o - o0) * (I / kGroup) + c * C::CODES / kGroup] : 0u;
         }
     }
 }
@@ -447,7 +463,9 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s, LayerPlan *p)
     // the staged kernel where its fixed tables hold the shape and a unit
     // fits its stage
     if constexpr (GCPL * R * 2 <= kStSlots && S * DCPL <= kStSlots && gemv_waves<BITS, GCPL>() == 4) {
-        if (a.D <= kStDmax && a.I <= kStImax) {
+        // (a down unit's scale/bias words must fit the stage's 64 * S * DCPL
+        // words, which holds whenever its LPR * DCPL lanes cover a row)
+        if (a.D <= kStDmax && a.I <= kStImax && RPU * S * (a.I / kGroup) <= 64 * S * DCPL) {
             static GemvPlanCache cache[64];
             return gemv_run(k_expert_gemv_st<BITS, GCPL, R, LPR, DCPL>, cache, 0u, a, s, p);
         }

@@ -14,8 +14,11 @@
 // digit planes, x_int = d0 + 256 d1 + 65536 d2.  A 32-bit word of codes,
 // masked so that each byte holds one code, then meets the matching digit
 // words in three v_dot4_i32_i8 (four code*digit products each, exact in
-// int32).  Per 16-byte chunk the three plane sums are combined once in fp32
-// and scaled by 2^-k * scale.  Apart from the fixed-point rounding of x
+// int32).  2-bit codes take six signed 4-bit digit planes instead,
+// x_int = sum_p d_p 16^p, and v_dot8_i32_i4 (eight products each): one mask
+// or one shift and mask of a code word leaves eight codes as nibbles.  Per
+// 16-byte chunk the plane sums are combined exactly in int32, rounded once
+// to fp32 and scaled by 2^-k * scale.  Apart from the fixed-point rounding of x
 // (half a unit of 2^-k, about 1e-7 of the vector's largest element) the sum
 // is exact.  Cost: 4-bit about 1.4 VALU operations per weight, 2-bit about
 // 1.3, against about 3 for a float conversion and an FMA per weight.
@@ -122,6 +125,36 @@ __device__ __forceinline__ void digit_words(float a, float b, float c, float d, 
                                     0x05040100u);
 }
 
+// 2-bit chunks: six signed base-16 digits of xi = round(v * mul),
+// xi = sum_p d_p 16^p with d_p in [-8, 7] (|xi| < 2^22 leaves |d_5| <= 4).
+// Word (2 k + s) * 6 + p of a chunk holds, in nibble j, digit p of value
+// 16 k + s + 2 j: the values of codes s, s + 2, ..., s + 14 of code word k,
+// which the mask 0x33333333 of the word (s = 0) or of the word shifted
+// right by 2 (s = 1) leaves as nibbles.  48 words per chunk (Codes<2>::DW).
+constexpr int kNibPlanes = 6;
+
+// The digits come out of one add and one XOR: y = xi + 0x888888 lies in
+// [0, 2^24) and equals sum_p (d_p + 8) 16^p, so nibble p of
+// y ^ 0x888888 is d_p + 8 - 8 read as a signed 4-bit number, d_p.
+__device__ __forceinline__ uint32_t nib_digits(float v, float mul)
+{
+    return (uint32_t)(__float2int_rn(v * mul) + 0x888888) ^ 0x888888u;
+}
+
+// the six digit words of the eight values v[0], v[2], ..., v[14]
+__device__ __forceinline__ void nib_words(const float *v, float mul, int *o)
+{
+    uint32_t w[kNibPlanes] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t z = nib_digits(v[2 * j], mul);
+#pragma unroll
+        for (int p = 0; p < kNibPlanes; ++p) w[p] |= ((z >> (4 * p)) & 15u) << (4 * j);
+    }
+#pragma unroll
+    for (int p = 0; p < kNibPlanes; ++p) o[p] = (int)w[p];
+}
+
 // Digit words of one chunk from the chunk's activations v[0..CODES): the
 // word of plane p for word k, sub s holds, in byte j, digit p of
 // v[k*PER_WORD + s + SUBS*j].  Plane-major: dg index p*PW + k*SUBS + s, so
@@ -131,6 +164,14 @@ template <int BITS>
 __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
 {
     using C = Codes<BITS>;
+    if constexpr (BITS == 2) {
+        // the nibble planes above
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) nib_words(v + 16 * k + sh, mul, dg + (2 * k + sh) * kNibPlanes);
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -148,6 +189,24 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
 {
     using C = Codes<BITS>;
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    if constexpr (BITS == 2) {
+        // nibble planes: |a_p| <= 64 * 3 * 8, and the Horner sums are partial
+        // sums of sum code * (xi >> 4m), below 8.1e8: exact in int32
+        int a[kNibPlanes] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ev = (int)(w[k] & 0x33333333u), od = (int)((w[k] >> 2) & 0x33333333u);
+#pragma unroll
+            for (int p = 0; p < kNibPlanes; ++p) {
+                a[p] = __builtin_amdgcn_sdot8(ev, dg[(2 * k) * kNibPlanes + p], a[p], false);
+                a[p] = __builtin_amdgcn_sdot8(od, dg[(2 * k + 1) * kNibPlanes + p], a[p], false);
+            }
+        }
+        int h = a[kNibPlanes - 1];
+#pragma unroll
+        for (int p = kNibPlanes - 2; p >= 0; --p) h = h * 16 + a[p];
+        return (float)h;
+    }
     int a0 = 0, a1 = 0, a2 = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -170,10 +229,10 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
 // Digit table of one chunk built in registers, with a fixed-point step of
 // its own.  A chunk's CODES values are held as float4 by G = CODES/4
 // consecutive lanes (lane f of the chunk holds values 4f..4f+3, float4 q
-// of the vector); the word of plane p for code word k, sub s holds values
-// k*PER_WORD + s + SUBS*j, which lie in the SUBS lanes of word k, so those
-// lanes trade components through quad DPP and lane f writes word f of
-// every plane.  The chunk's largest magnitude (step inv = 2^-k with
+// of the vector).  4-bit: the word of plane p for code word k, sub s holds
+// values k*PER_WORD + s + SUBS*j, which lie in the two lanes of word k, so
+// those lanes trade components through DPP and lane f writes word f of
+// every plane.  2-bit: the nibble planes, written bytewise.  The chunk's largest magnitude (step inv = 2^-k with
 // max * 2^k < 2^22) and its fp32 sum come from DPP reductions over the G
 // lanes; lane 0 of the chunk writes csum[c] and cinv[c].  All 64 lanes
 // call it; lanes past the end (whole chunks) pass valid = false and write
@@ -189,50 +248,48 @@ __device__ __forceinline__ void chunk_digits_lane(float4 v, int q, bool valid, i
     const float sum = group_sum<G>((v.x + v.y) + (v.z + v.w));
     float mul, inv;
     fixed_scale(m, mul, inv);
-    const int lane = threadIdx.x & 63;
-    float a, b, c, d;
-    if constexpr (BITS == 4) {
-        // pair (p = 0, 1): word p takes components p and p+2 of both lanes
-        const int p = lane & 1;
-        const float s0 = fdpp<0xB1>(p ? v.x : v.y, 0.f);
-        const float s1 = fdpp<0xB1>(p ? v.z : v.w, 0.f);
-        a = p ? s0 : v.x;
-        b = p ? s1 : v.z;
-        c = p ? v.y : s0;
-        d = p ? v.w : s1;
-    } else {
-        // quad (p = 0..3): word p takes component p of lanes 0..3 in order;
-        // in round r lane p reads lane (p + r) & 3, which sends component
-        // (its lane - r) & 3
-        const int p = lane & 3;
-        auto comp = [&](int i) {
-            const float lo = (i & 1) ? v.y : v.x, hi = (i & 1) ? v.w : v.z;
-            return (i & 2) ? hi : lo;
-        };
-        const float own = comp(p);
-        const float r1 = fdpp<0x39>(comp((p - 1) & 3), 0.f);  // quad_perm [1,2,3,0]
-        const float r2 = fdpp<0x4E>(comp((p - 2) & 3), 0.f);  // quad_perm [2,3,0,1]
-        const float r3 = fdpp<0x93>(comp((p - 3) & 3), 0.f);  // quad_perm [3,0,1,2]
-        auto from = [&](int j) {
-            const int r = (j - p) & 3;
-            return r == 0 ? own : r == 1 ? r1 : r == 2 ? r2 : r3;
-        };
-        a = from(0);
-        b = from(1);
-        c = from(2);
-        d = from(3);
-    }
-    int w0, w1, w2;
-    digit_words(a, b, c, d, mul, w0, w1, w2);
-    if (valid) {
+    if constexpr (BITS == 2) {
+        // nibble planes: lane f (values 4f..4f+3, code word f / 4) supplies
+        // byte f % 4 of its code word's twelve words, nibble pairs of its
+        // values (s, s + 2) for half s
+        if (!valid) return;  // after the reductions, which need every lane
         const int ch = q / G, f = q - ch * G;
-        int *o = dig + ch * C::DW + f;
-        o[0] = w0;
-        o[C::PW] = w1;
-        o[2 * C::PW] = w2;
+        const uint32_t z[4] = {nib_digits(v.x, mul), nib_digits(v.y, mul), nib_digits(v.z, mul), nib_digits(v.w, mul)};
+        uint8_t *base = reinterpret_cast<uint8_t *>(dig + ch * C::DW) + (f & 3);
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+            // byte m: planes 2m (ev) and 2m + 1 (od) of values sh and sh + 2
+            const uint32_t ev = (z[sh] & 0x0F0F0Fu) | ((z[sh + 2] & 0x0F0F0Fu) << 4);
+            const uint32_t od = ((z[sh] >> 4) & 0x0F0F0Fu) | (z[sh + 2] & 0xF0F0F0u);
+            uint8_t *wb = base + ((f >> 2) * 2 + sh) * kNibPlanes * 4;
+#pragma unroll
+            for (int m2 = 0; m2 < 3; ++m2) {
+                wb[(2 * m2) * 4] = (uint8_t)(ev >> (8 * m2));
+                wb[(2 * m2 + 1) * 4] = (uint8_t)(od >> (8 * m2));
+            }
+        }
         if (f == 0) {
             csum[ch] = sum;
             cinv[ch] = inv;
+        }
+    } else {
+        // pair (p = 0, 1): word p takes components p and p+2 of both lanes
+        const int p = threadIdx.x & 1;
+        const float s0 = fdpp<0xB1>(p ? v.x : v.y, 0.f);
+        const float s1 = fdpp<0xB1>(p ? v.z : v.w, 0.f);
+        const float a = p ? s0 : v.x, b = p ? s1 : v.z, c = p ? v.y : s0, d = p ? v.w : s1;
+        int w0, w1, w2;
+        digit_words(a, b, c, d, mul, w0, w1, w2);
+        if (valid) {
+            const int ch = q / G, f = q - ch * G;
+            int *o = dig + ch * C::DW + f;
+            o[0] = w0;
+            o[C::PW] = w1;
+            o[2 * C::PW] = w2;
+            if (f == 0) {
+                csum[ch] = sum;
+                cinv[ch] = inv;
+            }
         }
     }
 }
@@ -307,14 +364,24 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
     for (int w = 0; w < (nt >> 6); ++w) amax = fmaxf(amax, red[w]);
     float mul, inv;
     fixed_scale(amax, mul, inv);
-    // one thread per (chunk, word, sub): four activations -> three words
-    const int nwords = n / C::CODES * 4 * C::SUBS;
-    for (int t = tid; t < nwords; t += nt) {
-        const int c = t / (4 * C::SUBS), r = t - c * 4 * C::SUBS;
-        const int k = r / C::SUBS, s = r - k * C::SUBS;
-        const float *v = x + c * C::CODES + k * C::PER_WORD + s;
-        int *o = dig + c * C::DW + k * C::SUBS + s;
-        digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
+    if constexpr (BITS == 2) {
+        // one thread per (chunk, code word, half): eight activations -> six
+        // nibble words
+        const int nw = n / C::CODES * 8;
+        for (int t = tid; t < nw; t += nt) {
+            const int c = t >> 3, k = (t >> 1) & 3, sh = t & 1;
+            nib_words(x + c * C::CODES + 16 * k + sh, mul, dig + c * C::DW + (2 * k + sh) * kNibPlanes);
+        }
+    } else {
+        // one thread per (chunk, word, sub): four activations -> three words
+        const int nwords = n / C::CODES * 4 * C::SUBS;
+        for (int t = tid; t < nwords; t += nt) {
+            const int c = t / (4 * C::SUBS), r = t - c * 4 * C::SUBS;
+            const int k = r / C::SUBS, s = r - k * C::SUBS;
+            const float *v = x + c * C::CODES + k * C::PER_WORD + s;
+            int *o = dig + c * C::DW + k * C::SUBS + s;
+            digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
+        }
     }
     chunk_sums<BITS>(x, n / C::CODES, csum);
     bsync<LDS_SYNC>();

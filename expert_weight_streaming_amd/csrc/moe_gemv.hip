@@ -54,150 +54,17 @@ __host__ __device__ inline GemvLds gemv_lds(int D, int I, int bits)
     return l;
 }
 
-// 2-bit digit tables in six signed base-16 digit planes (the staged
-// kernel): the same fixed-point value xi = round(v 2^k) of every activation
-// (one step per 64-value chunk, |xi| < 2^22) written as
-// xi = sum_p d_p 16^p, d_p in [-8, 7], p < 6, so that one v_dot8_i32_i4
-// multiplies eight 2-bit codes by eight digits.  Word (2 k + s) * 6 + p of
-// a chunk holds, in nibble j, digit p of value 16 k + s + 2 j: the values
-// of code word k's codes s, s + 2, ..., which one mask (s = 0) or one shift
-// and mask (s = 1) of the code word leaves as nibbles.  48 words per chunk,
-// as the three-plane table.  A chunk's 64 values are held as float4 by 16
-// consecutive lanes; lane f supplies byte f % 4 of each of its code word's
-// twelve words.  All 64 lanes call it (DPP reductions); lanes past the end
-// pass valid = false and write nothing.
-__device__ __forceinline__ void chunk_nibbles_lane(float4 v, int q, bool valid, int *dig, float *csum, float *cinv)
-{
-    constexpr int G = 16;
-    if (!valid) v = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float m = group_max<G>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    const float sum = group_sum<G>((v.x + v.y) + (v.z + v.w));
-    float mul, inv;
-    fixed_scale(m, mul, inv);
-    if (!valid) return;
-    const int ch = q / G, f = q - ch * G;
-    int r[4] = {__float2int_rn(v.x * mul), __float2int_rn(v.y * mul), __float2int_rn(v.z * mul),
-                __float2int_rn(v.w * mul)};
-    int d[4][6];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            d[c][p] = __builtin_amdgcn_sbfe(r[c], 0, 4);
-            r[c] = (r[c] - d[c][p]) >> 4;  // exact: r - d is a multiple of 16
-        }
-    uint8_t *base = reinterpret_cast<uint8_t *>(dig + ch * 48) + (f & 3);
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-        for (int p = 0; p < 6; ++p)
-            base[(((f >> 2) * 2 + sh) * 6 + p) * 4] = (uint8_t)((d[sh][p] & 15) | ((d[sh + 2][p] & 15) << 4));
-    if (f == 0) {
-        csum[ch] = sum;
-        cinv[ch] = inv;
-    }
-}
-
-// sum over one 2-bit chunk of code * xi from its nibble digit words:
-// |a_p| <= 64 * 3 * 8 and the Horner sums are partial sums of
-// sum code * (xi >> 4m), below 8.1e8: exact in int32, rounded to fp32 once
-// (the same value as qdot's from the three-plane table)
-__device__ __forceinline__ float qdot_nib(const uint4 q, const int *dg)
-{
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    int a[6] = {0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int ev = (int)(w[k] & 0x33333333u), od = (int)((w[k] >> 2) & 0x33333333u);
-#pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            a[p] = __builtin_amdgcn_sdot8(ev, dg[k * 12 + p], a[p], false);
-            a[p] = __builtin_amdgcn_sdot8(od, dg[k * 12 + 6 + p], a[p], false);
-        }
-    }
-    int h = a[5];
-#pragma unroll
-    for (int p = 4; p >= 0; --p) h = h * 16 + a[p];
-    return (float)h;
-}
-
-template <int BITS, bool NIB>
-__device__ __forceinline__ float qdot_g(const uint4 q, const int *dg)
-{
-    if constexpr (NIB) {
-        static_assert(BITS == 2, "nibble digits serve 2-bit codes");
-        return qdot_nib(q, dg);
-    } else {
-        return qdot<BITS>(q, dg);
-    }
-}
-
 // A vector of n fp32 values (n a multiple of the chunk width; global or
-// LDS) as a digit table with one fixed-point step per chunk (NIB: the
-// nibble planes above).  Called by the whole workgroup.
-template <int BITS, bool NIB = false>
+// LDS) as a digit table with one fixed-point step per chunk.  Called by the
+// whole workgroup.
+template <int BITS>
 __device__ __forceinline__ void digit_table(const float *v, int n, int *dig, float *csum, float *cinv)
 {
     const int n4 = n / 4;
     for (int q0 = 0; q0 < n4; q0 += NT) {
         const int q = q0 + (int)threadIdx.x;
         const float4 f = q < n4 ? reinterpret_cast<const float4 *>(v)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        if constexpr (NIB)
-            chunk_nibbles_lane(f, q, q < n4, dig, csum, cinv);
-        else
-            chunk_digits_lane<BITS>(f, q, q < n4, dig, csum, cinv);
-    }
-}
-
-// gu_finish_c with the digit format chosen by NIB.
-template <int BITS, int CPL, int R, bool NIB>
-__device__ __forceinline__ void gu_finish_g(const GuRegs<BITS, CPL, R> &g, const int *dig, const float *csum,
-                                            const float *cinv, int D, int lane, float (&h)[R])
-{
-    if constexpr (!NIB) {
-        gu_finish_c<BITS, CPL, R>(g, dig, csum, cinv, D, lane, h);
-    } else {
-        using C = Codes<BITS>;
-        const int nchunks = D * BITS / 128;
-        float acc[R][2];
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
-#pragma unroll
-        for (int m = 0; m < CPL; ++m) {
-            const int c = lane + 64 * m;
-            int dg[C::DW];
-            float cs = 0.f, ci = 0.f;
-            if (c < nchunks) {
-                const int4 *src = reinterpret_cast<const int4 *>(dig + c * C::DW);
-#pragma unroll
-                for (int t = 0; t < C::DW / 4; ++t) {
-                    const int4 v = src[t];
-                    dg[4 * t] = v.x;
-                    dg[4 * t + 1] = v.y;
-                    dg[4 * t + 2] = v.z;
-                    dg[4 * t + 3] = v.w;
-                }
-                cs = csum[c];
-                ci = cinv[c];
-            } else {
-#pragma unroll
-                for (int t = 0; t < C::DW; ++t) dg[t] = 0;
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int mat = 0; mat < 2; ++mat) {
-                    const float qx = qdot_nib(g.q[m][r][mat], dg);
-                    acc[r][mat] = fmaf(bf16_lo(g.sb[m][r][mat]) * ci, qx, acc[r][mat]);
-                    acc[r][mat] = fmaf(bf16_hi(g.sb[m][r][mat]), cs, acc[r][mat]);
-                }
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float gg = group_sum<64>(acc[r][0]);
-            const float u = group_sum<64>(acc[r][1]);
-            h[r] = gg / (1.f + expf(-gg)) * u;
-        }
+        chunk_digits_lane<BITS>(f, q, q < n4, dig, csum, cinv);
     }
 }
 
@@ -219,7 +86,7 @@ __device__ __forceinline__ void dn_unit_load(DnUnit<BITS, DCPL, S> &u, const uin
 
 // The unit's rows against h's digit table (LDS), each chunk's digits read
 // once for all S groups; row sums in rows o0 + s*RPU + lane/LPR.
-template <int BITS, int LPR, int DCPL, int S, bool NIB = false>
+template <int BITS, int LPR, int DCPL, int S>
 __device__ __forceinline__ void dn_unit_finish(const DnUnit<BITS, DCPL, S> &u, const int *hdig, const float *hcsum,
                                                const float *hcinv, int I, int D, int o0, int lane, float *yn)
 {
@@ -247,7 +114,7 @@ __device__ __forceinline__ void dn_unit_finish(const DnUnit<BITS, DCPL, S> &u, c
             const float cs = hcsum[c], ci = hcinv[c];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const float qh = qdot_g<BITS, NIB>(u.d[s].q[m], dg);
+                const float qh = qdot<BITS>(u.d[s].q[m], dg);
                 t[s] = fmaf(bf16_lo(u.d[s].sb[m]) * ci, qh, t[s]);
                 t[s] = fmaf(bf16_hi(u.d[s].sb[m]), cs, t[s]);
             }
@@ -492,9 +359,8 @@ __global__ void __launch_bounds__(NT, 4) k_expert_gemv_st(GemvArgs a)
     const int D = a.D, I = a.I;
     uint4 (*sq)[64] = s_q[wave];
     uint32_t (*ssb)[64] = s_sb[wave];
-    constexpr bool NIB = BITS == 2;  // 2-bit codes take the nibble digit planes
 
-    digit_table<BITS, NIB>(a.x, D, t.dig, t.csum, t.cinv);
+    digit_table<BITS>(a.x, D, t.dig, t.csum, t.cinv);
     lds_barrier();
 
     const int ngu = (I + R - 1) / R;
@@ -512,7 +378,7 @@ __global__ void __launch_bounds__(NT, 4) k_expert_gemv_st(GemvArgs a)
             wait_lgkm0();
             if (u + NW < ngu) gu_stage<BITS, GCPL, R>(rs, sq, ssb, D, I, (u + NW) * R, lane);
             float hv[R];
-            gu_finish_g<BITS, GCPL, R, NIB>(g, t.dig, t.csum, t.cinv, D, lane, hv);
+            gu_finish_c<BITS, GCPL, R>(g, t.dig, t.csum, t.cinv, D, lane, hv);
             if (lane == 0) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -524,7 +390,7 @@ __global__ void __launch_bounds__(NT, 4) k_expert_gemv_st(GemvArgs a)
         // the first down unit streams while h is completed and converted
         if (wave < ndn) dn_stage<BITS, LPR, DCPL, S>(rs, sq, ssb, D, I, wave * RPD, lane);
         lds_barrier();
-        digit_table<BITS, NIB>(t.h, I, t.hdig, t.hcsum, t.hcinv);
+        digit_table<BITS>(t.h, I, t.hdig, t.hcsum, t.hcinv);
         for (int i = threadIdx.x; i < I; i += NT) hn[i] = t.h[i];
         lds_barrier();
         for (int u = wave; u < ndn; u += NW) {
@@ -533,7 +399,7 @@ __global__ void __launch_bounds__(NT, 4) k_expert_gemv_st(GemvArgs a)
             dn_unstage<BITS, LPR, DCPL, S>(d, sq, ssb, D, I, u * RPD, lane);
             wait_lgkm0();
             if (u + NW < ndn) dn_stage<BITS, LPR, DCPL, S>(rs, sq, ssb, D, I, (u + NW) * RPD, lane);
-            dn_unit_finish<BITS, LPR, DCPL, S, NIB>(d, t.hdig, t.hcsum, t.hcinv, I, D, u * RPD, lane, t.y);
+            dn_unit_finish<BITS, LPR, DCPL, S>(d, t.hdig, t.hcsum, t.hcinv, I, D, u * RPD, lane, t.y);
         }
         // y leaves in one coalesced pass (no stores between a wave's stage
         // refills, whose wait would also wait for them)

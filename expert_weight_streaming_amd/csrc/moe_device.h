@@ -14,11 +14,13 @@
 // digit planes, x_int = d0 + 256 d1 + 65536 d2.  A 32-bit word of codes,
 // masked so that each byte holds one code, then meets the matching digit
 // words in three v_dot4_i32_i8 (four code*digit products each, exact in
-// int32).  2-bit codes take six signed 4-bit digit planes instead,
-// x_int = sum_p d_p 16^p, and v_dot8_i32_i4 (eight products each): one mask
-// or one shift and mask of a code word leaves eight codes as nibbles.  Per
-// 16-byte chunk the plane sums are combined exactly in int32, rounded once
-// to fp32 and scaled by 2^-k * scale.  Apart from the fixed-point rounding of x
+// int32).  In the one-vector kernels the activations take six base-16
+// digit planes instead and the codes meet them eight at a time in
+// v_dot8 (4-bit codes: unsigned digits of x_int + 2^22, the offset removed
+// exactly with the codes' sum; 2-bit codes: signed digits, x_int =
+// sum_p d_p 16^p, after one mask or one shift and mask of a code word).
+// Per 16-byte chunk the plane sums are combined exactly in int32, rounded
+// once to fp32 and scaled by 2^-k * scale.  Apart from the fixed-point rounding of x
 // (half a unit of 2^-k, about 1e-7 of the vector's largest element) the sum
 // is exact.  Cost: 4-bit about 1.4 VALU operations per weight, 2-bit about
 // 1.3, against about 3 for a float conversion and an FMA per weight.
@@ -155,31 +157,45 @@ __device__ __forceinline__ void nib_words(const float *v, float mul, int *o)
     for (int p = 0; p < kNibPlanes; ++p) o[p] = (int)w[p];
 }
 
-// Digit words of one chunk from the chunk's activations v[0..CODES): the
-// word of plane p for word k, sub s holds, in byte j, digit p of
-// v[k*PER_WORD + s + SUBS*j].  Plane-major: dg index p*PW + k*SUBS + s, so
-// that the four words matching four masked code words of the same code
-// word(s) sit side by side (one 16-byte load for a matrix-core operand).
+// 4-bit chunks: six unsigned base-16 digits of u = xi + 2^22, which lies in
+// [0, 2^23): word k * 6 + p of a chunk holds, in nibble j, digit p of
+// value 8 k + j, the value of code j of code word k, so a code word meets
+// its six digit words unmasked in v_dot8_u32_u4.  sum code * u minus
+// 2^22 * sum code is sum code * xi exactly (modulo 2^32, and that sum is
+// below 2^31 in magnitude).  24 words per chunk (Codes<4>::DW).
+__device__ __forceinline__ uint32_t unib_digits(float v, float mul)
+{
+    return (uint32_t)(__float2int_rn(v * mul) + 0x400000);
+}
+
+// the six digit words of the eight values v[0..8)
+__device__ __forceinline__ void unib_words(const float *v, float mul, int *o)
+{
+    uint32_t w[kNibPlanes] = {0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t z = unib_digits(v[j], mul);
+#pragma unroll
+        for (int p = 0; p < kNibPlanes; ++p) w[p] |= ((z >> (4 * p)) & 15u) << (4 * j);
+    }
+#pragma unroll
+    for (int p = 0; p < kNibPlanes; ++p) o[p] = (int)w[p];
+}
+
+// Digit words of one chunk from the chunk's activations v[0..CODES) in the
+// nibble planes above (2-bit signed, 4-bit unsigned), by one thread.
 template <int BITS>
 __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
 {
-    using C = Codes<BITS>;
     if constexpr (BITS == 2) {
-        // the nibble planes above
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) nib_words(v + 16 * k + sh, mul, dg + (2 * k + sh) * kNibPlanes);
-        return;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) unib_words(v + 8 * k, mul, dg + k * kNibPlanes);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int s = 0; s < C::SUBS; ++s) {
-            const float *u = v + k * C::PER_WORD + s;
-            int *o = dg + k * C::SUBS + s;
-            digit_words(u[0], u[C::SUBS], u[2 * C::SUBS], u[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
-        }
 }
 
 // sum over one chunk of code * x_int, from the chunk's digit words; exact
@@ -187,7 +203,6 @@ __device__ __forceinline__ void chunk_digits(const float *v, float mul, int *dg)
 template <int BITS>
 __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
 {
-    using C = Codes<BITS>;
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     if constexpr (BITS == 2) {
         // nibble planes: |a_p| <= 64 * 3 * 8, and the Horner sums are partial
@@ -206,24 +221,23 @@ __device__ __forceinline__ float qdot(const uint4 q, const int *dg)
 #pragma unroll
         for (int p = kNibPlanes - 2; p >= 0; --p) h = h * 16 + a[p];
         return (float)h;
-    }
-    int a0 = 0, a1 = 0, a2 = 0;
+    } else {
+        // unsigned nibble planes: sum code * (xi + 2^22) by Horner over the
+        // planes (modulo 2^32), less 2^22 times the codes' sum
+        uint32_t a[kNibPlanes] = {0u, 0u, 0u, 0u, 0u, 0u};
+        uint32_t qs = 0u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 4; ++k) {
 #pragma unroll
-        for (int s = 0; s < C::SUBS; ++s) {
-            const int m = (int)((w[k] >> (BITS * s)) & C::MASK);
-            const int *d = dg + k * C::SUBS + s;
-            a0 = __builtin_amdgcn_sdot4(m, d[0], a0, false);
-            a1 = __builtin_amdgcn_sdot4(m, d[C::PW], a1, false);
-            a2 = __builtin_amdgcn_sdot4(m, d[2 * C::PW], a2, false);
+            for (int p = 0; p < kNibPlanes; ++p)
+                a[p] = __builtin_amdgcn_udot8(w[k], (uint32_t)dg[k * kNibPlanes + p], a[p], false);
+            qs = __builtin_amdgcn_udot8(w[k], 0x11111111u, qs, false);
         }
-    // |a0|, |a1| <= CODES (2^BITS - 1) 128 and |a2| <= CODES (2^BITS - 1) 64
-    // (digit bounds above), so every partial sum of a0 + 256 a1 + 65536 a2
-    // stays below 2.03e9 < 2^31 at 4-bit (8.1e8 at 2-bit): the chunk's sum
-    // of code * xi exactly, rounded once (the same value as
-    // fma(a2, 65536, a0 + 256 a1) in fp32)
-    return (float)(a2 * 65536 + a1 * 256 + a0);
+        uint32_t h = a[kNibPlanes - 1];
+#pragma unroll
+        for (int p = kNibPlanes - 2; p >= 0; --p) h = h * 16u + a[p];
+        return (float)(int)(h - (qs << 22));
+    }
 }
 
 // Digit table of one chunk built in registers, with a fixed-point step of
@@ -273,23 +287,27 @@ __device__ __forceinline__ void chunk_digits_lane(float4 v, int q, bool valid, i
             cinv[ch] = inv;
         }
     } else {
-        // pair (p = 0, 1): word p takes components p and p+2 of both lanes
-        const int p = threadIdx.x & 1;
-        const float s0 = fdpp<0xB1>(p ? v.x : v.y, 0.f);
-        const float s1 = fdpp<0xB1>(p ? v.z : v.w, 0.f);
-        const float a = p ? s0 : v.x, b = p ? s1 : v.z, c = p ? v.y : s0, d = p ? v.w : s1;
-        int w0, w1, w2;
-        digit_words(a, b, c, d, mul, w0, w1, w2);
-        if (valid) {
-            const int ch = q / G, f = q - ch * G;
-            int *o = dig + ch * C::DW + f;
-            o[0] = w0;
-            o[C::PW] = w1;
-            o[2 * C::PW] = w2;
-            if (f == 0) {
-                csum[ch] = sum;
-                cinv[ch] = inv;
-            }
+        // unsigned nibble planes: lane f (values 4f..4f+3, code word f / 2)
+        // supplies bytes 2 (f % 2) and 2 (f % 2) + 1 of its code word's six
+        // words, as one 16-bit store per word
+        if (!valid) return;  // after the reductions, which need every lane
+        const int ch = q / G, f = q - ch * G;
+        const uint32_t z0 = unib_digits(v.x, mul), z1 = unib_digits(v.y, mul);
+        const uint32_t z2 = unib_digits(v.z, mul), z3 = unib_digits(v.w, mul);
+        // byte m: digits 2m (ev) and 2m + 1 (od) of a value pair
+        const uint32_t ev01 = (z0 & 0x0F0F0Fu) | ((z1 & 0x0F0F0Fu) << 4), od01 = ((z0 >> 4) & 0x0F0F0Fu) | (z1 & 0xF0F0F0u);
+        const uint32_t ev23 = (z2 & 0x0F0F0Fu) | ((z3 & 0x0F0F0Fu) << 4), od23 = ((z2 >> 4) & 0x0F0F0Fu) | (z3 & 0xF0F0F0u);
+        uint16_t *wh = reinterpret_cast<uint16_t *>(dig + ch * C::DW + (f >> 1) * kNibPlanes) + (f & 1);
+#pragma unroll
+        for (int m2 = 0; m2 < 3; ++m2) {
+            // v_perm_b32(hi, lo, sel): byte m2 of lo, then byte m2 of hi
+            const uint32_t sel = 0x0c0c0000u | (uint32_t)m2 | ((uint32_t)(4 + m2) << 8);
+            wh[(2 * m2) * 2] = (uint16_t)__builtin_amdgcn_perm(ev23, ev01, sel);
+            wh[(2 * m2 + 1) * 2] = (uint16_t)__builtin_amdgcn_perm(od23, od01, sel);
+        }
+        if (f == 0) {
+            csum[ch] = sum;
+            cinv[ch] = inv;
         }
     }
 }
@@ -373,14 +391,12 @@ __device__ __forceinline__ float block_digit_table(const float *x, int n, int *d
             nib_words(x + c * C::CODES + 16 * k + sh, mul, dig + c * C::DW + (2 * k + sh) * kNibPlanes);
         }
     } else {
-        // one thread per (chunk, word, sub): four activations -> three words
-        const int nwords = n / C::CODES * 4 * C::SUBS;
-        for (int t = tid; t < nwords; t += nt) {
-            const int c = t / (4 * C::SUBS), r = t - c * 4 * C::SUBS;
-            const int k = r / C::SUBS, s = r - k * C::SUBS;
-            const float *v = x + c * C::CODES + k * C::PER_WORD + s;
-            int *o = dig + c * C::DW + k * C::SUBS + s;
-            digit_words(v[0], v[C::SUBS], v[2 * C::SUBS], v[3 * C::SUBS], mul, o[0], o[C::PW], o[2 * C::PW]);
+        // one thread per (chunk, code word): eight activations -> six
+        // unsigned nibble words
+        const int nw = n / C::CODES * 4;
+        for (int t = tid; t < nw; t += nt) {
+            const int c = t >> 2, k = t & 3;
+            unib_words(x + c * C::CODES + 8 * k, mul, dig + c * C::DW + k * kNibPlanes);
         }
     }
     chunk_sums<BITS>(x, n / C::CODES, csum);

@@ -22,8 +22,8 @@
 // Per 16-byte chunk the plane sums are combined exactly in int32, rounded
 // once to fp32 and scaled by 2^-k * scale.  Apart from the fixed-point rounding of x
 // (half a unit of 2^-k, about 1e-7 of the vector's largest element) the sum
-// is exact.  Cost: 4-bit about 1.4 VALU operations per weight, 2-bit about
-// 1.3, against about 3 for a float conversion and an FMA per weight.
+// is exact.  Cost in the one-vector kernels: under one vector operation per
+// weight, against about 3 for a float conversion and an FMA per weight.
 #pragma once
 #include "moe_internal.h"
 

@@ -348,6 +348,7 @@ moe::BatchArgs batch_args(const moe_layer_desc *d, int32_t T, const float *x, in
     b.n_act = reinterpret_cast<int32_t *>(ws + L.n_act);
     b.mwork = reinterpret_cast<int32_t *>(ws + L.mwork);
     b.n_mwork = reinterpret_cast<int32_t *>(ws + L.n_mwork);
+    b.grp_arrive = reinterpret_cast<uint32_t *>(ws + L.ctr_group);
     b.xdig = reinterpret_cast<int *>(ws + L.xdig);
     b.xcsum = reinterpret_cast<float *>(ws + L.xcsum);
     b.xinv = reinterpret_cast<float *>(ws + L.xinv);

@@ -11,7 +11,8 @@
 //                  tokens' activations as digit words, one fixed-point step
 //                  per scale group (k_xdigits alone when routing is given)
 //   k_topk_b       the logits (slices added in order), per-token top-K and
-//                  softmax weights (one wave per token)
+//                  softmax weights (one wave per token); up to 512 experts
+//                  its last block also does k_group's work
 //   k_group        the grouping: count[e], offset[e] (exclusive prefix
 //                  sum), the pair permutation perm[pos] = t*K + k sorted by
 //                  (expert, pair index), its inverse, the list of active
@@ -169,93 +170,6 @@ __host__ __device__ inline int route_splits(int D)
     return 1;
 }
 
-// ---------------------------------------------------------------------------
-// Top-K of every token: one wave per token, its logits (the slices' partial
-// logits added in slice order, also stored to logits[t]) in LDS; K rounds of
-// the wave's largest remaining key (larger logit first, the lower index on a
-// tie), then the softmax over the selected logits.
-__global__ void __launch_bounds__(256) k_topk_b(BatchArgs a, int splits)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    const int E = a.E, K = a.K, T = a.T;
-    __shared__ float lg[4][4096];
-    if (t >= T) return;  // whole waves leave; no block barrier follows
-    for (int e0 = 0; e0 < E; e0 += 64 * 8) {
-        float v[8][kRouteSplit];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = e0 + lane + 64 * u;
-#pragma unroll
-            for (int sl = 0; sl < kRouteSplit; ++sl)
-                v[u][sl] = e < E && sl < splits ? a.lpart[((size_t)sl * T + t) * E + e] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = e0 + lane + 64 * u;
-            float sum = v[u][0];
-#pragma unroll
-            for (int sl = 1; sl < kRouteSplit; ++sl)
-                if (sl < splits) sum += v[u][sl];
-            if (e < E) {
-                lg[wave][e] = sum;
-                a.logits[(size_t)t * E + e] = sum;
-            }
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    if (E <= 64 * 8) {
-        // the one-token kernels' selection on 32-bit order keys (same
-        // order, ties and weights as below, fewer instructions per round)
-        __shared__ int s_sel[4][kMaxTopK], s_rdy[4][kMaxTopK];
-        __shared__ float s_w[4][kMaxTopK];
-        uint32_t ord[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = lane + 64 * u;
-            ord[u] = e < E ? order_key(__float_as_uint(lg[wave][e])) : 0u;
-        }
-        topk_select<8>(ord, K, s_sel[wave], s_w[wave], s_rdy[wave], 1, lane);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        if (lane < K) {
-            a.topk_idx[(size_t)t * K + lane] = s_sel[wave][lane];
-            a.topk_w[(size_t)t * K + lane] = s_w[wave][lane];
-        }
-        return;
-    }
-    uint64_t taken = 0;  // bit j: element lane + 64 j selected
-    int idx[kMaxTopK];
-    float vals[kMaxTopK], w[kMaxTopK];
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-        idx[k] = -1;
-        vals[k] = -INFINITY;
-        if (k >= K) continue;
-        uint64_t best = 0ull;
-        for (int jj = 0, e = lane; e < E; ++jj, e += 64)
-            if (!((taken >> jj) & 1ull)) {
-                const uint64_t key = route_key(lg[wave][e], e);
-                best = key > best ? key : best;
-            }
-        const uint64_t m = wave_max_key(best);
-        const int e = key_index(m);
-        if ((e & 63) == lane) taken |= 1ull << (e >> 6);
-        idx[k] = e;
-        vals[k] = key_value(m);
-    }
-    topk_weights(vals, K, w);
-    if (lane < K) {
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k)
-            if (k == lane) {
-                a.topk_idx[(size_t)t * K + k] = idx[k];
-                a.topk_w[(size_t)t * K + k] = w[k];
-            }
-    }
-}
-
 // Exclusive prefix sums of three arrays v0, v1, v2 [0..n) in place
 // (n <= 4 * blockDim.x), their totals in tot[]; one block.  Each thread sums
 // 4 consecutive entries, a wave scan (shuffles) runs over the threads' sums,
@@ -307,32 +221,28 @@ __device__ __forceinline__ void block_exscan3(int *v0, int *v1, int *v2, int n, 
     __syncthreads();
 }
 
-// One block of 1024 threads: the token -> expert grouping of the
-// selections: count[e], offset[e] (exclusive prefix sums), the pair
-// permutation perm[pos] = t*K + k sorted by (expert, pair index), its
-// inverse, the active experts in ascending order; and the expert kernels'
-// dense work list: (item, tile of 16 of its tokens) for every active expert
-// in that order (item = its rank) and then the shared expert (item n_act).
-__global__ void __launch_bounds__(1024) k_group(BatchArgs a)
+// The token -> expert grouping of the selections, by one block, from the
+// pair ids in LDS (s_idx[t*K + k]): count[e], offset[e] (exclusive prefix
+// sums), the pair permutation perm[pos] = t*K + k sorted by (expert, pair
+// index), its inverse, the active experts in ascending order; and the
+// expert kernels' dense work list: (item, tile of 16 of its tokens) for
+// every active expert in that order (item = its rank) and then the shared
+// expert (item n_act).  s_count .. s_nt hold E entries (E <= 4 blockDim);
+// wsum: [blockDim / 64][3].
+__device__ __forceinline__ void group_pairs(const BatchArgs &a, const int *s_idx, int *s_count, int *s_off, int *s_flag,
+                                            int *s_nt, int (*wsum)[3])
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, nt = blockDim.x;
     const int T = a.T, K = a.K, E = a.E, P = T * K;
-    __shared__ __align__(16) int s_idx[64 * kMaxTopK];
-    __shared__ int s_count[4096];
-    __shared__ int s_off[4096];
-    __shared__ int s_flag[4096];
-    __shared__ int s_nt[4096];
-    __shared__ int wsum[16][3];
-    for (int p = tid; p < P; p += 1024) s_idx[p] = a.topk_idx[p];
-    for (int e = tid; e < E; e += 1024) s_count[e] = 0;
+    for (int e = tid; e < E; e += nt) s_count[e] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 1024) {
+    for (int p = tid; p < P; p += nt) {
         const int e = s_idx[p];
         if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
         else atomicOr(a.flags, MOE_DEVERR_EXPERT_RANGE);
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 1024) {
+    for (int e = tid; e < E; e += nt) {
         s_off[e] = s_count[e];
         s_flag[e] = s_count[e] > 0;
         s_nt[e] = (s_count[e] + 15) / 16;
@@ -341,7 +251,7 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
     __syncthreads();
     int tot[3];
     block_exscan3(s_off, s_flag, s_nt, E, wsum, tot);
-    for (int e = tid; e < E; e += 1024) {
+    for (int e = tid; e < E; e += nt) {
         a.offset[e] = s_off[e];
         if (s_count[e]) {
             a.act[s_flag[e]] = e;
@@ -355,7 +265,7 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
         *a.n_act = tot[1];
         *a.n_mwork = tot[2] + (shared ? (T + 15) / 16 : 0);
     }
-    for (int p = tid; p < P; p += 1024) {
+    for (int p = tid; p < P; p += nt) {
         const int e = s_idx[p];
         if (e < 0 || e >= E) {
             a.pos_of_pair[p] = -1;
@@ -375,6 +285,133 @@ __global__ void __launch_bounds__(1024) k_group(BatchArgs a)
         a.perm[pos] = p;
         a.pos_of_pair[p] = pos;
     }
+}
+
+// One block of 1024 threads: the grouping of the selections in topk_idx
+// (given by the caller, or taken by k_topk_b for more than 512 experts).
+__global__ void __launch_bounds__(1024) k_group(BatchArgs a)
+{
+    __shared__ __align__(16) int s_idx[64 * kMaxTopK];
+    __shared__ int s_count[4096];
+    __shared__ int s_off[4096];
+    __shared__ int s_flag[4096];
+    __shared__ int s_nt[4096];
+    __shared__ int wsum[16][3];
+    for (int p = threadIdx.x; p < a.T * a.K; p += blockDim.x) s_idx[p] = a.topk_idx[p];
+    group_pairs(a, s_idx, s_count, s_off, s_flag, s_nt, wsum);
+}
+
+// ---------------------------------------------------------------------------
+// Top-K of every token: one wave per token, its logits (the slices' partial
+// logits added in slice order, also stored to logits[t]) in LDS; K rounds of
+// the wave's largest remaining key (larger logit first, the lower index on a
+// tie), then the softmax over the selected logits.  With `group` (E <= 512)
+// the last block to finish also builds the grouping (k_group's work) from
+// every token's selection: the selections go out as agent-scope stores, each
+// block counts itself in with an agent-scope atomic once its stores are
+// acknowledged, and the last one reads them back at agent scope; it resets
+// the counter for the next call.
+__global__ void __launch_bounds__(256) k_topk_b(BatchArgs a, int splits, int group)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    const int E = a.E, K = a.K, T = a.T;
+    __shared__ __align__(16) float lg[4][4096];
+    __shared__ int s_sel[4][kMaxTopK], s_rdy[4][kMaxTopK];
+    __shared__ float s_w[4][kMaxTopK];
+    if (t < T) {
+        for (int e0 = 0; e0 < E; e0 += 64 * 8) {
+            float v[8][kRouteSplit];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + lane + 64 * u;
+#pragma unroll
+                for (int sl = 0; sl < kRouteSplit; ++sl)
+                    v[u][sl] = e < E && sl < splits ? a.lpart[((size_t)sl * T + t) * E + e] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + lane + 64 * u;
+                float sum = v[u][0];
+#pragma unroll
+                for (int sl = 1; sl < kRouteSplit; ++sl)
+                    if (sl < splits) sum += v[u][sl];
+                if (e < E) {
+                    lg[wave][e] = sum;
+                    a.logits[(size_t)t * E + e] = sum;
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        if (E <= 64 * 8) {
+            // the one-token kernels' selection on 32-bit order keys (same
+            // order, ties and weights as below, fewer instructions per round)
+            uint32_t ord[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = lane + 64 * u;
+                ord[u] = e < E ? order_key(__float_as_uint(lg[wave][e])) : 0u;
+            }
+            topk_select<8>(ord, K, s_sel[wave], s_w[wave], s_rdy[wave], 1, lane);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            if (lane < K) {
+                __hip_atomic_store(a.topk_idx + (size_t)t * K + lane, s_sel[wave][lane], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                a.topk_w[(size_t)t * K + lane] = s_w[wave][lane];
+            }
+        } else {
+            uint64_t taken = 0;  // bit j: element lane + 64 j selected
+            int idx[kMaxTopK];
+            float vals[kMaxTopK], w[kMaxTopK];
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                idx[k] = -1;
+                vals[k] = -INFINITY;
+                if (k >= K) continue;
+                uint64_t best = 0ull;
+                for (int jj = 0, e = lane; e < E; ++jj, e += 64)
+                    if (!((taken >> jj) & 1ull)) {
+                        const uint64_t key = route_key(lg[wave][e], e);
+                        best = key > best ? key : best;
+                    }
+                const uint64_t m = wave_max_key(best);
+                const int e = key_index(m);
+                if ((e & 63) == lane) taken |= 1ull << (e >> 6);
+                idx[k] = e;
+                vals[k] = key_value(m);
+            }
+            topk_weights(vals, K, w);
+            if (lane < K) {
+#pragma unroll
+                for (int k = 0; k < kMaxTopK; ++k)
+                    if (k == lane) {
+                        a.topk_idx[(size_t)t * K + k] = idx[k];
+                        a.topk_w[(size_t)t * K + k] = w[k];
+                    }
+            }
+        }
+    }
+    if (!group) return;  // uniform over the grid
+    __shared__ int is_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.grp_arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    // the grouping's LDS in the finished top-K's logit rows (E <= 512):
+    // pair ids, then count, offset, flag and tile count of every expert
+    int *gs = reinterpret_cast<int *>(&lg[0][0]);
+    __shared__ int wsum[4][3];
+    for (int p = threadIdx.x; p < T * K; p += blockDim.x)
+        gs[p] = __hip_atomic_load(a.topk_idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    group_pairs(a, gs, gs + 64 * kMaxTopK, gs + 64 * kMaxTopK + 512, gs + 64 * kMaxTopK + 1024,
+                gs + 64 * kMaxTopK + 1536, wsum);
+    if (threadIdx.x == 0) *a.grp_arrive = 0u;
 }
 
 // Tokens of active item a: routed expert act[a] (positions offset..+count),
@@ -859,8 +896,11 @@ hipError_t launch_batch_route(const BatchArgs &a, int do_topk, int bits, hipStre
             hipLaunchKernelGGL(k_route_m<2>, grid, dim3(256), 0, s, a, splits);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_topk_b, dim3((a.T + 3) / 4), dim3(256), 0, s, a, splits);
+        // up to 512 experts the top-K kernel's last block also groups
+        const int group = a.E <= 512;
+        hipLaunchKernelGGL(k_topk_b, dim3((a.T + 3) / 4), dim3(256), 0, s, a, splits, group);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (group) return hipSuccess;
     } else {
         const dim3 grid(ttiles * (a.D / kGroup));
         if (bits == 4)

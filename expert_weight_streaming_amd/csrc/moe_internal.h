@@ -37,6 +37,7 @@ struct WsLayout {
     size_t ctr_route = 64;   // uint32 arrival counter of the route kernel
     size_t hdr = 128;        // uint32 grid size of the persistent stack kernel last run on this workspace
     size_t ctr_down = 192;   // uint32 arrival counter of the down kernel (layer mode)
+    size_t ctr_group = 224;  // uint32 arrival counter of the batched top-K kernel (its last block groups)
     size_t slots = 0;        // uint32 [kMaxLayerBlocks][kSlotWords] epochs reached by each block of the stack kernel
     // the stack kernel's exchanges: (value, epoch) pairs, uint64
     size_t tss = 0;          // [kMaxLayerBlocks] per-block sums of squares
@@ -131,6 +132,7 @@ struct BatchArgs {
     int32_t *mwork;          // [(E+1)*4] expert-kernel work: item ii (act[ii], or the shared expert for
                              // ii == n_act) << 2 | tile of 16 of its tokens
     int32_t *n_mwork;        // [1]
+    uint32_t *grp_arrive;    // arrival counter of k_topk_b's blocks (zero between calls)
     int *xdig;               // [T][D/64][48] digit words of x, per scale group
     float *xcsum;            // [T][D/64] group sums of x
     float *xinv;             // [T][D/64] group steps 2^-k

@@ -15,7 +15,7 @@ constexpr int kMaxLayerBlocks = 1024;    // grid cap of the persistent stack ker
 constexpr int kSlotWords = 16;           // one 64-byte barrier slot per block
 // In a batch, experts with at least this many tokens take the matrix-core
 // grouped kernels, the others the dot-product ones.
-constexpr int kRouteSplit = 4;  // hidden-dimension slices of the batched router (partial logits)
+constexpr int kRouteSplit = 8;  // hidden-dimension slices of the batched router (partial logits)
 
 // Router GEMV of one token (shared by the fused stack kernel and k_route, so
 // that both produce the same fp32 logits bit for bit): RSL waves per router

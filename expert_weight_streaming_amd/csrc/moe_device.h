@@ -643,25 +643,23 @@ __device__ __forceinline__ void gu_finish_c(const GuRegs<BITS, CPL, R> &g, const
     for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
+        // a chunk past the row's end has zero codes (gu_load) and zero
+        // weights here; it reads the last chunk's digits, so that no branch
+        // or zeroing of the digit registers is needed
         const int c = lane + 64 * m;
+        const bool okc = c < nchunks;
+        const int cc = okc ? c : nchunks - 1;
         int dg[C::DW];
-        float cs = 0.f, ci = 0.f;
-        if (c < nchunks) {
-            const int4 *src = reinterpret_cast<const int4 *>(dig + c * C::DW);
+        const int4 *src = reinterpret_cast<const int4 *>(dig + cc * C::DW);
 #pragma unroll
-            for (int t = 0; t < C::DW / 4; ++t) {
-                const int4 v = src[t];
-                dg[4 * t] = v.x;
-                dg[4 * t + 1] = v.y;
-                dg[4 * t + 2] = v.z;
-                dg[4 * t + 3] = v.w;
-            }
-            cs = csum[c];
-            ci = cinv[c];
-        } else {
-#pragma unroll
-            for (int t = 0; t < C::DW; ++t) dg[t] = 0;
+        for (int t = 0; t < C::DW / 4; ++t) {
+            const int4 v = src[t];
+            dg[4 * t] = v.x;
+            dg[4 * t + 1] = v.y;
+            dg[4 * t + 2] = v.z;
+            dg[4 * t + 3] = v.w;
         }
+        const float cs = okc ? csum[cc] : 0.f, ci = okc ? cinv[cc] : 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll

@@ -89,8 +89,8 @@ struct Codes {
     static constexpr int PER_WORD = 32 / BITS;     // codes per word
     static constexpr int SUBS = 8 / BITS;          // masked copies per word
     static constexpr uint32_t MASK = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
-    static constexpr int PW = 4 * SUBS;            // digit words per plane and chunk
-    static constexpr int DW = 3 * PW;              // digit words per chunk
+    static constexpr int PW = 4 * SUBS;            // base-256 digit words per plane and chunk
+    static constexpr int DW = 3 * PW;              // digit words per chunk (both digit formats)
 };
 
 // Fixed-point exponent for a vector whose largest magnitude is amax:
@@ -104,7 +104,8 @@ __device__ __forceinline__ void fixed_scale(float amax, float &mul, float &inv)
     inv = ldexpf(1.f, -k);
 }
 
-// The three signed base-256 digits of xi = round(v * mul) (|xi| < 2^22):
+// The matrix-core (batched) path's digits: the three signed base-256
+// digits of xi = round(v * mul) (|xi| < 2^22):
 // xi = d0 + 256 d1 + 65536 d2 with d0, d1 in [-128, 127] (sign-extended low
 // bytes) and |d2| <= 64.  Four values at once, as three packed digit words
 // (byte j of word p: digit p of value j).  d0 is the low byte of xi;
@@ -136,8 +137,8 @@ __device__ __forceinline__ void digit_words(float a, float b, float c, float d, 
 constexpr int kNibPlanes = 6;
 
 // The digits come out of one add and one XOR: y = xi + 0x888888 lies in
-// [0, 2^24) and equals sum_p (d_p + 8) 16^p, so nibble p of
-// y ^ 0x888888 is d_p + 8 - 8 read as a signed 4-bit number, d_p.
+// [0, 2^24) and equals sum_p (d_p + 8) 16^p, so nibble p of y is d_p + 8
+// in [0, 15], and flipping its top bit leaves d_p as a signed 4-bit number.
 __device__ __forceinline__ uint32_t nib_digits(float v, float mul)
 {
     return (uint32_t)(__float2int_rn(v * mul) + 0x888888) ^ 0x888888u;

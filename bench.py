@@ -154,14 +154,24 @@ def cpu_baseline(cfg, v0, seconds, check_rows):
 
 
 def cpu_model():
+    """The host CPU's model name with its family and model numbers (which
+    name the generation where the model name is generic) and the count of
+    logical CPUs the kernel reports."""
+    fields = {}
+    n = 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k = k.strip()
+                if k == "processor":
+                    n += 1
+                elif k in ("model name", "cpu family", "model") and k not in fields:
+                    fields[k] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    return f"{name} (family {fields.get('cpu family', '?')}, model {fields.get('model', '?')}, {n} logical CPUs)"
 
 
 def mem_available():
